@@ -1,0 +1,415 @@
+"""Plain fp64 CPU oracle for MARS structured-mask attention, decode step and acceptance.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, links or runs this
+module: only the tests, the smoke check and the bench's ``cpu_baseline`` leg may.
+It shares no code with the HIP library and imports nothing from it.
+
+Every function is the plain definition written out, in float64, with no blocking,
+fusion or reordering beyond what the definition states.  Sources (cited by page
+title and section):
+
+* [MARS] "MARS: Enabling Autoregressive Models Multi-Token Generation"
+  (arXiv 2604.07023): §3.2 Eq. 1 (noisy copy), Eq. 2 (attention mask over
+  z = [x; x~]), Fig. 2 (mask for L=8, B=4; sliding-window inference), §3.3 Eq. 4.
+* [BLOG] MARS author blog post (xalp.net, "mars"), section "Inference: a knob,
+  not a mode switch" (left-to-right commit while confidence >= tau, tau = 1.0 is
+  exact AR) and "Batching is where methods like this usually die" (W = 1 appends
+  no mask slots).
+* [TRENDS] aitrends.kr summary of MARS, inference paragraph (at least one token
+  is always accepted).
+
+Readings taken where the pages are silent (each is listed in the design notes):
+
+* The prompt is a causal prefix in front of [x; x~]: prompt rows see prompt keys
+  up to themselves; clean and noisy rows see every prompt key; nothing in the
+  prompt sees the response; block indices count from the first response token.
+* Intra-block attention is self-inclusive (Eq. 2 states j <= i).
+* GQA: query head h reads KV head h // (Hq / Hkv).
+* Acceptance uses the temperature-1 softmax over the full vocabulary; the argmax
+  tie rule is "lowest index"; tau >= 1 accepts exactly one token.
+
+Parity status: every public function here is pinned by a ``-m "not gpu"`` test
+(brute-force rule enumeration, the Fig. 2 matrix, closed forms, invariants and
+library cross-checks); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "block_index",
+    "mask_rules_scalar",
+    "mask_rules",
+    "mask_intervals",
+    "row_intervals",
+    "mask_nnz",
+    "attn",
+    "attn_scalar",
+    "tile_map",
+    "tile_map_rules",
+    "visible_tile_elems",
+    "decode",
+    "decode_scalar",
+    "accept_rows",
+    "accept",
+    "accept_scalar",
+]
+
+
+# ---------------------------------------------------------------------------
+# Mask (MARS §3.2, Eq. 2, plus the prompt reading)
+# ---------------------------------------------------------------------------
+
+def block_index(t, B):
+    """beta(t) = ceil(t / B) for a 1-indexed position t inside either stream ([MARS] §3.2)."""
+    return -(-np.asarray(t) // B)
+
+
+def _eq2_visible(i, j, L, B):
+    """Eq. 2 of [MARS] §3.2 on 1-indexed z-positions i (query), j (key), 1 <= i, j <= 2L.
+
+    True where M_ij = 0, False where M_ij = -inf.  Works elementwise on arrays.
+    """
+    i = np.asarray(i)
+    j = np.asarray(j)
+    clean_causal = (i <= L) & (j <= L) & (j <= i)
+    noisy_intra = (i > L) & (j > L) & (block_index(i - L, B) == block_index(j - L, B)) & (j <= i)
+    # block_index of a non-positive argument is never used: the & masks it out.
+    noisy_to_clean = (i > L) & (j <= L) & (block_index(j, B) < block_index(np.maximum(i - L, 1), B))
+    return clean_causal | noisy_intra | noisy_to_clean
+
+
+def mask_rules_scalar(P, L, B):
+    """Dense visibility over [prompt; x; x~] by explicit loops (tiny shapes only).
+
+    Positions are 1-indexed as in [MARS] §3.2.  Returns uint8 [N, N], N = P + 2L,
+    1 = visible.  The prompt reading: prompt rows are causal over the prompt; every
+    response row (clean or noisy) sees the whole prompt; the prompt sees no response.
+    """
+    N = P + 2 * L
+    m = np.zeros((N, N), dtype=np.uint8)
+    for a in range(1, N + 1):
+        for c in range(1, N + 1):
+            if a <= P:
+                vis = c <= a
+            elif c <= P:
+                vis = True
+            else:
+                i, j = a - P, c - P
+                if i <= L and j <= L:
+                    vis = j <= i
+                elif i > L and j > L:
+                    vis = (math.ceil((i - L) / B) == math.ceil((j - L) / B)) and j <= i
+                elif i > L and j <= L:
+                    vis = math.ceil(j / B) < math.ceil((i - L) / B)
+                else:
+                    vis = False
+            m[a - 1, c - 1] = 1 if vis else 0
+    return m
+
+
+def mask_rules(P, L, B, rows=None):
+    """Vectorised form of :func:`mask_rules_scalar` (same rules, Eq. 2 case by case).
+
+    ``rows``: optional 0-indexed query positions to materialise (default: all N).
+    Returns bool [len(rows), N].
+    """
+    N = P + 2 * L
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    a = rows[:, None] + 1          # 1-indexed query position in [prompt; z]
+    c = np.arange(1, N + 1)[None, :]
+    prompt_row = a <= P
+    prompt_key = c <= P
+    i = a - P
+    j = c - P
+    resp = (~prompt_row) & (~prompt_key)
+    vis = np.where(prompt_row, c <= a, False)
+    vis |= (~prompt_row) & prompt_key
+    # Eq. 2 evaluated only where both positions are response positions.
+    ii = np.where(resp, i, 1)
+    jj = np.where(resp, j, 1)
+    vis |= resp & _eq2_visible(ii, jj, L, B)
+    return vis
+
+
+def row_intervals(P, L, B, rows=None):
+    """Two-interval encoding of each row's visible keys (0-indexed, half-open).
+
+    Row r sees keys [0, hi1) and [lo2, r + 1).  For prompt and clean rows the second
+    interval is empty (lo2 = r + 1) and hi1 = r + 1.  A noisy row at response offset
+    t0 = r - P - L, block k = t0 // B, sees [0, P + kB) (prompt plus the clean tokens
+    of earlier blocks) and [P + L + kB, r] (its own block up to itself).
+    """
+    N = P + 2 * L
+    r = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    noisy = r >= P + L
+    k = np.where(noisy, (r - P - L) // B, 0)
+    hi1 = np.where(noisy, P + k * B, r + 1)
+    lo2 = np.where(noisy, P + L + k * B, r + 1)
+    return hi1, lo2
+
+
+def mask_intervals(P, L, B, rows=None):
+    """Dense bool mask built from :func:`row_intervals` (independent second encoding)."""
+    N = P + 2 * L
+    r = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    hi1, lo2 = row_intervals(P, L, B, r)
+    j = np.arange(N)[None, :]
+    return (j < hi1[:, None]) | ((j >= lo2[:, None]) & (j <= r[:, None]))
+
+
+def mask_nnz(P, L, B):
+    """Number of visible (query, key) pairs, by summing the per-row interval lengths."""
+    hi1, lo2 = row_intervals(P, L, B)
+    r = np.arange(P + 2 * L)
+    return int(np.sum(hi1) + np.sum(r + 1 - lo2))
+
+
+# ---------------------------------------------------------------------------
+# Training-layout attention: O = softmax(scale * Q K^T + M) V
+# ---------------------------------------------------------------------------
+
+def _gqa_group(Hq, Hkv):
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    return Hq // Hkv
+
+
+def attn(q, k, v, P, L, B, scale=None, rows=None, row_chunk=1024, mask_fn=mask_rules):
+    """Masked attention over [prompt; x; x~] in float64.
+
+    q: [b, N, Hq, D]; k, v: [b, N, Hkv, D] (any float dtype; upcast to float64).
+    Query head h uses KV head h // (Hq/Hkv).  ``rows`` restricts the output to those
+    0-indexed query positions.  Returns (O [b, R, Hq, D] float64, LSE [b, Hq, R]).
+    The mask is materialised explicitly (``mask_fn``); masked scores are -inf; then
+    m = rowmax, p = exp(S - m), O = p V / sum p, LSE = m + ln sum p.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert N == P + 2 * L and k.shape == (b, N, Hkv, D) and v.shape == k.shape
+    G = _gqa_group(Hq, Hkv)
+    if scale is None or scale == 0:
+        scale = 1.0 / math.sqrt(D)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    out = np.zeros((b, R, Hq, D))
+    lse = np.zeros((b, Hq, R))
+    for c0 in range(0, R, row_chunk):
+        rr = rows[c0:c0 + row_chunk]
+        vis = mask_fn(P, L, B, rr)
+        for bi in range(b):
+            for h in range(Hq):
+                g = h // G
+                s = scale * (q[bi, rr, h, :] @ k[bi, :, g, :].T)
+                s = np.where(vis, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                den = p.sum(axis=1, keepdims=True)
+                out[bi, c0:c0 + len(rr), h, :] = (p @ v[bi, :, g, :]) / den
+                lse[bi, h, c0:c0 + len(rr)] = m[:, 0] + np.log(den[:, 0])
+    return out, lse
+
+
+def attn_scalar(q, k, v, vis, scale):
+    """Single-head masked attention by explicit loops in key order (tiny shapes only).
+
+    q: [R, D], k, v: [N, D], vis: bool [R, N].  Python floats (IEEE double), keys
+    visited in increasing index order; a masked key contributes exactly +0.0 to the
+    running sums.  Used for the bit-exact invariants.
+    """
+    R, D = len(q), len(q[0])
+    N = len(k)
+    out = [[0.0] * D for _ in range(R)]
+    for i in range(R):
+        s = [0.0] * N
+        m = -math.inf
+        for j in range(N):
+            if vis[i][j]:
+                acc = 0.0
+                for d in range(D):
+                    acc += float(q[i][d]) * float(k[j][d])
+                s[j] = scale * acc
+                m = max(m, s[j])
+        den = 0.0
+        num = [0.0] * D
+        for j in range(N):
+            p = math.exp(s[j] - m) if vis[i][j] else 0.0
+            den += p
+            for d in range(D):
+                num[d] += p * float(v[j][d])
+        out[i] = [x / den for x in num]
+    return np.array(out, dtype=np.float64)
+
+
+def tile_map(vis, bm, bn):
+    """Per (q-tile, k-tile) class on a bm x bn grid: 0 all masked, 2 all visible, 1 mixed.
+
+    Only in-range elements count (ragged last tiles are classified on what they hold).
+    ``vis``: bool [N, N].  Returns int8 [ceil(N/bm), ceil(N/bn)].
+    """
+    N0, N1 = vis.shape
+    T0, T1 = -(-N0 // bm), -(-N1 // bn)
+    out = np.zeros((T0, T1), dtype=np.int8)
+    for a in range(T0):
+        for c in range(T1):
+            blk = vis[a * bm:(a + 1) * bm, c * bn:(c + 1) * bn]
+            if blk.all():
+                out[a, c] = 2
+            elif blk.any():
+                out[a, c] = 1
+    return out
+
+
+def tile_map_rules(P, L, B, bm, bn):
+    """:func:`tile_map` of the Eq. 2 mask, built one q-tile row band at a time.
+
+    Same classification as ``tile_map(mask_rules(P, L, B), bm, bn)`` without holding
+    the N x N mask (the long layouts have N = 15360).
+    """
+    N = P + 2 * L
+    T0 = -(-N // bm)
+    bands = []
+    for a in range(T0):
+        rows = np.arange(a * bm, min(N, (a + 1) * bm))
+        bands.append(tile_map(mask_rules(P, L, B, rows), bm, bn))
+    return np.concatenate(bands, axis=0) if bands else np.zeros((0, 0), dtype=np.int8)
+
+
+def visible_tile_elems(P, L, B, bm, bn):
+    """In-range (query, key) elements of the tiles that are not fully masked.
+
+    4 * D * this * batch * Hq is the "visible-tile" FLOP count of a forward on a
+    bm x bn grid (QK^T and PV, 2 FLOP per multiply-add each).
+    """
+    N = P + 2 * L
+    tm = tile_map_rules(P, L, B, bm, bn)
+    h = np.minimum(bm, N - bm * np.arange(tm.shape[0]))
+    w = np.minimum(bn, N - bn * np.arange(tm.shape[1]))
+    return int(np.sum((tm > 0) * np.outer(h, w)))
+
+
+# ---------------------------------------------------------------------------
+# Sliding-window decode step ([MARS] Fig. 2 right; [BLOG] inference section)
+# ---------------------------------------------------------------------------
+
+def decode(q_win, k_win, v_win, k_cache, v_cache, cache_len, scale=None):
+    """Attention of W window rows against a per-sequence KV cache plus the window.
+
+    q_win [b, W, Hq, D]; k_win, v_win [b, W, Hkv, D]; k_cache, v_cache
+    [b, Hkv, cap, D]; cache_len [b] (0 <= len <= cap).  Window row i of sequence bi
+    attends to cache positions [0, len_bi) followed by window rows 0..i (causal,
+    self-inclusive, as within a noisy block of Eq. 2).  Returns O [b, W, Hq, D] float64.
+    """
+    q_win = np.asarray(q_win, dtype=np.float64)
+    k_win = np.asarray(k_win, dtype=np.float64)
+    v_win = np.asarray(v_win, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    b, W, Hq, D = q_win.shape
+    Hkv = k_win.shape[2]
+    G = _gqa_group(Hq, Hkv)
+    if scale is None or scale == 0:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((b, W, Hq, D))
+    for bi in range(b):
+        n = int(cache_len[bi])
+        for h in range(Hq):
+            g = h // G
+            keys = np.concatenate([k_cache[bi, g, :n, :], k_win[bi, :, g, :]], axis=0)
+            vals = np.concatenate([v_cache[bi, g, :n, :], v_win[bi, :, g, :]], axis=0)
+            s = scale * (q_win[bi, :, h, :] @ keys.T)          # [W, n + W]
+            vis = np.ones_like(s, dtype=bool)
+            for i in range(W):
+                vis[i, n + i + 1:] = False
+            s = np.where(vis, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            out[bi, :, h, :] = (p @ vals) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def decode_scalar(q_win, k_win, v_win, k_cache, v_cache, cache_len, scale):
+    """Loop form of :func:`decode` built on :func:`attn_scalar` (tiny shapes only)."""
+    b, W, Hq, D = q_win.shape
+    Hkv = k_win.shape[2]
+    G = _gqa_group(Hq, Hkv)
+    out = np.zeros((b, W, Hq, D))
+    for bi in range(b):
+        n = int(cache_len[bi])
+        for h in range(Hq):
+            g = h // G
+            keys = np.concatenate([k_cache[bi, g, :n, :], k_win[bi, :, g, :]], axis=0)
+            vals = np.concatenate([v_cache[bi, g, :n, :], v_win[bi, :, g, :]], axis=0)
+            vis = [[j < n + i + 1 for j in range(n + W)] for i in range(W)]
+            out[bi, :, h, :] = attn_scalar(q_win[bi, :, h, :], keys, vals, vis, scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Confidence-threshold acceptance ([BLOG] inference section; [TRENDS] inference)
+# ---------------------------------------------------------------------------
+
+def accept_rows(logits):
+    """Per row of logits [..., V]: (argmax with lowest-index ties, top-1 softmax probability).
+
+    Temperature-1 softmax over the full vocabulary, in float64:
+    m = max, token = min{v : l_v = m}, S = sum exp(l - m), pmax = 1 / S.
+    """
+    x = np.asarray(logits, dtype=np.float64)
+    m = x.max(axis=-1, keepdims=True)
+    token = np.argmax(x == m, axis=-1)          # first index attaining the max
+    S = np.exp(x - m).sum(axis=-1)
+    return token.astype(np.int32), 1.0 / S
+
+
+def accept(logits, tau):
+    """Acceptance over a window: logits [b, W, V] -> (tokens [b, W], pmax [b, W], n [b]).
+
+    Commit window positions left to right while pmax >= tau, stop at the first one
+    below tau, and always commit at least one.  tau >= 1 is the exact AR fallback
+    and commits exactly one.
+    """
+    tokens, pmax = accept_rows(logits)
+    b, W = pmax.shape
+    n = np.zeros(b, dtype=np.int32)
+    for bi in range(b):
+        if tau >= 1.0:
+            n[bi] = 1
+            continue
+        run = 0
+        while run < W and pmax[bi, run] >= tau:
+            run += 1
+        n[bi] = max(1, run)
+    return tokens, pmax, n
+
+
+def accept_scalar(logits, tau):
+    """Loop form of :func:`accept` with compensated summation (tiny vocabularies)."""
+    x = np.asarray(logits, dtype=np.float64)
+    b, W, V = x.shape
+    tokens = np.zeros((b, W), dtype=np.int32)
+    pmax = np.zeros((b, W))
+    n = np.zeros(b, dtype=np.int32)
+    for bi in range(b):
+        for i in range(W):
+            row = [float(t) for t in x[bi, i]]
+            best, arg = row[0], 0
+            for vi in range(1, V):
+                if row[vi] > best:
+                    best, arg = row[vi], vi
+            tokens[bi, i] = arg
+            pmax[bi, i] = 1.0 / math.fsum(math.exp(t - best) for t in row)
+        cnt = 0
+        if tau < 1.0:
+            for i in range(W):
+                if pmax[bi, i] >= tau:
+                    cnt += 1
+                else:
+                    break
+        n[bi] = max(1, cnt)
+    return tokens, pmax, n

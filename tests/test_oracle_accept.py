@@ -1,0 +1,84 @@
+"""Pins for the oracle's acceptance rule (CPU only).
+
+Anchors: the MARS blog ("commits them left to right while its confidence holds,
+stopping at the first token below a threshold tau"; "tau=1.0 recovers exact
+single-token AR decoding"), the aitrends.kr summary (at least one token is always
+accepted), greedy decoding (argmax), and closed forms of the softmax maximum.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mars_oracle as O
+
+
+def test_tau_one_is_exact_ar():
+    x = np.zeros((3, 4, 50))
+    x[:, :, 7] = 200.0                      # pmax rounds to 1.0 in float64
+    tok, pmax, n = O.accept(x, 1.0)
+    assert (pmax == 1.0).all() and (n == 1).all() and (tok == 7).all()
+
+
+def test_tau_below_uniform_accepts_whole_window():
+    x = np.random.default_rng(1).standard_normal((4, 5, 33))
+    _, pmax, n = O.accept(x, 1.0 / 33)
+    assert (pmax >= 1.0 / 33).all() and (n == 5).all()
+
+
+def test_constant_row():
+    _, pmax, _ = O.accept(np.full((1, 1, 1000), -3.25), 0.5)
+    tok, _, _ = O.accept(np.full((1, 1, 1000), -3.25), 0.5)
+    assert pmax[0, 0] == 1.0 / 1000 and tok[0, 0] == 0
+
+
+@pytest.mark.parametrize("h,V", [(0.0, 10), (2.5, 100), (20.0, 152064), (-4.0, 7)])
+def test_single_spike_closed_form(h, V):
+    x = np.zeros((1, 1, V))
+    x[0, 0, V // 3] = h
+    tok, pmax, _ = O.accept(x, 0.5)
+    if h >= 0:   # the spike is the maximum (ties at h = 0 go to index 0)
+        expect = math.exp(h) / (math.exp(h) + V - 1)
+        expect_tok = V // 3 if h > 0 else 0
+    else:        # the zeros are the maximum
+        expect = 1.0 / (V - 1 + math.exp(h))
+        expect_tok = 0
+    assert abs(pmax[0, 0] - expect) <= 1e-15 * max(1.0, expect)
+    assert tok[0, 0] == expect_tok
+
+
+def test_ties_take_lowest_index():
+    x = np.zeros((1, 2, 9))
+    x[0, 0, [3, 5]] = 4.0
+    x[0, 1, [8, 2, 6]] = 1.5
+    tok, _, _ = O.accept(x, 0.9)
+    assert tok.tolist() == [[3, 2]]
+
+
+def test_prefix_stops_at_first_below_tau():
+    def row(p, V=10):
+        # logits giving top-1 probability p: one entry log(p (V-1) / (1 - p)), others 0
+        r = np.zeros(V)
+        r[0] = math.log(p * (V - 1) / (1 - p))
+        return r
+    x = np.stack([np.stack([row(0.99), row(0.5), row(0.99), row(0.99)]),
+                  np.stack([row(0.99), row(0.99), row(0.2), row(0.99)]),
+                  np.stack([row(0.1), row(0.99), row(0.99), row(0.99)]),
+                  np.stack([row(0.97), row(0.96), row(0.99), row(0.951)])])
+    _, pmax, n = O.accept(x, 0.95)
+    assert n.tolist() == [1, 2, 1, 4]
+    _, _, n2 = O.accept(x, 0.995)
+    assert n2.tolist() == [1, 1, 1, 1]
+
+
+def test_matches_scalar_and_torch_softmax():
+    x = np.random.default_rng(2).standard_normal((3, 4, 257)) * 3
+    x[1, 2, 17] += 15
+    tok, pmax, n = O.accept(x, 0.6)
+    tok2, pmax2, n2 = O.accept_scalar(x, 0.6)
+    assert np.array_equal(tok, tok2) and np.array_equal(n, n2)
+    assert np.max(np.abs(pmax - pmax2)) <= 1e-15
+    sm = torch.softmax(torch.from_numpy(x), -1)
+    assert np.max(np.abs(sm.max(-1).values.numpy() - pmax)) <= 1e-15
+    assert np.array_equal(sm.argmax(-1).numpy(), tok)

@@ -1,0 +1,185 @@
+"""Pins for the oracle's attention and decode (CPU only).
+
+Independent anchors:
+  * the MARS blog's separate-forward check: clean-stream outputs equal a plain causal
+    forward over [prompt; x] bit for bit in float64 (scalar path), and to rounding on
+    the BLAS path (checked against torch's float64 scaled_dot_product_attention);
+  * B = 1: a masked position sees the clean prefix plus itself (MARS §3.3, first
+    position of a block);
+  * noisy block k equals a decode step whose cache holds [prompt; clean blocks < k]
+    and whose window is block k (MARS Fig. 2, sliding-window inference);
+  * W = 1 decode equals a textbook single-query AR step (the blog's "W=1 appends no
+    mask slots");
+  * closed forms: K = 0 gives the mean of the visible V; constant V gives that constant;
+  * torch float64 SDPA with an explicit boolean mask on small shapes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import mars_oracle as O
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def sdpa_ref(q, k, v, vis, scale):
+    """torch float64 SDPA, q [b,N,Hq,D], k/v [b,N,Hkv,D], vis [R,N] bool (GQA by repeat)."""
+    G = q.shape[2] // k.shape[2]
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+    vt = torch.from_numpy(v).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(vis), scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("b,Hq,Hkv,D,P,L,B", [
+    (1, 1, 1, 8, 3, 10, 3),
+    (2, 4, 2, 16, 0, 12, 4),
+    (1, 6, 2, 8, 5, 9, 1),
+    (1, 2, 1, 4, 2, 7, 9),
+])
+def test_attn_matches_torch_sdpa(b, Hq, Hkv, D, P, L, B):
+    N = P + 2 * L
+    q, k, v = rand((b, N, Hq, D), 1), rand((b, N, Hkv, D), 2), rand((b, N, Hkv, D), 3)
+    scale = 1 / math.sqrt(D)
+    out, lse = O.attn(q, k, v, P, L, B)
+    ref = sdpa_ref(q, k, v, O.mask_rules(P, L, B), scale)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    # LSE against scipy-free log-sum-exp written with torch
+    G = Hq // Hkv
+    vis = torch.from_numpy(O.mask_rules(P, L, B))
+    for h in range(Hq):
+        s = scale * torch.from_numpy(q[0, :, h]) @ torch.from_numpy(k[0, :, h // G]).T
+        s = s.masked_fill(~vis, -math.inf)
+        assert np.max(np.abs(torch.logsumexp(s, 1).numpy() - lse[0, h])) <= 1e-12
+
+
+def test_clean_rows_bit_identical_to_causal_scalar():
+    """fp64 scalar path: masked keys add exact zeros, so clean rows equal AR bit for bit."""
+    P, L, B, D = 3, 8, 4, 5
+    N = P + 2 * L
+    q, k, v = rand((N, D), 4), rand((N, D), 5), rand((N, D), 6)
+    scale = 1 / math.sqrt(D)
+    vis = O.mask_rules(P, L, B)
+    full = O.attn_scalar(q, k, v, vis, scale)
+    n = P + L
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    ar = O.attn_scalar(q[:n], k[:n], v[:n], causal, scale)
+    assert np.array_equal(full[:n], ar)
+
+
+def test_clean_rows_equal_causal_blas():
+    b, Hq, Hkv, D, P, L, B = 2, 4, 2, 16, 9, 20, 4
+    N = P + 2 * L
+    q, k, v = rand((b, N, Hq, D), 7), rand((b, N, Hkv, D), 8), rand((b, N, Hkv, D), 9)
+    out, _ = O.attn(q, k, v, P, L, B)
+    n = P + L
+    G = Hq // Hkv
+    qt = torch.from_numpy(q[:, :n]).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k[:, :n]).repeat_interleave(G, 2).permute(0, 2, 1, 3).contiguous()
+    vt = torch.from_numpy(v[:, :n]).repeat_interleave(G, 2).permute(0, 2, 1, 3).contiguous()
+    ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True).permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(out[:, :n] - ref)) <= 1e-12
+
+
+def test_b1_masked_position_sees_clean_prefix_plus_itself():
+    P, L, D = 4, 9, 6
+    N = P + 2 * L
+    q, k, v = rand((1, N, 1, D), 10), rand((1, N, 1, D), 11), rand((1, N, 1, D), 12)
+    out, _ = O.attn(q, k, v, P, L, 1)
+    scale = 1 / math.sqrt(D)
+    for t0 in range(L):
+        r = P + L + t0
+        keys = list(range(P + t0)) + [r]
+        s = np.array([scale * q[0, r, 0] @ k[0, j, 0] for j in keys])
+        p = np.exp(s - s.max())
+        ref = (p[:, None] * v[0, keys, 0]).sum(0) / p.sum()
+        assert np.max(np.abs(out[0, r, 0] - ref)) <= 1e-13
+
+
+def test_noisy_block_equals_decode_step():
+    """Noisy block k (0-indexed) = decode with cache [0, P + kB) and window = block k."""
+    P, L, B, D, Hq, Hkv = 3, 12, 4, 5, 2, 1
+    N = P + 2 * L
+    q, k, v = rand((1, N, Hq, D), 13), rand((1, N, Hkv, D), 14), rand((1, N, Hkv, D), 15)
+    scale = 1 / math.sqrt(D)
+    vis = O.mask_rules(P, L, B)
+    for blk in range(L // B):
+        rows = np.arange(P + L + blk * B, P + L + (blk + 1) * B)
+        n = P + blk * B
+        cap = N
+        kc = np.zeros((1, Hkv, cap, D)); vc = np.zeros((1, Hkv, cap, D))
+        kc[0, :, :n] = k[0, :n].transpose(1, 0, 2)
+        vc[0, :, :n] = v[0, :n].transpose(1, 0, 2)
+        dec = O.decode_scalar(q[:, rows], k[:, rows], v[:, rows], kc, vc, np.array([n]), scale)
+        for h in range(Hq):
+            full = O.attn_scalar(q[0, rows, h], k[0, :, 0], v[0, :, 0], vis[rows], scale)
+            assert np.array_equal(full, dec[0, :, h])
+        dec_blas = O.decode(q[:, rows], k[:, rows], v[:, rows], kc, vc, np.array([n]))
+        assert np.max(np.abs(dec_blas - dec)) <= 1e-12
+
+
+def test_decode_w1_is_textbook_ar_step():
+    b, Hq, Hkv, D, cap = 3, 4, 2, 8, 20
+    lens = np.array([0, 7, 20])
+    q = rand((b, 1, Hq, D), 16); kw = rand((b, 1, Hkv, D), 17); vw = rand((b, 1, Hkv, D), 18)
+    kc = rand((b, Hkv, cap, D), 19); vc = rand((b, Hkv, cap, D), 20)
+    out = O.decode(q, kw, vw, kc, vc, lens)
+    G = Hq // Hkv
+    for bi in range(b):
+        for h in range(Hq):
+            g = h // G
+            keys = np.concatenate([kc[bi, g, :lens[bi]], kw[bi, :, g]])
+            vals = np.concatenate([vc[bi, g, :lens[bi]], vw[bi, :, g]])
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(q[bi, :, h])[None], torch.from_numpy(keys)[None],
+                torch.from_numpy(vals)[None])[0].numpy()
+            assert np.max(np.abs(out[bi, :, h] - ref)) <= 1e-12
+
+
+def test_decode_matches_torch_with_window_mask():
+    b, W, Hq, Hkv, D, cap = 2, 4, 6, 2, 8, 16
+    lens = np.array([5, 16])
+    q = rand((b, W, Hq, D), 21); kw = rand((b, W, Hkv, D), 22); vw = rand((b, W, Hkv, D), 23)
+    kc = rand((b, Hkv, cap, D), 24); vc = rand((b, Hkv, cap, D), 25)
+    out = O.decode(q, kw, vw, kc, vc, lens)
+    assert np.max(np.abs(out - O.decode_scalar(q, kw, vw, kc, vc, lens, 1 / math.sqrt(D)))) <= 1e-12
+    G = Hq // Hkv
+    for bi in range(b):
+        n = lens[bi]
+        vis = np.zeros((W, n + W), dtype=bool)
+        vis[:, :n] = True
+        vis[:, n:] = np.tril(np.ones((W, W), dtype=bool))
+        for h in range(Hq):
+            keys = np.concatenate([kc[bi, h // G, :n], kw[bi, :, h // G]])
+            vals = np.concatenate([vc[bi, h // G, :n], vw[bi, :, h // G]])
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(q[bi, :, h]), torch.from_numpy(keys), torch.from_numpy(vals),
+                attn_mask=torch.from_numpy(vis)).numpy()
+            assert np.max(np.abs(out[bi, :, h] - ref)) <= 1e-12
+
+
+def test_decode_empty_cache_first_row_is_own_value():
+    q = rand((1, 3, 2, 4), 26); kw = rand((1, 3, 1, 4), 27); vw = rand((1, 3, 1, 4), 28)
+    kc = np.zeros((1, 1, 4, 4)); vc = np.zeros((1, 1, 4, 4))
+    out = O.decode(q, kw, vw, kc, vc, np.array([0]))
+    assert np.array_equal(out[0, 0, 0], vw[0, 0, 0]) and np.array_equal(out[0, 0, 1], vw[0, 0, 0])
+
+
+def test_closed_forms():
+    P, L, B, D = 4, 10, 3, 6
+    N = P + 2 * L
+    q, v = rand((1, N, 2, D), 29), rand((1, N, 1, D), 30)
+    out, lse = O.attn(q, np.zeros((1, N, 1, D)), v, P, L, B)
+    vis = O.mask_rules(P, L, B)
+    mean = (vis.astype(float) @ v[0, :, 0]) / vis.sum(1, keepdims=True)
+    assert np.max(np.abs(out[0, :, 0] - mean)) <= 1e-13
+    assert np.max(np.abs(lse[0, 0] - np.log(vis.sum(1)))) <= 1e-13
+    c = np.full((1, N, 1, D), 0.375)
+    out2, _ = O.attn(q, rand((1, N, 1, D), 31), c, P, L, B)
+    assert np.max(np.abs(out2 - 0.375)) <= 1e-15
