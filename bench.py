@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the MARS hot path on one MI355X.
+
+One step = one pass of the whole path on synthetic, seeded inputs resident in HBM:
+  1. mars_attn_fwd on the Qwen2.5-0.5B-shaped training layout (batch 8, 14/2 heads,
+     head_dim 64, P=256, L=512, B=4)                          -> visible-tile TFLOP/s;
+  2. mars_decode_step on the Qwen2.5-7B-shaped decode workload (32 sequences, 28/4 heads,
+     head_dim 128, cache lengths U[512, 4096], 4 window rows)  -> GB/s;
+  3. mars_accept on its logits [32, 4, 152064] at tau = 0.95   -> GB/s;
+  decode tokens/s = sum(n_accept) / (t_decode + t_accept)  (one attention layer + accept).
+Each kernel is timed with HIP events on the stream it is launched on.  Before every step a
+1 GiB buffer is overwritten so that the 256 MB Infinity Cache holds none of the inputs.
+The 7B-shaped and long training layouts are timed as well (own events) and reported.
+The CPU baseline is the fp64 oracle on a bounded sample of the same workloads.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "visible-tile TFLOP/s (train layout) + decode-step tokens/s at τ=0.95, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-layouts", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    return ap.parse_args()
+
+
+def train_flops(M, s):
+    """(FLOP_vt on the fixed 128x128 grid, FLOP_alg from the exact nnz) of one forward."""
+    nnz, vis = M.mars_attn_work(s.batch, s.hq, s.hkv, s.d, s.P, s.L, s.B, 128, 128)
+    per = 4.0 * s.d * s.batch * s.hq
+    return per * vis, per * nnz
+
+
+def traffic_from_profile(kernel_tag, src_file):
+    """HBM bytes per launch from a committed counter summary, if the kernel source still matches."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b):
+        return None
+    sha = hashlib.sha256(open(src_file, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def cpu_baseline_train(s, budget_s=12.0):
+    """fp64 oracle on whole (batch, head) slices of the training layout, FLOP_vt-scaled."""
+    from oracle import mars_oracle as O
+    from structured_mask_attention_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, k, v = I.train_inputs(s)
+    G = s.hq // s.hkv
+    qn = q[:1].float().numpy().astype(np.float64)
+    kn = k[:1].float().numpy().astype(np.float64)
+    vn = v[:1].float().numpy().astype(np.float64)
+    vis = O.visible_tile_elems(s.P, s.L, s.B, 128, 128)
+    heads, t0 = 0, time.perf_counter()
+    while heads < s.hq and time.perf_counter() - t0 < budget_s:
+        h = heads
+        O.attn(qn[:, :, h:h + 1], kn[:, :, h // G:h // G + 1], vn[:, :, h // G:h // G + 1], s.P, s.L, s.B)
+        heads += 1
+    dt = time.perf_counter() - t0
+    tflops = 4.0 * s.d * vis * heads / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s (visible-tile)", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {s.batch * s.hq} (batch, head) slices of {s.name}, fp64 NumPy, {dt:.1f} s"}
+
+
+def cpu_baseline_decode(s, budget_s=8.0):
+    from oracle import mars_oracle as O
+    from structured_mask_attention_amd import inputs as I
+    x = I.decode_inputs(s)
+    f = lambda t: t.float().numpy().astype(np.float64)
+    qw, kw, vw, kc, vc, lg = f(x.q_win), f(x.k_win), f(x.v_win), f(x.k_cache), f(x.v_cache), f(x.logits)
+    lens = x.cache_len.numpy()
+    seqs, toks, t0 = 0, 0, time.perf_counter()
+    while seqs < s.batch and time.perf_counter() - t0 < budget_s:
+        b = seqs
+        O.decode(qw[b:b + 1], kw[b:b + 1], vw[b:b + 1], kc[b:b + 1], vc[b:b + 1], lens[b:b + 1])
+        _, _, n = O.accept(lg[b:b + 1], s.tau)
+        toks += int(n.sum())
+        seqs += 1
+    dt = time.perf_counter() - t0
+    return {"value": toks / dt, "unit": "tokens/s", "kind": "oracle",
+            "sample": f"{seqs} of {s.batch} sequences of the decode step + accept, fp64 NumPy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the MARS hot path here has no multi-GPU mode "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import structured_mask_attention_amd as M
+    from structured_mask_attention_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- inputs (generated on the host, copied once; resident in HBM) ----
+    st = I.QWEN05B
+    q, k, v = (t.to(dev) for t in I.train_inputs(st))
+    o = torch.empty_like(q)
+    sd = I.DECODE7B
+    x = I.decode_inputs(sd)
+    qw, kw, vw = x.q_win.to(dev), x.k_win.to(dev), x.v_win.to(dev)
+    kc, vc = x.k_cache.to(dev), x.v_cache.to(dev)
+    lens = x.cache_len.to(dev)
+    logits = x.logits.to(dev)
+    od = torch.empty_like(qw)
+    dws = torch.empty(M.mars_decode_workspace_bytes(sd.batch, sd.hq, sd.hkv, sd.d, sd.W, sd.cap),
+                      dtype=torch.uint8, device=dev)
+    aws = torch.zeros(M.mars_accept_workspace_bytes(sd.batch, sd.W, sd.vocab, sd.tau), dtype=torch.uint8, device=dev)
+    tok = torch.empty((sd.batch, sd.W), dtype=torch.int32, device=dev)
+    pmx = torch.empty((sd.batch, sd.W), dtype=torch.float32, device=dev)
+    nacc = torch.empty((sd.batch,), dtype=torch.int32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        M.mars_attn_fwd(q, k, v, st.P, st.L, st.B, out=o)
+        if ev: ev[1].record(stream)
+        M.mars_decode_step(qw, kw, vw, kc, vc, lens, out=od, ws=dws)
+        if ev: ev[2].record(stream)
+        M.mars_accept(logits, sd.tau, ws=aws, tokens=tok, pmax=pmx, n_accept=nacc)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(1)
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    t_attn = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_acc = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in evs]) * 1e-3
+
+    flop_vt, flop_alg = train_flops(M, st)
+    ta = float(np.mean(t_attn))
+    tflops = flop_vt / ta / 1e12
+    n_sum = int(nacc.sum().item())
+    lens_sum = int(x.cache_len.sum().item())
+    dec_bytes = lens_sum * sd.hkv * sd.d * 2 * 2 + (qw.numel() + kw.numel() + vw.numel() + od.numel()) * 2
+    acc_bytes = logits.numel() * 2
+    td, tc = float(np.mean(t_dec)), float(np.mean(t_acc))
+
+    # ---- other training layouts (own events, same flush discipline) ----
+    layouts = {}
+    if not args.no_extra_layouts:
+        for s2 in (I.QWEN7B, I.LONG7B):
+            q2, k2, v2 = (t.to(dev) for t in I.train_inputs(s2))
+            o2 = torch.empty_like(q2)
+            for _ in range(3):
+                M.mars_attn_fwd(q2, k2, v2, s2.P, s2.L, s2.B, out=o2)
+            reps = 10
+            ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for r in range(reps):
+                if not args.no_flush:
+                    flush.fill_(1)
+                ev2[r][0].record(stream)
+                M.mars_attn_fwd(q2, k2, v2, s2.P, s2.L, s2.B, out=o2)
+                ev2[r][1].record(stream)
+            torch.cuda.synchronize()
+            t2 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev2])) * 1e-3
+            fvt, falg = train_flops(M, s2)
+            layouts[s2.name] = {"us": t2 * 1e6, "tflops_visible_tile": fvt / t2 / 1e12,
+                                "tflops_alg": falg / t2 / 1e12, "frac_of_peak": fvt / t2 / 1e12 / PEAK_BF16_TFLOPS}
+            del q2, k2, v2, o2
+        torch.cuda.empty_cache()
+
+    src = os.path.join(ROOT, "structured_mask_attention_amd", "csrc", "attn_fwd.hip")
+    traffic = traffic_from_profile("attn_fwd_bf16_qwen05b", src)
+    roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "kernel": "attn_fwd_bf16_kernel<64>", "work_per_launch_flop_vt": flop_vt,
+                "achieved_alg": flop_alg / ta / 1e12}
+
+    cpu = None
+    cpu_dec = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_train(st)
+        cpu_dec = cpu_baseline_decode(sd)
+
+    rec = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": float(np.mean(t_step)) * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the Qwen2.5 workloads; no weights or datasets)",
+        "config": {"workload": st.name, "decode_workload": sd.name, "global_batch": st.batch, "seq_len": st.N,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode": {
+            "tokens_per_s": n_sum / (td + tc),
+            "tokens_accepted": n_sum,
+            "decode_us": td * 1e6, "accept_us": tc * 1e6,
+            "decode_GBps": dec_bytes / td / 1e9, "decode_frac_hbm": dec_bytes / td / 1e9 / PEAK_HBM_GBS,
+            "accept_GBps": acc_bytes / tc / 1e9, "accept_frac_hbm": acc_bytes / tc / 1e9 / PEAK_HBM_GBS,
+            "cpu_baseline": cpu_dec,
+        },
+        "train_attn_us": ta * 1e6,
+        "train_attn_p10_p90_us": [float(np.percentile(t_attn, 10)) * 1e6, float(np.percentile(t_attn, 90)) * 1e6],
+        "train_layouts": layouts,
+        "wall_s_timed_region": t_wall,
+        "mall_flush": not args.no_flush,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

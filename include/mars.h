@@ -1,0 +1,225 @@
+/*
+ * mars.h - C ABI of libmars: MARS structured-mask attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "MARS: Enabling Autoregressive Models Multi-Token Generation"
+ * (arXiv 2604.07023):
+ *   - mars_attn_fwd:    one forward of attention over [prompt ; x ; x~] with the
+ *                       structured mask M of §3.2, Eq. 2 (training layout);
+ *   - mars_decode_step: the sliding-window inference step of Fig. 2 (right): B appended
+ *                       window rows attend to a per-sequence KV cache and, causally, to
+ *                       the window itself;
+ *   - mars_accept:      the confidence-threshold rule of the MARS author blog, section
+ *                       "Inference: a knob, not a mode switch": commit window positions
+ *                       left to right while the top-1 probability is >= tau, at least one.
+ *
+ * Conventions (all entry points):
+ *   - Every call returns an int status: MARS_OK (0) or a negative MARS_E* code.
+ *   - Descriptors live in host memory and are read during the call only.
+ *   - Tensor pointers are device pointers owned by the caller. The library never
+ *     allocates, frees or keeps them. Scratch memory comes in as a caller workspace.
+ *   - Validation is complete before any launch: on an error nothing is launched and
+ *     nothing is written.
+ *   - Work is enqueued on the caller's stream and the call returns without a host sync.
+ *     A device fault surfaces at the caller's next synchronisation.
+ *   - The library keeps no state between calls; calls are thread-safe. Two calls that
+ *     share a workspace must not run concurrently.
+ *   - Strides are in elements. The innermost dimension (head_dim or vocab) is contiguous.
+ *     Tensor base pointers must be 16-byte aligned and every stride a multiple of
+ *     16 bytes worth of elements (8 for bf16, 4 for fp32); MARS_EINVAL otherwise.
+ *   - Outputs are fully overwritten.
+ *   - A call with no work (batch == 0, or N == 0 for the forward) returns MARS_OK after
+ *     validating the descriptor; its tensor pointers are not inspected and may be NULL.
+ *   - bf16 means IEEE binary32 truncated to its top 16 bits (bfloat16); results are
+ *     rounded to nearest even when stored as bf16.
+ */
+#ifndef MARS_H
+#define MARS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MARS_ABI_VERSION 1
+
+/* Status codes. */
+#define MARS_OK 0
+#define MARS_EINVAL (-1)       /* bad shape, enum, tau, null pointer, alignment or stride */
+#define MARS_EUNSUPPORTED (-2) /* valid request this build does not implement (head_dim, dtype, window) */
+#define MARS_EWORKSPACE (-3)   /* workspace null or smaller than the *_workspace_bytes figure */
+#define MARS_EHIP (-4)         /* the HIP runtime reported an error at launch */
+
+/* Element types. */
+#define MARS_DTYPE_BF16 0
+#define MARS_DTYPE_FP32 1
+
+/* Returns MARS_ABI_VERSION of the loaded library. */
+int mars_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* mars_strerror(int status);
+
+/* ------------------------------------------------------------------------------------
+ * Training-layout attention (MARS §3.2, Eq. 2; prompt as a causal prefix).
+ *
+ * Positions 0..N-1, N = prompt_len + 2*resp_len, hold [prompt ; x ; x~]:
+ *   prompt  [0, P), clean stream x [P, P+L), noisy stream x~ [P+L, P+2L).
+ * Row r sees key j when
+ *   r < P + L (prompt or clean row):  j <= r                      (causal)
+ *   r >= P + L (noisy row), t0 = r - P - L, k = t0 / block:
+ *       j < P + k*block                 (the prompt and clean blocks before block k)
+ *    or P + L + k*block <= j <= r        (its own block, causal and self-inclusive)
+ * This is Eq. 2 with 1-indexed beta(t) = ceil(t/B) rewritten 0-indexed; a short last
+ * block (L % block != 0) is allowed.  Every row sees at least itself.
+ *
+ * Computes O = softmax(scale * Q K^T + M) V per (batch, query head); query head h
+ * reads KV head h / (n_q_heads / n_kv_heads) (grouped-query attention).
+ * ------------------------------------------------------------------------------------ */
+typedef struct mars_attn_desc {
+    int32_t batch;       /* >= 0 (0: nothing to do) */
+    int32_t n_q_heads;   /* >= 1, multiple of n_kv_heads */
+    int32_t n_kv_heads;  /* >= 1 */
+    int32_t head_dim;    /* 64 or 128 */
+    int32_t prompt_len;  /* P >= 0 */
+    int32_t resp_len;    /* L >= 0; N = P + 2L (N = 0: nothing to do) */
+    int32_t block;       /* B >= 1 */
+    int32_t dtype;       /* MARS_DTYPE_BF16 (MFMA path) or MARS_DTYPE_FP32 (fp32 vector path) */
+    float scale;         /* softmax scale; 0 means 1/sqrt(head_dim); must be finite */
+    int32_t reserved;    /* must be 0 */
+    int64_t q_strides[3]; /* q [batch][N][n_q_heads][head_dim]: batch, position, head */
+    int64_t k_strides[3]; /* k [batch][N][n_kv_heads][head_dim] */
+    int64_t v_strides[3]; /* v [batch][N][n_kv_heads][head_dim] */
+    int64_t o_strides[3]; /* o [batch][N][n_q_heads][head_dim] */
+} mars_attn_desc;
+
+/*
+ * q, k, v: inputs in desc->dtype.  o: output in desc->dtype (bf16 rounded to nearest
+ * even).  lse (optional, may be NULL): fp32 [batch][n_q_heads][N], contiguous, the
+ * natural-log log-sum-exp of each row's scaled, masked scores.  o must not alias q/k/v.
+ */
+int mars_attn_fwd(const mars_attn_desc* desc, const void* q, const void* k, const void* v,
+                  void* o, float* lse, hipStream_t stream);
+
+/*
+ * Host-only work counts for one (batch, query head) of a forward:
+ *   *nnz          = visible (query, key) pairs of the mask;
+ *   *visible_elems = in-range elements of the bm x bn tiles that are not fully masked.
+ * FLOPs of a forward = 4 * head_dim * count * batch * n_q_heads.  Either output may be NULL.
+ */
+int mars_attn_work(const mars_attn_desc* desc, int32_t bm, int32_t bn, int64_t* nnz,
+                   int64_t* visible_elems);
+
+/* Test support: the dense mask, uint8 [N][N] row-major (1 = visible), written on the
+ * device by the same visibility predicate the attention kernels use. */
+int mars_mask_materialize(const mars_attn_desc* desc, uint8_t* mask, hipStream_t stream);
+
+/* Test support: class of each bm x bn tile of the mask, int8 [ceil(N/bm)][ceil(N/bn)]
+ * row-major: 0 every in-range element masked, 2 every one visible, 1 mixed.
+ * 1 <= bm, bn <= 1024. */
+int mars_tile_map(const mars_attn_desc* desc, int32_t bm, int32_t bn, int8_t* map,
+                  hipStream_t stream);
+
+/*
+ * Test support: geometry of the bf16 forward's tile log (see mars_attn_fwd_tilelog).
+ * The bf16 kernel packs the G = n_q_heads/n_kv_heads query heads of a KV head as rows:
+ * row u of a (batch, kv head) pair is position u / G, query head kvh*G + u % G.
+ * It walks those rows in groups of *row_block and the keys in groups of *key_block.
+ * *rows_per_pair = N * G.  Outputs may be NULL.  MARS_EUNSUPPORTED for fp32.
+ */
+int mars_attn_tilelog_geometry(const mars_attn_desc* desc, int32_t* row_block,
+                               int32_t* key_block, int64_t* rows_per_pair);
+
+/*
+ * Test support: mars_attn_fwd (bf16 only) that also records, for every (batch, kv head,
+ * row group, key group), how the kernel treated that tile:
+ *   0 skipped, 1 computed with the element mask, 2 computed without it (all visible).
+ * A key group that runs past position N - 1 is always computed with the mask.
+ * tile_log: int8 [batch][n_kv_heads][ceil(N*G/row_block)][ceil(N/key_block)], device;
+ * the caller zero-fills it (skipped tiles are not written).
+ */
+int mars_attn_fwd_tilelog(const mars_attn_desc* desc, const void* q, const void* k,
+                          const void* v, void* o, float* lse, int8_t* tile_log,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Sliding-window decode step (MARS Fig. 2, right).
+ *
+ * For sequence b, window row i (0 <= i < window) and query head h (KV head
+ * g = h / (n_q_heads / n_kv_heads)) the visible keys are, in order,
+ *   cache positions [0, cache_len[b]) of k_cache/v_cache, then window rows 0..i of
+ *   k_win/v_win (causal and self-inclusive, like a noisy block of Eq. 2).
+ * o[b][i][h] = softmax(scale * q . keys) . values.  The cache is read only; committing
+ * accepted window KV into it is the caller's business.
+ * ------------------------------------------------------------------------------------ */
+typedef struct mars_decode_desc {
+    int32_t batch;          /* >= 0 */
+    int32_t n_q_heads;      /* >= 1, multiple of n_kv_heads */
+    int32_t n_kv_heads;     /* >= 1 */
+    int32_t head_dim;       /* 128 or 64 */
+    int32_t window;         /* 1 <= window; (n_q_heads/n_kv_heads) * window <= 64 */
+    int32_t cache_capacity; /* >= 0: positions allocated per (sequence, kv head) */
+    int32_t dtype;          /* MARS_DTYPE_BF16 */
+    float scale;            /* 0 means 1/sqrt(head_dim); must be finite */
+    int64_t qw_strides[3];  /* q_win [batch][window][n_q_heads][head_dim]: batch, row, head */
+    int64_t kw_strides[3];  /* k_win [batch][window][n_kv_heads][head_dim] */
+    int64_t vw_strides[3];  /* v_win */
+    int64_t kc_strides[3];  /* k_cache [batch][n_kv_heads][cache_capacity][head_dim]: batch, head, position */
+    int64_t vc_strides[3];  /* v_cache */
+    int64_t o_strides[3];   /* o [batch][window][n_q_heads][head_dim] */
+} mars_decode_desc;
+
+/* Workspace the decode step needs, in bytes (fp32 partial results of the cache split). */
+int mars_decode_workspace_bytes(const mars_decode_desc* desc, size_t* bytes);
+
+/*
+ * cache_len: int32 [batch] on the device; entries are clamped to [0, cache_capacity]
+ * by the kernels (an out-of-range entry never causes an out-of-bounds read).
+ * ws: device workspace of at least mars_decode_workspace_bytes; no initialisation needed.
+ * o: bf16 output.
+ */
+int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void* k_win,
+                     const void* v_win, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_len, void* o, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Confidence-threshold acceptance (MARS author blog, "Inference: a knob, not a mode
+ * switch"; greedy decoding).
+ *
+ * Per window row (b, i): m = max_v logit, token = lowest v with logit == m,
+ * pmax = 1 / sum_v exp(logit_v - m) (temperature-1 softmax over the full vocabulary).
+ * Per sequence: n_accept[b] = length of the leading run of rows with pmax >= tau,
+ * at least min_accept (= 1); tau >= 1 gives exactly 1 (exact AR decoding).
+ * ------------------------------------------------------------------------------------ */
+typedef struct mars_accept_desc {
+    int32_t batch;         /* >= 0 */
+    int32_t window;        /* 1 <= window <= 64 */
+    int32_t vocab;         /* >= 1 */
+    int32_t dtype;         /* MARS_DTYPE_BF16 */
+    int64_t batch_stride;  /* elements between sequences */
+    int64_t row_stride;    /* elements between window rows */
+    float tau;             /* 0 < tau (tau >= 1 means exact AR: one token) */
+    int32_t min_accept;    /* must be 1 */
+} mars_accept_desc;
+
+/* Workspace mars_accept needs, in bytes. */
+int mars_accept_workspace_bytes(const mars_accept_desc* desc, size_t* bytes);
+
+/*
+ * logits: bf16 [batch][window][vocab] (strided as in desc).  Outputs on the device:
+ * tokens int32 [batch][window], pmax fp32 [batch][window], n_accept int32 [batch].
+ * ws: at least mars_accept_workspace_bytes, zero-filled by the caller before its first
+ * use with mars_accept; every completed call leaves it zero-filled again.
+ */
+int mars_accept(const mars_accept_desc* desc, const void* logits, int32_t* tokens, float* pmax,
+                int32_t* n_accept, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MARS_H */

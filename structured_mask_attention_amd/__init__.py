@@ -1,0 +1,243 @@
+"""MARS structured-mask attention on MI355X: Python binding of libmars (include/mars.h).
+
+Same names as the C ABI.  Tensors are torch CUDA (ROCm) tensors used for device memory
+and streams only; every step of the computation runs in libmars's HIP kernels.  Calls
+are asynchronous on the current stream of the tensors' device.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "MarsError",
+    "mars_abi_version",
+    "mars_strerror",
+    "mars_attn_fwd",
+    "mars_attn_work",
+    "mars_mask_materialize",
+    "mars_tile_map",
+    "mars_attn_tilelog_geometry",
+    "mars_attn_fwd_tilelog",
+    "mars_decode_workspace_bytes",
+    "mars_decode_step",
+    "mars_accept_workspace_bytes",
+    "mars_accept",
+]
+
+
+class MarsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = L.load().mars_strerror(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != L.MARS_OK:
+        raise MarsError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return L.MARS_DTYPE_BF16
+    if dt == torch.float32:
+        return L.MARS_DTYPE_FP32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _s3(t, dims=(0, 1, 2)):
+    if t.numel() == 0:   # no element is ever addressed: report dense strides
+        dense = [1] * t.dim()
+        for i in range(t.dim() - 2, -1, -1):
+            dense[i] = dense[i + 1] * max(t.shape[i + 1], 1)
+        return L.I64x3(*(dense[i] for i in dims))
+    if t.stride(-1) != 1:
+        raise ValueError("innermost dimension must be contiguous")
+    return L.I64x3(*(t.stride(i) for i in dims))
+
+
+def mars_abi_version() -> int:
+    return L.load().mars_abi_version()
+
+
+def mars_strerror(status: int) -> str:
+    return L.load().mars_strerror(status).decode()
+
+
+def attn_desc(batch, hq, hkv, d, P, Lr, B, dtype=torch.bfloat16, scale=0.0, q=None, k=None, v=None, o=None):
+    desc = L.AttnDesc()
+    desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim = batch, hq, hkv, d
+    desc.prompt_len, desc.resp_len, desc.block = P, Lr, B
+    desc.dtype = _dtype_code(dtype)
+    desc.scale = float(scale)
+    desc.reserved = 0
+    N = P + 2 * Lr
+    dense_q = (N * hq * d, hq * d, d)
+    dense_kv = (N * hkv * d, hkv * d, d)
+    desc.q_strides = _s3(q) if q is not None else L.I64x3(*dense_q)
+    desc.k_strides = _s3(k) if k is not None else L.I64x3(*dense_kv)
+    desc.v_strides = _s3(v) if v is not None else L.I64x3(*dense_kv)
+    desc.o_strides = _s3(o) if o is not None else L.I64x3(*dense_q)
+    return desc
+
+
+def _attn_desc_from(q, k, v, o, P, Lr, B, scale):
+    b, N, hq, d = q.shape
+    hkv = k.shape[2]
+    if N != P + 2 * Lr:
+        raise ValueError(f"sequence length {N} != P + 2L = {P + 2 * Lr}")
+    if k.shape != (b, N, hkv, d) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("q/k/v/o shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise TypeError("q/k/v/o dtypes disagree")
+    return attn_desc(b, hq, hkv, d, P, Lr, B, q.dtype, scale, q, k, v, o)
+
+
+def mars_attn_fwd(q, k, v, prompt_len, resp_len, block, scale=0.0, out=None, lse=None):
+    """O = softmax(scale Q K^T + M) V over [prompt; x; x~]; q [b,N,Hq,D], k/v [b,N,Hkv,D].
+
+    ``lse``: optional fp32 [b, Hq, N] tensor to receive the log-sum-exp.  Returns ``out``.
+    """
+    out = torch.empty_like(q) if out is None else out
+    desc = _attn_desc_from(q, k, v, out, prompt_len, resp_len, block, scale)
+    _check(L.load().mars_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                  _stream(q)), "mars_attn_fwd")
+    return out
+
+
+def mars_attn_work(batch, hq, hkv, d, P, Lr, B, bm=128, bn=128, dtype=torch.bfloat16):
+    """(nnz, visible_elems) per (batch, head), host-side (see mars.h)."""
+    desc = attn_desc(batch, hq, hkv, d, P, Lr, B, dtype)
+    nnz, vis = ctypes.c_int64(), ctypes.c_int64()
+    _check(L.load().mars_attn_work(ctypes.byref(desc), bm, bn, ctypes.byref(nnz), ctypes.byref(vis)),
+           "mars_attn_work")
+    return nnz.value, vis.value
+
+
+def mars_mask_materialize(P, Lr, B, device="cuda"):
+    N = P + 2 * Lr
+    mask = torch.empty((N, N), dtype=torch.uint8, device=device)
+    desc = attn_desc(1, 1, 1, 64, P, Lr, B)
+    _check(L.load().mars_mask_materialize(ctypes.byref(desc), _ptr(mask), _stream(mask)), "mars_mask_materialize")
+    return mask
+
+
+def mars_tile_map(P, Lr, B, bm, bn, device="cuda"):
+    N = P + 2 * Lr
+    m = torch.empty(((N + bm - 1) // bm, (N + bn - 1) // bn), dtype=torch.int8, device=device)
+    desc = attn_desc(1, 1, 1, 64, P, Lr, B)
+    _check(L.load().mars_tile_map(ctypes.byref(desc), bm, bn, _ptr(m), _stream(m)), "mars_tile_map")
+    return m
+
+
+def mars_attn_tilelog_geometry(batch, hq, hkv, d, P, Lr, B):
+    desc = attn_desc(batch, hq, hkv, d, P, Lr, B)
+    rb, kb, rows = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(L.load().mars_attn_tilelog_geometry(ctypes.byref(desc), ctypes.byref(rb), ctypes.byref(kb),
+                                               ctypes.byref(rows)), "mars_attn_tilelog_geometry")
+    return rb.value, kb.value, rows.value
+
+
+def mars_attn_fwd_tilelog(q, k, v, prompt_len, resp_len, block, scale=0.0, out=None, lse=None):
+    """bf16 forward that also returns the kernel's tile log int8 [b, Hkv, row groups, key groups]."""
+    out = torch.empty_like(q) if out is None else out
+    desc = _attn_desc_from(q, k, v, out, prompt_len, resp_len, block, scale)
+    rb, kb, rows = mars_attn_tilelog_geometry(q.shape[0], q.shape[2], k.shape[2], q.shape[3],
+                                              prompt_len, resp_len, block)
+    N = q.shape[1]
+    log = torch.zeros((q.shape[0], k.shape[2], (rows + rb - 1) // rb, (N + kb - 1) // kb),
+                      dtype=torch.int8, device=q.device)
+    _check(L.load().mars_attn_fwd_tilelog(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                          _ptr(log), _stream(q)), "mars_attn_fwd_tilelog")
+    return out, log
+
+
+def decode_desc(batch, hq, hkv, d, W, cap, scale=0.0, qw=None, kw=None, vw=None, kc=None, vc=None, o=None):
+    desc = L.DecodeDesc()
+    desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim = batch, hq, hkv, d
+    desc.window, desc.cache_capacity = W, cap
+    desc.dtype = L.MARS_DTYPE_BF16
+    desc.scale = float(scale)
+    desc.qw_strides = _s3(qw) if qw is not None else L.I64x3(W * hq * d, hq * d, d)
+    desc.kw_strides = _s3(kw) if kw is not None else L.I64x3(W * hkv * d, hkv * d, d)
+    desc.vw_strides = _s3(vw) if vw is not None else L.I64x3(W * hkv * d, hkv * d, d)
+    desc.kc_strides = _s3(kc) if kc is not None else L.I64x3(hkv * cap * d, cap * d, d)
+    desc.vc_strides = _s3(vc) if vc is not None else L.I64x3(hkv * cap * d, cap * d, d)
+    desc.o_strides = _s3(o) if o is not None else L.I64x3(W * hq * d, hq * d, d)
+    return desc
+
+
+def mars_decode_workspace_bytes(batch, hq, hkv, d, W, cap):
+    desc = decode_desc(batch, hq, hkv, d, W, cap)
+    n = ctypes.c_size_t()
+    _check(L.load().mars_decode_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "mars_decode_workspace_bytes")
+    return n.value
+
+
+def mars_decode_step(q_win, k_win, v_win, k_cache, v_cache, cache_len, scale=0.0, out=None, ws=None):
+    """Window rows [b,W,Hq,D] attend to cache [b,Hkv,cap,D] prefix of cache_len[b] plus the causal window."""
+    b, W, hq, d = q_win.shape
+    hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if k_win.shape != (b, W, hkv, d) or v_win.shape != k_win.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("decode shapes disagree")
+    if cache_len.dtype != torch.int32 or cache_len.shape != (b,):
+        raise ValueError("cache_len must be int32 [batch]")
+    out = torch.empty_like(q_win) if out is None else out
+    desc = decode_desc(b, hq, hkv, d, W, cap, scale, q_win, k_win, v_win, k_cache, v_cache, out)
+    need = mars_decode_workspace_bytes(b, hq, hkv, d, W, cap)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q_win.device)
+    _check(L.load().mars_decode_step(ctypes.byref(desc), _ptr(q_win), _ptr(k_win), _ptr(v_win), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(ws), ws.numel(),
+                                     _stream(q_win)), "mars_decode_step")
+    return out
+
+
+def accept_desc(batch, W, V, tau, batch_stride=None, row_stride=None):
+    desc = L.AcceptDesc()
+    desc.batch, desc.window, desc.vocab = batch, W, V
+    desc.dtype = L.MARS_DTYPE_BF16
+    desc.batch_stride = W * V if batch_stride is None else batch_stride
+    desc.row_stride = V if row_stride is None else row_stride
+    desc.tau = float(tau)
+    desc.min_accept = 1
+    return desc
+
+
+def mars_accept_workspace_bytes(batch, W, V, tau=0.95):
+    desc = accept_desc(batch, W, V, tau)
+    n = ctypes.c_size_t()
+    _check(L.load().mars_accept_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "mars_accept_workspace_bytes")
+    return n.value
+
+
+def mars_accept(logits, tau, ws=None, tokens=None, pmax=None, n_accept=None):
+    """logits bf16 [b, W, V] -> (tokens int32 [b,W], pmax fp32 [b,W], n_accept int32 [b]).
+
+    ``ws`` must be zero-filled before its first use (a fresh one is made with torch.zeros).
+    """
+    b, W, V = logits.shape
+    if logits.stride(-1) != 1:
+        raise ValueError("vocab dimension must be contiguous")
+    desc = accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1))
+    dev = logits.device
+    tokens = torch.empty((b, W), dtype=torch.int32, device=dev) if tokens is None else tokens
+    pmax = torch.empty((b, W), dtype=torch.float32, device=dev) if pmax is None else pmax
+    n_accept = torch.empty((b,), dtype=torch.int32, device=dev) if n_accept is None else n_accept
+    if ws is None:
+        ws = torch.zeros(max(mars_accept_workspace_bytes(b, W, V, tau), 16), dtype=torch.uint8, device=dev)
+    _check(L.load().mars_accept(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(pmax), _ptr(n_accept),
+                                _ptr(ws), ws.numel(), _stream(logits)), "mars_accept")
+    return tokens, pmax, n_accept

@@ -1,0 +1,451 @@
+// Training-layout attention over [prompt ; x ; x~] with the MARS structured mask
+// ("MARS: Enabling Autoregressive Models Multi-Token Generation", §3.2 Eq. 2 and Fig. 2
+// left; the prompt is a causal prefix seen by every response row).
+//
+// bf16 path (gfx950 MFMA):
+//   * Rows: the G = Hq/Hkv query heads of one KV head are packed as rows (row u of a
+//     (batch, kv head) pair = position u / G, head kvh*G + u % G), so every K/V tile a
+//     workgroup stages in LDS serves G heads.  A workgroup owns 256 such rows (4 waves x
+//     64 rows); a wave owns two 32-row column blocks.
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the K
+//     tile is the A operand (read from LDS), the wave's Q rows the B operand (registers for
+//     the whole kernel).  In the output layout a lane owns one query row and 16 of the 32
+//     keys, its partner lane (l ^ 32) the other 16, so row max/sum need one permlane32 swap.
+//   * O^T += V^T P^T: P^T comes straight from the score registers (bf16, RNE); V^T is read
+//     from the natural [key][d] LDS tile with ds_read_b64_tr_b16 (transposing 16-bit read).
+//   * Keys are walked in 32-key tiles over at most two intervals per workgroup (the union
+//     of its rows' visible keys, see mars_device.h); each wave classifies every tile for its
+//     own rows: skipped, computed with the element mask, or computed without it.
+//   * Online softmax in the log2 domain, fp32 statistics, fp32 MFMA accumulation.
+//   * Workgroup order: heaviest row tiles first (noisy and clean tiles from the far end,
+//     interleaved, then the prompt); the (batch, kv head) index is the fastest-varying part
+//     of the workgroup id, so the round-robin dispatch over the 8 XCDs keeps each pair's
+//     K/V on few L2s.
+//
+// fp32 path: one thread per query row on the vector ALUs, fp32 throughout (for fp32
+// inputs; a correctness path, not a tuned one).
+#include <cmath>
+
+#include "mars_device.h"
+#include "mars_internal.h"
+
+namespace mars {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kNcb = 2;                              // 32-row column blocks per wave
+constexpr int kRowsPerWave = 32 * kNcb;              // == kAttnRowBlock
+constexpr int kRowsPerWG = kWaves * kRowsPerWave;    // 256
+constexpr int kKT = kAttnKeyBlock;                   // 32 keys per LDS tile
+static_assert(kRowsPerWave == kAttnRowBlock, "row block");
+
+struct AttnKParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    int8_t* tilelog;
+    int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+    int hq, hkv, G, P, L, B, N;
+    int rows_per_pair;   // N * G
+    int tiles_per_pair;  // ceil(rows_per_pair / 256)
+    int tN0;             // first row tile whose first row is a noisy position
+    int bg_count;        // batch * hkv
+    int key_tiles;       // ceil(N / 32)
+    int row_groups;      // ceil(rows_per_pair / 64)
+    float scale_log2;    // scale * log2(e)
+};
+
+// Workgroup rank -> row tile: noisy tiles from the end interleaved with the other tiles
+// from the end of the clean stream, then whatever remains, in descending order.
+__device__ inline int rank_to_tile(int rank, int T, int tN0) {
+    const int nN = T - tN0, nR = tN0;
+    const int m = nN < nR ? nN : nR;
+    if (rank < 2 * m) return (rank & 1) ? (tN0 - 1 - (rank >> 1)) : (T - 1 - (rank >> 1));
+    const int rr = rank - 2 * m;
+    return (nN > m) ? (T - 1 - m - rr) : (tN0 - 1 - m - rr);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(AttnKParams p) {
+    constexpr int KSTR = D + 8;         // K tile row stride (elements)
+    constexpr int VSTR = D + 32;        // V tile row stride (elements)
+    constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
+    constexpr int NDB = D / 32;         // 32-row d blocks of O^T
+    constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+    constexpr int LOADS = (kKT * CPR) / 256;
+    static_assert(LOADS >= 1 && (kKT * CPR) % 256 == 0, "tile load split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * VSTR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hl = lane & 31, g2 = lane >> 5;
+
+    const int bg = blockIdx.x % p.bg_count;
+    const int rank = blockIdx.x / p.bg_count;
+    const int tile = rank_to_tile(rank, p.tiles_per_pair, p.tN0);
+    const int b = bg / p.hkv, g = bg % p.hkv;
+    const int row0 = tile * kRowsPerWG;
+    const int wrow0 = row0 + wave * kRowsPerWave;
+
+    // This lane's query rows (one per column block).
+    int pos[kNcb], head[kNcb];
+    bool valid[kNcb];
+    RowBounds rb[kNcb];
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+        const int u = wrow0 + cb * 32 + hl;
+        valid[cb] = u < p.rows_per_pair;
+        const int uu = valid[cb] ? u : p.rows_per_pair - 1;
+        pos[cb] = uu / p.G;
+        head[cb] = g * p.G + uu % p.G;
+        rb[cb] = row_bounds(pos[cb], p.P, p.L, p.B);
+    }
+
+    // Q^T operand: lane holds Q[row][16c + 8*g2 .. +7] for every chunk c.
+    bf16x8_t qf[kNcb][NC];
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+        const uint16_t* qp = p.q + b * p.qs0 + (int64_t)pos[cb] * p.qs1 + (int64_t)head[cb] * p.qs2 + 8 * g2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (valid[cb]) {
+                qf[cb][c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
+            } else {
+                qf[cb][c] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    }
+
+    // Union of the workgroup's visible keys: [0, endA) and [startC, endC).
+    const int u_last = min(row0 + kRowsPerWG, p.rows_per_pair) - 1;
+    const int pf = row0 / p.G, pl = u_last / p.G;
+    const int PL = p.P + p.L;
+    int endA = 0, startC = 0, endC = 0;
+    if (pf < PL) endA = min(pl, PL - 1) + 1;
+    if (pl >= PL) {
+        endA = max(endA, p.P + ((pl - PL) / p.B) * p.B);
+        startC = PL + ((max(pf, PL) - PL) / p.B) * p.B;
+        endC = pl + 1;
+    }
+    const int nA = (endA + kKT - 1) / kKT;
+    int c0t = startC / kKT;
+    const int c1t = (endC + kKT - 1) / kKT;
+    if (c0t < nA) c0t = nA;
+    const int nCt = c1t > c0t ? c1t - c0t : 0;
+    const int ntiles = nA + nCt;
+
+    const uint16_t* kbase = p.k + b * p.ks0 + (int64_t)g * p.ks2;
+    const uint16_t* vbase = p.v + b * p.vs0 + (int64_t)g * p.vs2;
+    bf16x8_t kreg[LOADS], vreg[LOADS];
+
+    auto tile_of = [&](int it) { return it < nA ? it : c0t + (it - nA); };
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int idx = tid + 256 * i;
+            const int key = kt * kKT + idx / CPR;
+            const int ch = idx % CPR;
+            if (key < p.N) {
+                kreg[i] = *reinterpret_cast<const bf16x8_t*>(kbase + (int64_t)key * p.ks1 + 8 * ch);
+                vreg[i] = *reinterpret_cast<const bf16x8_t*>(vbase + (int64_t)key * p.vs1 + 8 * ch);
+            } else {
+                kreg[i] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                vreg[i] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int idx = tid + 256 * i;
+            const int kl = idx / CPR, ch = idx % CPR;
+            *reinterpret_cast<bf16x8_t*>(&sK[buf][kl * KSTR + 8 * ch]) = kreg[i];
+            *reinterpret_cast<bf16x8_t*>(&sV[buf][kl * VSTR + 8 * ch]) = vreg[i];
+        }
+    };
+
+    float m_run[kNcb], l_run[kNcb];
+    f32x16_t acc[kNcb][NDB];
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[cb][db][e] = 0.f;
+        }
+    }
+
+    const bool wave_has_rows = wrow0 < p.rows_per_pair;
+    int8_t* logrow = nullptr;
+    if (p.tilelog && wave_has_rows)
+        logrow = p.tilelog + ((int64_t)bg * p.row_groups + wrow0 / kRowsPerWave) * p.key_tiles;
+
+    // Transposed-read addressing for V^T (see header comment): lane (s16, grp) reads 4
+    // bf16 at V[16kh + 4*(grp>>1) + s16/4 (+8)][32db + 16*(grp&1) + 4*(s16&3)].
+    const int s16 = lane & 15, grp = lane >> 4;
+    const int vkey = 4 * (grp >> 1) + (s16 >> 2);
+    const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);
+
+    gload(tile_of(0));
+    swrite(0);
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int kt = tile_of(it);
+        const int buf = it & 1;
+        if (it + 1 < ntiles) gload(tile_of(it + 1));
+
+        const int kb = kt * kKT;
+        const int ke = min(kb + kKT, p.N);
+        bool lany = false, lall = true;
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) {
+            if (valid[cb]) {
+                lany |= range_any(pos[cb], kb, ke, rb[cb]);
+                lall &= range_all(pos[cb], kb, ke, rb[cb]);
+            }
+        }
+        const bool wany = __ballot(lany) != 0ull;
+        const bool wall = (kb + kKT <= p.N) && (__ballot(!lall) == 0ull);
+        if (logrow && lane == 0 && wany) logrow[kt] = wall ? 2 : 1;
+
+        if (wany) {
+            f32x16_t s[kNcb];
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[cb][e] = 0.f;
+            }
+            const uint16_t* kl = &sK[buf][hl * KSTR + 8 * g2];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kl + 16 * c);
+#pragma unroll
+                for (int cb = 0; cb < kNcb; ++cb)
+                    s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][c], s[cb], 0, 0, 0);
+            }
+            if (!wall) {
+#pragma unroll
+                for (int cb = 0; cb < kNcb; ++cb) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = kb + 8 * (e >> 2) + 4 * g2 + (e & 3);
+                        if (!key_visible(pos[cb], j, rb[cb])) s[cb][e] = -INFINITY;
+                    }
+                }
+            }
+            bf16x8_t pb[kNcb][2];
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) {
+                float mx = s[cb][0];
+#pragma unroll
+                for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[cb][e]);
+                mx = half_swap_max(mx);
+                const float mnew = fmaxf(m_run[cb], mx * p.scale_log2);
+                const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+                const float alpha = exp2f(m_run[cb] - msafe);
+                m_run[cb] = mnew;
+                float pv[16];
+                float rs = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    pv[e] = exp2f(fmaf(s[cb][e], p.scale_log2, -msafe));
+                    rs += pv[e];
+                }
+                l_run[cb] = fmaf(l_run[cb], alpha, rs);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                }
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
+                    uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
+                    uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
+                    uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
+                    typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+                    u32x4_t w = {w0, w1, w2, w3};
+                    pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
+                }
+            }
+            const uint16_t* vt = &sV[buf][0];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const uint16_t* a0 = vt + (16 * kh + vkey) * VSTR + 32 * db + vcol;
+                    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(a0));
+                    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(a0 + 8 * VSTR));
+                    const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int cb = 0; cb < kNcb; ++cb)
+                        acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cb][kh], acc[cb][db], 0, 0, 0);
+                }
+            }
+        }
+        if (it + 1 < ntiles) swrite(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2.
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+        const float lt = half_swap_sum(l_run[cb]);
+        const float inv = 1.f / lt;
+        if (valid[cb]) {
+            uint16_t* op = p.o + b * p.os0 + (int64_t)pos[cb] * p.os1 + (int64_t)head[cb] * p.os2;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int d = 32 * db + 8 * bb + 4 * g2;
+                    uint2 w;
+                    w.x = pack_bf16x2(acc[cb][db][4 * bb + 0] * inv, acc[cb][db][4 * bb + 1] * inv);
+                    w.y = pack_bf16x2(acc[cb][db][4 * bb + 2] * inv, acc[cb][db][4 * bb + 3] * inv);
+                    *reinterpret_cast<uint2*>(op + d) = w;
+                }
+            }
+            if (p.lse && g2 == 0)
+                p.lse[((int64_t)b * p.hq + head[cb]) * p.N + pos[cb]] = (m_run[cb] + log2f(lt)) * kLn2;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32 vector path: thread = query row; grid (ceil(N/64), Hq, batch).
+// ---------------------------------------------------------------------------------------
+struct AttnF32Params {
+    const float* q;
+    const float* k;
+    const float* v;
+    float* o;
+    float* lse;
+    int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+    int hq, G, P, L, B, N;
+    float scale;
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnF32Params p) {
+    const int r0 = blockIdx.x * 64;
+    const int r = r0 + threadIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z, g = h / p.G;
+    const bool valid = r < p.N;
+    const int rr = valid ? r : p.N - 1;
+    const RowBounds rb = row_bounds(rr, p.P, p.L, p.B);
+
+    float q[D], acc[D];
+    const float* qp = p.q + b * p.qs0 + (int64_t)rr * p.qs1 + (int64_t)h * p.qs2;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        q[d] = qp[d];
+        acc[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    const int jmax = min(r0 + 63, p.N - 1);
+    const float* kb = p.k + b * p.ks0 + (int64_t)g * p.ks2;
+    const float* vb = p.v + b * p.vs0 + (int64_t)g * p.vs2;
+    for (int j = 0; j <= jmax; ++j) {
+        const float* kp = kb + (int64_t)j * p.ks1;
+        float sdot = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) sdot = fmaf(q[d], kp[d], sdot);
+        if (key_visible(rr, j, rb)) {
+            const float sc = sdot * p.scale;
+            const float mnew = fmaxf(m, sc);
+            const float alpha = expf(m - mnew);
+            const float pj = expf(sc - mnew);
+            l = fmaf(l, alpha, pj);
+            const float* vp = vb + (int64_t)j * p.vs1;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], alpha, pj * vp[d]);
+            m = mnew;
+        }
+    }
+    if (valid) {
+        float* op = p.o + b * p.os0 + (int64_t)r * p.os1 + (int64_t)h * p.os2;
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+        if (p.lse) p.lse[((int64_t)b * p.hq + h) * p.N + r] = m + logf(l);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
+    AttnKParams p;
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k = static_cast<const uint16_t*>(a.k);
+    p.v = static_cast<const uint16_t*>(a.v);
+    p.o = static_cast<uint16_t*>(a.o);
+    p.lse = a.lse;
+    p.tilelog = a.tilelog;
+    p.qs0 = a.qs[0]; p.qs1 = a.qs[1]; p.qs2 = a.qs[2];
+    p.ks0 = a.ks[0]; p.ks1 = a.ks[1]; p.ks2 = a.ks[2];
+    p.vs0 = a.vs[0]; p.vs1 = a.vs[1]; p.vs2 = a.vs[2];
+    p.os0 = a.os[0]; p.os1 = a.os[1]; p.os2 = a.os[2];
+    p.hq = a.hq;
+    p.hkv = a.hkv;
+    p.G = a.hq / a.hkv;
+    p.P = a.P;
+    p.L = a.L;
+    p.B = a.B;
+    p.N = a.N;
+    p.rows_per_pair = a.N * p.G;
+    p.tiles_per_pair = (p.rows_per_pair + kRowsPerWG - 1) / kRowsPerWG;
+    const int64_t noisy_row0 = (int64_t)(a.P + a.L) * p.G;
+    int tN0 = (int)((noisy_row0 + kRowsPerWG - 1) / kRowsPerWG);
+    if (tN0 > p.tiles_per_pair) tN0 = p.tiles_per_pair;
+    p.tN0 = tN0;
+    p.bg_count = a.batch * a.hkv;
+    p.key_tiles = (a.N + kKT - 1) / kKT;
+    p.row_groups = (p.rows_per_pair + kRowsPerWave - 1) / kRowsPerWave;
+    p.scale_log2 = a.scale * kLog2e;
+    const int64_t grid = (int64_t)p.tiles_per_pair * p.bg_count;
+    if (grid == 0) return hipSuccess;
+    if (a.d == 128) {
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s) {
+    AttnF32Params p;
+    p.q = static_cast<const float*>(a.q);
+    p.k = static_cast<const float*>(a.k);
+    p.v = static_cast<const float*>(a.v);
+    p.o = static_cast<float*>(a.o);
+    p.lse = a.lse;
+    p.qs0 = a.qs[0]; p.qs1 = a.qs[1]; p.qs2 = a.qs[2];
+    p.ks0 = a.ks[0]; p.ks1 = a.ks[1]; p.ks2 = a.ks[2];
+    p.vs0 = a.vs[0]; p.vs1 = a.vs[1]; p.vs2 = a.vs[2];
+    p.os0 = a.os[0]; p.os1 = a.os[1]; p.os2 = a.os[2];
+    p.hq = a.hq;
+    p.G = a.hq / a.hkv;
+    p.P = a.P;
+    p.L = a.L;
+    p.B = a.B;
+    p.N = a.N;
+    p.scale = a.scale;
+    if (a.N == 0 || a.batch == 0) return hipSuccess;
+    dim3 grid((a.N + 63) / 64, a.hq, a.batch);
+    if (a.d == 128) {
+        hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(64), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(64), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mars

@@ -1,0 +1,305 @@
+// C ABI of libmars (include/mars.h): argument validation, then kernel launches on the
+// caller's stream.  Validation is complete before anything is launched, so an error
+// leaves every buffer untouched.  Nothing here allocates device memory or keeps state.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/mars.h"
+#include "mars_device.h"
+#include "mars_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Strides: non-negative and keep 16-byte alignment of every row start.
+bool strides_ok(const int64_t s[3], int elem_bytes) {
+    const int64_t unit = 16 / elem_bytes;
+    for (int i = 0; i < 3; ++i) {
+        if (s[i] < 0 || s[i] % unit != 0) return false;
+    }
+    return true;
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? MARS_OK : MARS_EHIP; }
+
+int check_attn_desc(const mars_attn_desc* d) {
+    if (!d) return MARS_EINVAL;
+    if (d->batch < 0 || d->n_q_heads < 1 || d->n_kv_heads < 1) return MARS_EINVAL;
+    if (d->n_q_heads % d->n_kv_heads != 0) return MARS_EINVAL;
+    if (d->prompt_len < 0 || d->resp_len < 0 || d->block < 1) return MARS_EINVAL;
+    if (d->reserved != 0) return MARS_EINVAL;
+    if (!isfinite(d->scale) || d->scale < 0.f) return MARS_EINVAL;
+    if (d->dtype != MARS_DTYPE_BF16 && d->dtype != MARS_DTYPE_FP32) return MARS_EINVAL;
+    const int64_t N = (int64_t)d->prompt_len + 2 * (int64_t)d->resp_len;
+    if (N > (1 << 24)) return MARS_EUNSUPPORTED;
+    if ((int64_t)N * (d->n_q_heads / d->n_kv_heads) > INT32_MAX / 2) return MARS_EUNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128) return MARS_EUNSUPPORTED;
+    return MARS_OK;
+}
+
+int64_t attn_N(const mars_attn_desc* d) { return (int64_t)d->prompt_len + 2 * (int64_t)d->resp_len; }
+
+float eff_scale(float scale, int head_dim) { return scale == 0.f ? 1.f / sqrtf((float)head_dim) : scale; }
+
+int check_attn_tensors(const mars_attn_desc* d, const void* q, const void* k, const void* v, const void* o,
+                       const float* lse) {
+    if (!q || !k || !v || !o) return MARS_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MARS_EINVAL;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return MARS_EINVAL;
+    const int eb = d->dtype == MARS_DTYPE_BF16 ? 2 : 4;
+    if (!strides_ok(d->q_strides, eb) || !strides_ok(d->k_strides, eb) || !strides_ok(d->v_strides, eb) ||
+        !strides_ok(d->o_strides, eb))
+        return MARS_EINVAL;
+    return MARS_OK;
+}
+
+mars::AttnArgs make_attn_args(const mars_attn_desc* d, const void* q, const void* k, const void* v, void* o,
+                              float* lse, int8_t* tilelog) {
+    mars::AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.tilelog = tilelog;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = d->q_strides[i];
+        a.ks[i] = d->k_strides[i];
+        a.vs[i] = d->v_strides[i];
+        a.os[i] = d->o_strides[i];
+    }
+    a.batch = d->batch;
+    a.hq = d->n_q_heads;
+    a.hkv = d->n_kv_heads;
+    a.d = d->head_dim;
+    a.P = d->prompt_len;
+    a.L = d->resp_len;
+    a.B = d->block;
+    a.N = (int)attn_N(d);
+    a.scale = eff_scale(d->scale, d->head_dim);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mars_abi_version(void) { return MARS_ABI_VERSION; }
+
+const char* mars_strerror(int status) {
+    switch (status) {
+        case MARS_OK: return "success";
+        case MARS_EINVAL: return "invalid argument (shape, enum, tau, null pointer, alignment or stride)";
+        case MARS_EUNSUPPORTED: return "unsupported configuration (head_dim, dtype, window or size)";
+        case MARS_EWORKSPACE: return "workspace missing or too small";
+        case MARS_EHIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int mars_attn_fwd(const mars_attn_desc* desc, const void* q, const void* k, const void* v, void* o, float* lse,
+                  hipStream_t stream) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (desc->batch == 0 || attn_N(desc) == 0) return MARS_OK;
+    st = check_attn_tensors(desc, q, k, v, o, lse);
+    if (st) return st;
+    const mars::AttnArgs a = make_attn_args(desc, q, k, v, o, lse, nullptr);
+    if (desc->dtype == MARS_DTYPE_BF16) return map_hip(mars::launch_attn_fwd_bf16(a, stream));
+    return map_hip(mars::launch_attn_fwd_f32(a, stream));
+}
+
+int mars_attn_tilelog_geometry(const mars_attn_desc* desc, int32_t* row_block, int32_t* key_block,
+                               int64_t* rows_per_pair) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (desc->dtype != MARS_DTYPE_BF16) return MARS_EUNSUPPORTED;
+    if (row_block) *row_block = mars::kAttnRowBlock;
+    if (key_block) *key_block = mars::kAttnKeyBlock;
+    if (rows_per_pair) *rows_per_pair = attn_N(desc) * (desc->n_q_heads / desc->n_kv_heads);
+    return MARS_OK;
+}
+
+int mars_attn_fwd_tilelog(const mars_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                          float* lse, int8_t* tile_log, hipStream_t stream) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (desc->dtype != MARS_DTYPE_BF16) return MARS_EUNSUPPORTED;
+    if (desc->batch == 0 || attn_N(desc) == 0) return MARS_OK;
+    st = check_attn_tensors(desc, q, k, v, o, lse);
+    if (st) return st;
+    if (!tile_log) return MARS_EINVAL;
+    const mars::AttnArgs a = make_attn_args(desc, q, k, v, o, lse, tile_log);
+    return map_hip(mars::launch_attn_fwd_bf16(a, stream));
+}
+
+int mars_attn_work(const mars_attn_desc* desc, int32_t bm, int32_t bn, int64_t* nnz, int64_t* visible_elems) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (bm < 1 || bn < 1) return MARS_EINVAL;
+    const int P = desc->prompt_len, L = desc->resp_len, B = desc->block;
+    const int N = (int)attn_N(desc);
+    if (nnz) {
+        int64_t total = 0;
+        for (int r = 0; r < N; ++r) {
+            const mars::RowBounds rb = mars::row_bounds(r, P, L, B);
+            total += rb.hi1 + std::max(0, r + 1 - rb.lo2);
+        }
+        *nnz = total;
+    }
+    if (visible_elems) {
+        int64_t total = 0;
+        for (int r0 = 0; r0 < N; r0 += bm) {
+            const int r1 = std::min(N, r0 + bm);
+            for (int c0 = 0; c0 < N; c0 += bn) {
+                const int c1 = std::min(N, c0 + bn);
+                bool any = false;
+                for (int r = r0; r < r1 && !any; ++r) any = mars::range_any(r, c0, c1, mars::row_bounds(r, P, L, B));
+                if (any) total += (int64_t)(r1 - r0) * (c1 - c0);
+            }
+        }
+        *visible_elems = total;
+    }
+    return MARS_OK;
+}
+
+int mars_mask_materialize(const mars_attn_desc* desc, uint8_t* mask, hipStream_t stream) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (!mask) return MARS_EINVAL;
+    const int64_t N = attn_N(desc);
+    if (N > 65535) return MARS_EUNSUPPORTED;
+    return map_hip(mars::launch_mask_materialize(desc->prompt_len, desc->resp_len, desc->block, mask, stream));
+}
+
+int mars_tile_map(const mars_attn_desc* desc, int32_t bm, int32_t bn, int8_t* map, hipStream_t stream) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (!map || bm < 1 || bn < 1 || bm > 1024 || bn > 1024) return MARS_EINVAL;
+    const int64_t N = attn_N(desc);
+    if ((N + bm - 1) / bm > 65535 || (N + bn - 1) / bn > (1 << 30)) return MARS_EUNSUPPORTED;
+    return map_hip(mars::launch_tile_map(desc->prompt_len, desc->resp_len, desc->block, bm, bn, map, stream));
+}
+
+// ---------------------------------------------------------------------------------------
+
+static int check_decode_desc(const mars_decode_desc* d) {
+    if (!d) return MARS_EINVAL;
+    if (d->batch < 0 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->window < 1 || d->cache_capacity < 0)
+        return MARS_EINVAL;
+    if (d->n_q_heads % d->n_kv_heads != 0) return MARS_EINVAL;
+    if (!isfinite(d->scale) || d->scale < 0.f) return MARS_EINVAL;
+    if (d->dtype != MARS_DTYPE_BF16) return d->dtype == MARS_DTYPE_FP32 ? MARS_EUNSUPPORTED : MARS_EINVAL;
+    if (d->head_dim != 64 && d->head_dim != 128) return MARS_EUNSUPPORTED;
+    if ((int64_t)(d->n_q_heads / d->n_kv_heads) * d->window > 64) return MARS_EUNSUPPORTED;
+    if (d->batch > 65535 || d->n_kv_heads > 65535) return MARS_EUNSUPPORTED;
+    return MARS_OK;
+}
+
+int mars_decode_workspace_bytes(const mars_decode_desc* desc, size_t* bytes) {
+    int st = check_decode_desc(desc);
+    if (st) return st;
+    if (!bytes) return MARS_EINVAL;
+    *bytes = mars::decode_workspace_bytes(desc->batch, desc->n_kv_heads, desc->n_q_heads / desc->n_kv_heads,
+                                          desc->window, desc->head_dim, desc->cache_capacity);
+    return MARS_OK;
+}
+
+int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void* k_win, const void* v_win,
+                     const void* k_cache, const void* v_cache, const int32_t* cache_len, void* o, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    int st = check_decode_desc(desc);
+    if (st) return st;
+    if (desc->batch == 0) return MARS_OK;
+    if (!q_win || !k_win || !v_win || !cache_len || !o) return MARS_EINVAL;
+    if (desc->cache_capacity > 0 && (!k_cache || !v_cache)) return MARS_EINVAL;
+    if (!aligned16(q_win) || !aligned16(k_win) || !aligned16(v_win) || !aligned16(o) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(cache_len) & 3u))
+        return MARS_EINVAL;
+    if (!strides_ok(desc->qw_strides, 2) || !strides_ok(desc->kw_strides, 2) || !strides_ok(desc->vw_strides, 2) ||
+        !strides_ok(desc->kc_strides, 2) || !strides_ok(desc->vc_strides, 2) || !strides_ok(desc->o_strides, 2))
+        return MARS_EINVAL;
+    const size_t need = mars::decode_workspace_bytes(desc->batch, desc->n_kv_heads,
+                                                     desc->n_q_heads / desc->n_kv_heads, desc->window,
+                                                     desc->head_dim, desc->cache_capacity);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MARS_EWORKSPACE;
+    mars::DecodeArgs a;
+    a.qw = q_win;
+    a.kw = k_win;
+    a.vw = v_win;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.cache_len = cache_len;
+    a.o = o;
+    a.ws = ws;
+    for (int i = 0; i < 3; ++i) {
+        a.qws[i] = desc->qw_strides[i];
+        a.kws[i] = desc->kw_strides[i];
+        a.vws[i] = desc->vw_strides[i];
+        a.kcs[i] = desc->kc_strides[i];
+        a.vcs[i] = desc->vc_strides[i];
+        a.os[i] = desc->o_strides[i];
+    }
+    a.batch = desc->batch;
+    a.hq = desc->n_q_heads;
+    a.hkv = desc->n_kv_heads;
+    a.d = desc->head_dim;
+    a.W = desc->window;
+    a.cap = desc->cache_capacity;
+    a.scale = eff_scale(desc->scale, desc->head_dim);
+    return map_hip(mars::launch_decode(a, stream));
+}
+
+// ---------------------------------------------------------------------------------------
+
+static int check_accept_desc(const mars_accept_desc* d) {
+    if (!d) return MARS_EINVAL;
+    if (d->batch < 0 || d->window < 1 || d->vocab < 1) return MARS_EINVAL;
+    if (d->window > 64) return MARS_EUNSUPPORTED;
+    if (d->dtype != MARS_DTYPE_BF16) return d->dtype == MARS_DTYPE_FP32 ? MARS_EUNSUPPORTED : MARS_EINVAL;
+    if (!(d->tau > 0.f) || !isfinite(d->tau)) return MARS_EINVAL;
+    if (d->min_accept != 1) return MARS_EINVAL;
+    if (d->batch > 65535) return MARS_EUNSUPPORTED;
+    return MARS_OK;
+}
+
+int mars_accept_workspace_bytes(const mars_accept_desc* desc, size_t* bytes) {
+    int st = check_accept_desc(desc);
+    if (st) return st;
+    if (!bytes) return MARS_EINVAL;
+    *bytes = mars::accept_workspace_bytes(desc->batch, desc->window, desc->vocab);
+    return MARS_OK;
+}
+
+int mars_accept(const mars_accept_desc* desc, const void* logits, int32_t* tokens, float* pmax, int32_t* n_accept,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_accept_desc(desc);
+    if (st) return st;
+    if (desc->batch == 0) return MARS_OK;
+    if (!logits || !tokens || !pmax || !n_accept) return MARS_EINVAL;
+    if (desc->batch_stride < 0 || desc->row_stride < 0 || desc->batch_stride % 8 || desc->row_stride % 8)
+        return MARS_EINVAL;
+    if (!aligned16(logits) || (reinterpret_cast<uintptr_t>(tokens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(pmax) & 3u) || (reinterpret_cast<uintptr_t>(n_accept) & 3u))
+        return MARS_EINVAL;
+    const size_t need = mars::accept_workspace_bytes(desc->batch, desc->window, desc->vocab);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MARS_EWORKSPACE;
+    mars::AcceptArgs a;
+    a.logits = logits;
+    a.tokens = tokens;
+    a.pmax = pmax;
+    a.n_accept = n_accept;
+    a.ws = ws;
+    a.batch_stride = desc->batch_stride;
+    a.row_stride = desc->row_stride;
+    a.batch = desc->batch;
+    a.W = desc->window;
+    a.V = desc->vocab;
+    a.tau = desc->tau;
+    return map_hip(mars::launch_accept(a, stream));
+}
+
+}  // extern "C"

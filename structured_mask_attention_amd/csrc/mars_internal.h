@@ -1,0 +1,65 @@
+// Internal launch interface between the C ABI layer (mars_api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mars {
+
+// Training-layout forward (attn_fwd.hip).
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;        // may be null
+    int8_t* tilelog;   // may be null (bf16 path only)
+    int64_t qs[3], ks[3], vs[3], os[3];
+    int batch, hq, hkv, d, P, L, B, N;
+    float scale;       // > 0
+};
+
+// Geometry of the bf16 forward's row/key grouping (for the tile log).
+constexpr int kAttnRowBlock = 64;   // rows per wave
+constexpr int kAttnKeyBlock = 32;   // keys per LDS tile
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);
+
+// Debug mask kernels (mask_kernels.hip).
+hipError_t launch_mask_materialize(int P, int L, int B, uint8_t* mask, hipStream_t s);
+hipError_t launch_tile_map(int P, int L, int B, int bm, int bn, int8_t* map, hipStream_t s);
+
+// Decode step (decode.hip).
+struct DecodeArgs {
+    const void* qw;
+    const void* kw;
+    const void* vw;
+    const void* kc;
+    const void* vc;
+    const int32_t* cache_len;
+    void* o;
+    void* ws;
+    int64_t qws[3], kws[3], vws[3], kcs[3], vcs[3], os[3];
+    int batch, hq, hkv, d, W, cap;
+    float scale;
+};
+size_t decode_workspace_bytes(int batch, int hkv, int G, int W, int d, int cap);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Acceptance (accept.hip).
+struct AcceptArgs {
+    const void* logits;
+    int32_t* tokens;
+    float* pmax;
+    int32_t* n_accept;
+    void* ws;
+    int64_t batch_stride, row_stride;
+    int batch, W, V;
+    float tau;
+};
+size_t accept_workspace_bytes(int batch, int W, int V);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
+
+}  // namespace mars

@@ -1,0 +1,152 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared entry point,
+validates arguments before launching anything, and its host-side work counts agree with
+the oracle.  No call here reaches a kernel launch (no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import structured_mask_attention_amd as M
+from oracle import mars_oracle as O
+from structured_mask_attention_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000           # aligned dummy device address (never dereferenced: validation fails first)
+MISALIGNED = 0x10002
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mars.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mars_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.load()
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.exported_symbols()) == names
+    assert M.mars_abi_version() == 1
+
+
+def test_strerror_codes():
+    for code in (0, -1, -2, -3, -4):
+        assert M.mars_strerror(code) and M.mars_strerror(code) != "unknown status"
+    assert M.mars_strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("P,Lr,B", [(16, 64, 4), (256, 512, 4), (512, 1536, 8), (3, 37, 8), (0, 1, 1), (5, 0, 2)])
+def test_attn_work_matches_oracle(P, Lr, B):
+    nnz, vis = M.mars_attn_work(1, 1, 1, 64, P, Lr, B, 128, 128)
+    assert nnz == O.mask_nnz(P, Lr, B)
+    assert vis == O.visible_tile_elems(P, Lr, B, 128, 128)
+    nnz2, vis2 = M.mars_attn_work(1, 1, 1, 64, P, Lr, B, 16, 48)
+    assert vis2 == O.visible_tile_elems(P, Lr, B, 16, 48)
+
+
+def _attn(desc, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
+    return L.load().mars_attn_fwd(ctypes.byref(desc), q, k, v, o, lse, None)
+
+
+def test_attn_validation_errors():
+    lib = L.load()
+    assert lib.mars_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, None, None) == L.MARS_EINVAL
+    good = lambda: M.attn_desc(2, 14, 2, 64, 10, 20, 4)
+    d = good(); d.n_q_heads = 15
+    assert _attn(d) == L.MARS_EINVAL                      # Hq % Hkv
+    d = good(); d.head_dim = 96
+    assert _attn(d) == L.MARS_EUNSUPPORTED
+    d = good(); d.block = 0
+    assert _attn(d) == L.MARS_EINVAL
+    d = good(); d.resp_len = -1
+    assert _attn(d) == L.MARS_EINVAL
+    d = good(); d.dtype = 7
+    assert _attn(d) == L.MARS_EINVAL
+    d = good(); d.scale = float("nan")
+    assert _attn(d) == L.MARS_EINVAL
+    d = good(); d.scale = -1.0
+    assert _attn(d) == L.MARS_EINVAL
+    d = good(); d.reserved = 1
+    assert _attn(d) == L.MARS_EINVAL
+    assert _attn(good(), q=None) == L.MARS_EINVAL
+    assert _attn(good(), o=MISALIGNED) == L.MARS_EINVAL
+    d = good(); d.k_strides[1] = 2 * 64 + 4                # row start loses 16-byte alignment
+    assert _attn(d) == L.MARS_EINVAL
+    d = good(); d.q_strides[0] = -8
+    assert _attn(d) == L.MARS_EINVAL
+    assert _attn(good(), lse=FAKE + 2) == L.MARS_EINVAL
+    # empty work: OK without touching pointers
+    d = good(); d.batch = 0
+    assert _attn(d, q=None, k=None, v=None, o=None) == L.MARS_OK
+    d = good(); d.prompt_len = 0; d.resp_len = 0
+    assert _attn(d, q=None, k=None, v=None, o=None) == L.MARS_OK
+    # fp32 tile log unsupported; tile map bounds
+    d = good(); d.dtype = L.MARS_DTYPE_FP32
+    assert lib.mars_attn_fwd_tilelog(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == L.MARS_EUNSUPPORTED
+    assert lib.mars_tile_map(ctypes.byref(good()), 0, 16, FAKE, None) == L.MARS_EINVAL
+    assert lib.mars_tile_map(ctypes.byref(good()), 16, 2048, FAKE, None) == L.MARS_EINVAL
+    assert lib.mars_tile_map(ctypes.byref(good()), 16, 16, None, None) == L.MARS_EINVAL
+    assert lib.mars_mask_materialize(ctypes.byref(good()), None, None) == L.MARS_EINVAL
+
+
+def test_decode_validation_errors():
+    lib = L.load()
+    good = lambda: M.decode_desc(4, 28, 4, 128, 4, 4096)
+
+    def call(d, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE, lens=FAKE):
+        return lib.mars_decode_step(ctypes.byref(d), ptr, ptr, ptr, ptr, ptr, lens, ptr, ws, ws_bytes, None)
+
+    d = good(); d.window = 0
+    assert call(d) == L.MARS_EINVAL
+    d = good(); d.window = 10                              # 7 * 10 rows > 64
+    assert call(d) == L.MARS_EUNSUPPORTED
+    d = good(); d.head_dim = 80
+    assert call(d) == L.MARS_EUNSUPPORTED
+    d = good(); d.dtype = L.MARS_DTYPE_FP32
+    assert call(d) == L.MARS_EUNSUPPORTED
+    assert call(good(), lens=None) == L.MARS_EINVAL
+    d = good(); d.kc_strides[2] = 100                      # cache rows lose 16-byte alignment
+    assert call(d) == L.MARS_EINVAL
+    assert call(good(), ptr=MISALIGNED) == L.MARS_EINVAL
+    need = M.mars_decode_workspace_bytes(4, 28, 4, 128, 4, 4096)
+    assert need > 0
+    assert call(good(), ws=None) == L.MARS_EWORKSPACE
+    assert call(good(), ws_bytes=need - 1) == L.MARS_EWORKSPACE
+    d = good(); d.batch = 0
+    assert call(d, ptr=None, lens=None, ws=None) == L.MARS_OK
+
+
+def test_accept_validation_errors():
+    lib = L.load()
+    good = lambda: M.accept_desc(32, 4, 152064, 0.95)
+
+    def call(d, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE):
+        return lib.mars_accept(ctypes.byref(d), ptr, ptr, ptr, ptr, ws, ws_bytes, None)
+
+    for field, val, code in [("tau", 0.0, L.MARS_EINVAL), ("tau", -0.5, L.MARS_EINVAL),
+                             ("tau", float("inf"), L.MARS_EINVAL), ("min_accept", 2, L.MARS_EINVAL),
+                             ("window", 65, L.MARS_EUNSUPPORTED), ("window", 0, L.MARS_EINVAL),
+                             ("vocab", 0, L.MARS_EINVAL),
+                             ("dtype", L.MARS_DTYPE_FP32, L.MARS_EUNSUPPORTED)]:
+        d = good()
+        setattr(d, field, val)
+        assert call(d) == code, field
+    d = good(); d.row_stride = 152063                     # rows lose 16-byte alignment
+    assert call(d) == L.MARS_EINVAL
+    assert call(good(), ptr=MISALIGNED) == L.MARS_EINVAL
+    assert call(good(), ptr=None) == L.MARS_EINVAL
+    need = M.mars_accept_workspace_bytes(32, 4, 152064)
+    assert call(good(), ws_bytes=need - 1) == L.MARS_EWORKSPACE
+    assert call(good(), ws=FAKE + 8) == L.MARS_EWORKSPACE
+    d = good(); d.batch = 0
+    assert call(d, ptr=None, ws=None) == L.MARS_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        L.load()
