@@ -169,6 +169,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
         }
     };
 
+    // Running row statistics in the log2 domain.  m_run is raised lazily: only when a tile's
+    // row max exceeds it by more than kLazy (so p = 2^(s*c - m_run) <= 2^kLazy stays exact
+    // in fp32/bf16) are O and l rescaled; otherwise the stale max is kept.
+    constexpr float kLazy = 8.f;
     float m_run[kNcb], l_run[kNcb];
     f32x16_t acc[kNcb][NDB];
 #pragma unroll
@@ -181,17 +185,21 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
             for (int e = 0; e < 16; ++e) acc[cb][db][e] = 0.f;
         }
     }
+    const float c = p.scale_log2;
 
     const bool wave_has_rows = wrow0 < p.rows_per_pair;
     int8_t* logrow = nullptr;
     if (p.tilelog && wave_has_rows)
         logrow = p.tilelog + ((int64_t)bg * p.row_groups + wrow0 / kRowsPerWave) * p.key_tiles;
 
-    // Transposed-read addressing for V^T (see header comment): lane (s16, grp) reads 4
-    // bf16 at V[16kh + 4*(grp>>1) + s16/4 (+8)][32db + 16*(grp&1) + 4*(s16&3)].
+    // Transposed-read addressing for V^T: lane (s16, grp) reads 4 bf16 at
+    // V[16kh + 4*(grp>>1) + s16/4 (+8)][32db + 16*(grp&1) + 4*(s16&3)].
     const int s16 = lane & 15, grp = lane >> 4;
     const int vkey = 4 * (grp >> 1) + (s16 >> 2);
     const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);
+
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
     gload(tile_of(0));
     swrite(0);
@@ -212,11 +220,13 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
                 lall &= range_all(pos[cb], kb, ke, rb[cb]);
             }
         }
-        const bool wany = __ballot(lany) != 0ull;
-        const bool wall = (kb + kKT <= p.N) && (__ballot(!lall) == 0ull);
+        // Wave-uniform tile class, made scalar so the branches below are real branches.
+        const int wany = __builtin_amdgcn_readfirstlane(__ballot(lany) != 0ull ? 1 : 0);
+        const int wall = __builtin_amdgcn_readfirstlane((kb + kKT <= p.N) && (__ballot(!lall) == 0ull) ? 1 : 0);
         if (logrow && lane == 0 && wany) logrow[kt] = wall ? 2 : 1;
 
         if (wany) {
+            // S^T = K Q^T for this wave's two 32-row column blocks.
             f32x16_t s[kNcb];
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb) {
@@ -225,57 +235,85 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
             }
             const uint16_t* kl = &sK[buf][hl * KSTR + 8 * g2];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kl + 16 * c);
+            for (int cc = 0; cc < NC; ++cc) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kl + 16 * cc);
 #pragma unroll
                 for (int cb = 0; cb < kNcb; ++cb)
-                    s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][c], s[cb], 0, 0, 0);
+                    s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], s[cb], 0, 0, 0);
             }
+            // Element mask on tiles that are not entirely visible.  Element e of this lane
+            // holds key kb + 4*g2 + o(e), o(e) = 8*(e/4) + e%4.
             if (!wall) {
 #pragma unroll
                 for (int cb = 0; cb < kNcb; ++cb) {
+                    const int base = kb + 4 * g2;
+                    const int A = rb[cb].hi1 - base, Lo = rb[cb].lo2 - base, Hi = pos[cb] - base;
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const int j = kb + 8 * (e >> 2) + 4 * g2 + (e & 3);
-                        if (!key_visible(pos[cb], j, rb[cb])) s[cb][e] = -INFINITY;
+                        const int o = 8 * (e >> 2) + (e & 3);
+                        const bool vis = (o < A) | ((o >= Lo) & (o <= Hi));
+                        s[cb][e] = vis ? s[cb][e] : -INFINITY;
                     }
                 }
             }
+            // Row max (this lane's 16 keys, then the partner half), lazy rescale.
+            float mx[kNcb];
+            bool need = false;
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) {
+                float a = fmaxf(fmaxf(s[cb][0], s[cb][1]), s[cb][2]);
+                float b2 = fmaxf(fmaxf(s[cb][3], s[cb][4]), s[cb][5]);
+                float c2 = fmaxf(fmaxf(s[cb][6], s[cb][7]), s[cb][8]);
+                float d2 = fmaxf(fmaxf(s[cb][9], s[cb][10]), s[cb][11]);
+                float e2 = fmaxf(fmaxf(s[cb][12], s[cb][13]), s[cb][14]);
+                float m = fmaxf(fmaxf(a, b2), fmaxf(fmaxf(c2, d2), fmaxf(e2, s[cb][15])));
+                mx[cb] = half_swap_max(m) * c;
+                need |= mx[cb] > m_run[cb] + kLazy;
+            }
+            if (__builtin_amdgcn_readfirstlane(__ballot(need) != 0ull ? 1 : 0)) {
+#pragma unroll
+                for (int cb = 0; cb < kNcb; ++cb) {
+                    const float mnew = fmaxf(m_run[cb], mx[cb]);
+                    if (mnew > m_run[cb]) {
+                        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
+                        l_run[cb] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                        }
+                        m_run[cb] = mnew;
+                    }
+                }
+            }
+            // P = 2^(s*c - m) in bf16; l += sum of the rounded P (dot2 with ones).
             bf16x8_t pb[kNcb][2];
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb) {
-                float mx = s[cb][0];
-#pragma unroll
-                for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[cb][e]);
-                mx = half_swap_max(mx);
-                const float mnew = fmaxf(m_run[cb], mx * p.scale_log2);
-                const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-                const float alpha = exp2f(m_run[cb] - msafe);
-                m_run[cb] = mnew;
+                const float msafe = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
                 float pv[16];
-                float rs = 0.f;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    pv[e] = exp2f(fmaf(s[cb][e], p.scale_log2, -msafe));
-                    rs += pv[e];
-                }
-                l_run[cb] = fmaf(l_run[cb], alpha, rs);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
-                }
+                for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[cb][e], c, -msafe));
+                float lsum = l_run[cb];
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
-                    uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
-                    uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
-                    uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
-                    uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
+                    // Scalar temporaries: element reads of a partially built vector in this
+                    // unrolled loop were miscompiled (every dot2 read element 0).
+                    const uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
+                    const uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
+                    const uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
+                    const uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w0), ones2, lsum, false);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w1), ones2, lsum, false);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w2), ones2, lsum, false);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w3), ones2, lsum, false);
                     typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
-                    u32x4_t w = {w0, w1, w2, w3};
+                    const u32x4_t w = {w0, w1, w2, w3};
                     pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
                 }
+                l_run[cb] = lsum;
             }
+            // O^T += V^T P^T.
             const uint16_t* vt = &sV[buf][0];
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
