@@ -212,8 +212,8 @@ int mars_accept_workspace_bytes(const mars_accept_desc* desc, size_t* bytes);
 /*
  * logits: bf16 [batch][window][vocab] (strided as in desc).  Outputs on the device:
  * tokens int32 [batch][window], pmax fp32 [batch][window], n_accept int32 [batch].
- * ws: at least mars_accept_workspace_bytes, zero-filled by the caller before its first
- * use with mars_accept; every completed call leaves it zero-filled again.
+ * ws: device workspace of at least mars_accept_workspace_bytes; no initialisation needed.
+ * Logits must be finite.
  */
 int mars_accept(const mars_accept_desc* desc, const void* logits, int32_t* tokens, float* pmax,
                 int32_t* n_accept, void* ws, size_t ws_bytes, hipStream_t stream);

@@ -226,7 +226,7 @@ def mars_accept_workspace_bytes(batch, W, V, tau=0.95):
 def mars_accept(logits, tau, ws=None, tokens=None, pmax=None, n_accept=None):
     """logits bf16 [b, W, V] -> (tokens int32 [b,W], pmax fp32 [b,W], n_accept int32 [b]).
 
-    ``ws`` must be zero-filled before its first use (a fresh one is made with torch.zeros).
+    ``ws``: optional device workspace (uint8, at least mars_accept_workspace_bytes).
     """
     b, W, V = logits.shape
     if logits.stride(-1) != 1:
@@ -237,7 +237,7 @@ def mars_accept(logits, tau, ws=None, tokens=None, pmax=None, n_accept=None):
     pmax = torch.empty((b, W), dtype=torch.float32, device=dev) if pmax is None else pmax
     n_accept = torch.empty((b,), dtype=torch.int32, device=dev) if n_accept is None else n_accept
     if ws is None:
-        ws = torch.zeros(max(mars_accept_workspace_bytes(b, W, V, tau), 16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(mars_accept_workspace_bytes(b, W, V, tau), 16), dtype=torch.uint8, device=dev)
     _check(L.load().mars_accept(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(pmax), _ptr(n_accept),
                                 _ptr(ws), ws.numel(), _stream(logits)), "mars_accept")
     return tokens, pmax, n_accept

@@ -15,6 +15,7 @@
 // Chunks past a sequence's length exit at once, so the grid is fixed while the work is
 // ragged; the cache is read exactly once.
 #include <cmath>
+#include <type_traits>
 
 #include "mars_device.h"
 #include "mars_internal.h"
@@ -23,9 +24,9 @@ namespace mars {
 
 namespace {
 
-constexpr int kCH = 256;      // cache keys per split workgroup
+constexpr int kCH = 512;      // cache keys per split workgroup
 constexpr int kStep = 32;     // keys per MFMA step
-constexpr int kMaxRows = 64;  // G * W
+constexpr int kStages = 3;    // LDS ring depth of the split kernel
 
 struct DecodeKParams {
     const uint16_t* qw;
@@ -45,13 +46,38 @@ struct DecodeKParams {
 
 __device__ inline int clamp_len(int len, int cap) { return len < 0 ? 0 : (len > cap ? cap : len); }
 
+// LDS ring of the split kernel: one __shared__ object per stage and tensor (sized for
+// D = 128), named directly at every access so no generic pointer to LDS is ever formed and
+// the compiler's LDS-DMA wait tracking keeps the in-flight stages apart.
+__shared__ __attribute__((aligned(16))) uint16_t g_dk0[kStep * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_dk1[kStep * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_dk2[kStep * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_dv0[kStep * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_dv1[kStep * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_dv2[kStep * 128];
+
+template <int ST>
+__device__ inline uint16_t* dec_k() {
+    if constexpr (ST == 0) return g_dk0;
+    else if constexpr (ST == 1) return g_dk1;
+    else return g_dk2;
+}
+template <int ST>
+__device__ inline uint16_t* dec_v() {
+    if constexpr (ST == 0) return g_dv0;
+    else if constexpr (ST == 1) return g_dv1;
+    else return g_dv2;
+}
+
 template <int D, int NCB>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
-    constexpr int VSTR = D + 32;
-    constexpr int NC = D / 16;
-    constexpr int NDB = D / 32;
-    constexpr int VL = (kStep * D / 8) / 64;   // 16-byte V loads per lane per step
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kStep * VSTR];
+    constexpr int NC = D / 16;                 // 16-wide d chunks of the QK^T contraction
+    constexpr int NDB = D / 32;                // 32-row d blocks of O^T
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int NINS = kStep * CPR / 64;     // 1 KB DMA instructions per tile (per tensor)
+    constexpr int GROUP = 2 * NINS;            // DMA instructions per step (K and V)
+    constexpr float kLazy = 8.f;
+    static_assert(D <= 128, "ring sized for head_dim <= 128");
 
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int len = clamp_len(p.cache_len[b], p.cap);
@@ -63,7 +89,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
     const int lane = threadIdx.x;
     const int hl = lane & 31, g2 = lane >> 5;
 
-    // Query rows u = i*G + hh (window row i, query head g*G + hh).
+    const uint16_t* kbase = p.kc + b * p.kcs0 + (int64_t)g * p.kcs1;
+    const uint16_t* vbase = p.vc + b * p.vcs0 + (int64_t)g * p.vcs1;
+
+    // DMA of step `step` into stage arrays (sk, sv): slot (row r, position pos) holds logical
+    // chunk pos ^ swz(r) of key k0 + r (keys past the chunk end repeat its last key; they are
+    // masked to -inf, and repeating a real row keeps V finite).
+    auto issue = [&](int step, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        const int k0 = k_begin + step * kStep;
+#pragma unroll
+        for (int j = 0; j < NINS; ++j) {
+            const int slot = 64 * j + lane;
+            const int r = slot / CPR, pos = slot % CPR;
+            const int key = min(k0 + r, k_end - 1);
+            dma16(kbase + (int64_t)key * p.kcs2 + 8 * (pos ^ swz_k<D>(r)), lds_addr(dec_k<ST>()) + 1024 * j);
+            dma16(vbase + (int64_t)key * p.vcs2 + 8 * (pos ^ swz_v<D>(r)), lds_addr(dec_v<ST>()) + 1024 * j);
+        }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+
+    // Query rows u = i*G + hh (window row i, query head g*G + hh): the B operand, in registers.
     bf16x8_t qf[NCB][NC];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -76,32 +124,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
         for (int cc = 0; cc < NC; ++cc)
             qf[cb][cc] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * cc) : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
+    // Drain the Q loads before any copy is issued: the compiler does not count the copies,
+    // so a Q wait inside the loop would otherwise become a full vmcnt(0).
+    wait_vmcnt<0>();
 
-    const uint16_t* kbase = p.kc + b * p.kcs0 + (int64_t)g * p.kcs1;
-    const uint16_t* vbase = p.vc + b * p.vcs0 + (int64_t)g * p.vcs1;
-
-    bf16x8_t kreg[NC], vreg[VL];
-    auto gload = [&](int step) {
-        const int k0 = k_begin + step * kStep;
-        const int key = k0 + hl;
-        if (key < k_end) {
-            const uint16_t* kp = kbase + (int64_t)key * p.kcs2 + 8 * g2;
-#pragma unroll
-            for (int cc = 0; cc < NC; ++cc) kreg[cc] = *reinterpret_cast<const bf16x8_t*>(kp + 16 * cc);
-        } else {
-#pragma unroll
-            for (int cc = 0; cc < NC; ++cc) kreg[cc] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < VL; ++i) {
-            const int idx = lane + 64 * i;
-            const int kl = idx / (D / 8), ch = idx % (D / 8);
-            if (k0 + kl < k_end)
-                vreg[i] = *reinterpret_cast<const bf16x8_t*>(vbase + (int64_t)(k0 + kl) * p.vcs2 + 8 * ch);
-            else
-                vreg[i] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    };
+    issue(0, S0{});
+    if (nsteps > 1) issue(1, S1{});
 
     float m_run[NCB], l_run[NCB];
     f32x16_t acc[NCB][NDB];
@@ -115,97 +143,140 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
             for (int e = 0; e < 16; ++e) acc[cb][db][e] = 0.f;
         }
     }
+    const float csc = p.scale_log2;
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+    // Per-lane LDS byte offsets of the MFMA operands (independent of the stage).
+    int koff[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) koff[cc] = hl * (2 * D) + 16 * ((2 * cc + g2) ^ swz_k<D>(hl));
     const int s16 = lane & 15, grp = lane >> 4;
-    const int vkey = 4 * (grp >> 1) + (s16 >> 2);
-    const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);
+    int voff[NDB][2][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int row = 16 * kh + 8 * hf + 4 * (grp >> 1) + (s16 >> 2);
+                const int col = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
+                voff[db][kh][hf] = row * (2 * D) + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
+            }
+        }
+    }
 
-    gload(0);
-    for (int step = 0; step < nsteps; ++step) {
-        const int buf = step & 1;
-        // Stage this step's V tile in LDS, then take K out of the load registers so the
-        // next step's loads can be issued before the math.
-#pragma unroll
-        for (int i = 0; i < VL; ++i) {
-            const int idx = lane + 64 * i;
-            const int kl = idx / (D / 8), ch = idx % (D / 8);
-            *reinterpret_cast<bf16x8_t*>(&sV[buf][kl * VSTR + 8 * ch]) = vreg[i];
-        }
-        bf16x8_t kf[NC];
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) kf[cc] = kreg[cc];
-        __syncthreads();
-        if (step + 1 < nsteps) gload(step + 1);
-
-        const int k0 = k_begin + step * kStep;
-        f32x16_t s[NCB];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[cb][e] = 0.f;
-        }
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[cb][cc], s[cb], 0, 0, 0);
-        }
-        if (k0 + kStep > k_end) {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = k0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-                    if (j >= k_end) s[cb][e] = -INFINITY;
+    // One step on stage (ks, vs); step + 2 is issued into (nk, nv), the stage step - 1 used.
+    auto body = [&](const int step, auto stage) __attribute__((always_inline)) {
+                constexpr int ST = decltype(stage)::value;
+                // Keep two steps in flight, then wait until this step's DMA group has landed.
+                const int ahead = nsteps - 1 - step;   // groups issued after this one
+                if (ahead >= 2) {
+                    issue(step + 2, std::integral_constant<int, (ST + 2) % kStages>{});
+                    wait_vmcnt<2 * GROUP>();
+                } else if (ahead == 1) {
+                    wait_vmcnt<GROUP>();
+                } else {
+                    wait_vmcnt<0>();
                 }
-            }
-        }
-        bf16x8_t pb[NCB][2];
+                __syncthreads();
+                const char* kt = reinterpret_cast<const char*>(dec_k<ST>());
+                const char* vt = reinterpret_cast<const char*>(dec_v<ST>());
+                const int k0 = k_begin + step * kStep;
+
+                f32x16_t s[NCB];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            float mx = s[cb][0];
+                for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[cb][e]);
-            mx = half_swap_max(mx);
-            const float mnew = fmaxf(m_run[cb], mx * p.scale_log2);
-            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = exp2f(m_run[cb] - msafe);
-            m_run[cb] = mnew;
-            float pv[16];
-            float rs = 0.f;
+                    for (int e = 0; e < 16; ++e) s[cb][e] = 0.f;
+                }
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                pv[e] = exp2f(fmaf(s[cb][e], p.scale_log2, -msafe));
-                rs += pv[e];
-            }
-            l_run[cb] = fmaf(l_run[cb], alpha, rs);
+                for (int cc = 0; cc < NC; ++cc) {
+                    const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + koff[cc]);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+                    for (int cb = 0; cb < NCB; ++cb)
+                        s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], s[cb], 0, 0, 0);
+                }
+                if (__builtin_amdgcn_readfirstlane(k0 + kStep > k_end ? 1 : 0)) {
+                    const int lim = k_end - k0 - 4 * g2;   // element o is a key iff o < lim
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
-            }
+                    for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
-                u32x4_t w = {pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]), pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
-                             pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]), pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
-                pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
-            }
-        }
-        const uint16_t* vt = &sV[buf][0];
+                        for (int e = 0; e < 16; ++e) {
+                            const int o = 8 * (e >> 2) + (e & 3);
+                            s[cb][e] = (o < lim) ? s[cb][e] : -INFINITY;
+                        }
+                    }
+                }
+                float mx[NCB];
+                bool need = false;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float m = fmaxf(fmaxf(fmaxf(s[cb][0], s[cb][1]), fmaxf(s[cb][2], s[cb][3])),
+                                    fmaxf(fmaxf(s[cb][4], s[cb][5]), fmaxf(s[cb][6], s[cb][7])));
+                    m = fmaxf(m, fmaxf(fmaxf(fmaxf(s[cb][8], s[cb][9]), fmaxf(s[cb][10], s[cb][11])),
+                                       fmaxf(fmaxf(s[cb][12], s[cb][13]), fmaxf(s[cb][14], s[cb][15]))));
+                    mx[cb] = half_swap_max(m) * csc;
+                    need |= mx[cb] > m_run[cb] + kLazy;
+                }
+                if (__builtin_amdgcn_readfirstlane(__ballot(need) != 0ull ? 1 : 0)) {
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const uint16_t* a0 = vt + (16 * kh + vkey) * VSTR + 32 * db + vcol;
-                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(a0));
-                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(a0 + 8 * VSTR));
-                const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const float mnew = fmaxf(m_run[cb], mx[cb]);
+                        if (mnew > m_run[cb]) {
+                            const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);
+                            l_run[cb] *= alpha;
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cb][kh], acc[cb][db], 0, 0, 0);
-            }
-        }
+                            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                                for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                            }
+                            m_run[cb] = mnew;
+                        }
+                    }
+                }
+                bf16x8_t pb[NCB][2];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const float msafe = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+                    float pv[16];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[cb][e], csc, -msafe));
+                    float lsum = l_run[cb];
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh) {
+                        const uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
+                        const uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
+                        const uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
+                        const uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
+                        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w0), ones2, lsum, false);
+                        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w1), ones2, lsum, false);
+                        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w2), ones2, lsum, false);
+                        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w3), ones2, lsum, false);
+                        typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+                        const u32x4_t w = {w0, w1, w2, w3};
+                        pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
+                    }
+                    l_run[cb] = lsum;
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh) {
+                        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vt + voff[db][kh][0]));
+                        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vt + voff[db][kh][1]));
+                        const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
+                            acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cb][kh], acc[cb][db], 0, 0, 0);
+                    }
+                }
+                __syncthreads();   // this stage is refilled two steps later
+    };
+    for (int t0 = 0; t0 < nsteps; t0 += kStages) {
+        body(t0, S0{});
+        if (t0 + 1 < nsteps) body(t0 + 1, S1{});
+        if (t0 + 2 < nsteps) body(t0 + 2, S2{});
     }
 
     // Unnormalised partial of this chunk.
@@ -233,63 +304,86 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
     }
 }
 
-// One workgroup (64 threads) per (sequence, query head); thread t owns d = t, t + 64.
+// One 256-thread workgroup per (sequence, kv head, group of 8 query rows u = i*G + hh);
+// 32 threads per row, each owning D/32 consecutive output columns.  The chunk partials are
+// merged online (max, rescale, accumulate) with independent loads per chunk, then the
+// window keys 0..i are added (dot products reduced over the row's 32 threads).
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeKParams p) {
-    constexpr int DPT = D / 64;
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int g = h / p.G, hh = h % p.G;
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeKParams p) {
+    constexpr int DPT = D / 32;   // columns per thread (4 or 2)
+    const int rg = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int t = threadIdx.x;
+    const int u = rg * 8 + (t >> 5);
+    const int l32 = t & 31;
+    if (u >= p.R) return;   // whole 32-lane groups exit together; no barriers below
+    const int i = u / p.G, h = g * p.G + u % p.G;
     const int len = clamp_len(p.cache_len[b], p.cap);
     const int nch = (len + kCH - 1) / kCH;
+    const int d0 = l32 * DPT;
 
-    for (int i = 0; i < p.W; ++i) {
-        const int u = i * p.G + hh;
-        const uint16_t* qp = p.qw + b * p.qws0 + (int64_t)i * p.qws1 + (int64_t)h * p.qws2;
-        float qv[DPT];
+    float M = -INFINITY, den = 0.f;
+    float num[DPT];
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) qv[e] = bf16_bits_to_f32(qp[t + 64 * e]);
+    for (int e = 0; e < DPT; ++e) num[e] = 0.f;
 
-        // Window scores (log2 domain), rows 0..i of this sequence's window.
-        float sw[kMaxRows];
-        float M = -INFINITY;
-        for (int j = 0; j <= i; ++j) {
-            const uint16_t* kp = p.kw + b * p.kws0 + (int64_t)j * p.kws1 + (int64_t)g * p.kws2;
-            float part = 0.f;
-#pragma unroll
-            for (int e = 0; e < DPT; ++e) part = fmaf(qv[e], bf16_bits_to_f32(kp[t + 64 * e]), part);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-            sw[j] = part * p.scale_log2;
-            M = fmaxf(M, sw[j]);
-        }
-        const int64_t slot0 = ((int64_t)(b * p.hkv + g) * p.nchunk) * p.R + u;
-        for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, p.ws_ml[(slot0 + (int64_t)cc * p.R) * 2]);
-
-        float num[DPT] = {};
-        float den = 0.f;
-        for (int cc = 0; cc < nch; ++cc) {
-            const int64_t sl = slot0 + (int64_t)cc * p.R;
-            const float w = exp2f(p.ws_ml[sl * 2] - M);
-            den = fmaf(p.ws_ml[sl * 2 + 1], w, den);
-            const float* ap = p.ws_acc + sl * D;
-#pragma unroll
-            for (int e = 0; e < DPT; ++e) num[e] = fmaf(ap[t + 64 * e], w, num[e]);
-        }
-        for (int j = 0; j <= i; ++j) {
-            const float w = exp2f(sw[j] - M);
-            den += w;
-            const uint16_t* vp = p.vw + b * p.vws0 + (int64_t)j * p.vws1 + (int64_t)g * p.vws2;
-#pragma unroll
-            for (int e = 0; e < DPT; ++e) num[e] = fmaf(bf16_bits_to_f32(vp[t + 64 * e]), w, num[e]);
-        }
-        const float inv = 1.f / den;
-        uint16_t* op = p.o + b * p.os0 + (int64_t)i * p.os1 + (int64_t)h * p.os2;
+    const int64_t slot0 = ((int64_t)(b * p.hkv + g) * p.nchunk) * p.R + u;
+    int cc = 0;
+    for (; cc + 1 < nch; cc += 2) {   // two chunks per step: loads issued together
+        const int64_t sa = slot0 + (int64_t)cc * p.R, sb = sa + p.R;
+        const float2 mla = *reinterpret_cast<const float2*>(p.ws_ml + sa * 2);
+        const float2 mlb = *reinterpret_cast<const float2*>(p.ws_ml + sb * 2);
+        float aa[DPT], ab[DPT];
 #pragma unroll
         for (int e = 0; e < DPT; ++e) {
-            const uint32_t pk = pack_bf16x2(num[e] * inv, 0.f);
-            op[t + 64 * e] = (uint16_t)(pk & 0xffffu);
+            aa[e] = p.ws_acc[sa * D + d0 + e];
+            ab[e] = p.ws_acc[sb * D + d0 + e];
         }
+        const float Mn = fmaxf(M, fmaxf(mla.x, mlb.x));
+        const float r0 = __builtin_amdgcn_exp2f(M - Mn), ra = __builtin_amdgcn_exp2f(mla.x - Mn),
+                    rb = __builtin_amdgcn_exp2f(mlb.x - Mn);
+        den = den * r0 + mla.y * ra + mlb.y * rb;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) num[e] = num[e] * r0 + aa[e] * ra + ab[e] * rb;
+        M = Mn;
+    }
+    if (cc < nch) {
+        const int64_t sa = slot0 + (int64_t)cc * p.R;
+        const float2 mla = *reinterpret_cast<const float2*>(p.ws_ml + sa * 2);
+        const float Mn = fmaxf(M, mla.x);
+        const float r0 = __builtin_amdgcn_exp2f(M - Mn), ra = __builtin_amdgcn_exp2f(mla.x - Mn);
+        den = den * r0 + mla.y * ra;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) num[e] = num[e] * r0 + p.ws_acc[sa * D + d0 + e] * ra;
+        M = Mn;
+    }
+
+    // Window keys 0..i of this sequence (causal, self-inclusive).
+    const uint16_t* qp = p.qw + b * p.qws0 + (int64_t)i * p.qws1 + (int64_t)h * p.qws2 + d0;
+    float qv[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) qv[e] = bf16_bits_to_f32(qp[e]);
+    for (int j = 0; j <= i; ++j) {
+        const uint16_t* kp = p.kw + b * p.kws0 + (int64_t)j * p.kws1 + (int64_t)g * p.kws2 + d0;
+        const uint16_t* vp = p.vw + b * p.vws0 + (int64_t)j * p.vws1 + (int64_t)g * p.vws2 + d0;
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) part = fmaf(qv[e], bf16_bits_to_f32(kp[e]), part);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 32);
+        const float sj = part * p.scale_log2;
+        const float Mn = fmaxf(M, sj);
+        const float r0 = __builtin_amdgcn_exp2f(M - Mn), rj = __builtin_amdgcn_exp2f(sj - Mn);
+        den = den * r0 + rj;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) num[e] = num[e] * r0 + bf16_bits_to_f32(vp[e]) * rj;
+        M = Mn;
+    }
+    const float inv = 1.f / den;
+    uint16_t* op = p.o + b * p.os0 + (int64_t)i * p.os1 + (int64_t)h * p.os2 + d0;
+#pragma unroll
+    for (int e = 0; e < DPT; e += 2) {
+        const uint32_t pk = pack_bf16x2(num[e] * inv, num[e + 1] * inv);
+        *reinterpret_cast<uint32_t*>(op + e) = pk;
     }
 }
 
@@ -341,9 +435,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 cgrid(a.hq, a.batch);
-    if (a.d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(64), 0, s, p);
+    dim3 cgrid((p.R + 7) / 8, a.hkv, a.batch);
+    if (a.d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

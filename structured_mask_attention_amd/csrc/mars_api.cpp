@@ -259,6 +259,7 @@ static int check_accept_desc(const mars_accept_desc* d) {
     if (!d) return MARS_EINVAL;
     if (d->batch < 0 || d->window < 1 || d->vocab < 1) return MARS_EINVAL;
     if (d->window > 64) return MARS_EUNSUPPORTED;
+    if (d->vocab > 65535 * 8192) return MARS_EUNSUPPORTED;
     if (d->dtype != MARS_DTYPE_BF16) return d->dtype == MARS_DTYPE_FP32 ? MARS_EUNSUPPORTED : MARS_EINVAL;
     if (!(d->tau > 0.f) || !isfinite(d->tau)) return MARS_EINVAL;
     if (d->min_accept != 1) return MARS_EINVAL;

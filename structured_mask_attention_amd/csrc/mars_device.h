@@ -76,4 +76,48 @@ __device__ inline float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---------------------------------------------------------------------------------------
+// K/V tiles in LDS: rows of D bf16 (2D bytes, no padding), 16-byte chunks XOR-swizzled by
+// row so that the MFMA operand reads are free of bank conflicts:
+//   * K (ds_read_b128, lane = row, same logical chunk): chunk c of row r at c ^ swz_k(r);
+//   * V (ds_read_b64_tr_b16, 4 rows x 2 chunks per 16 lanes): chunk c of row r at c ^ swz_v(r).
+// Tiles are filled with global_load_lds_dwordx4: lane L of a 64-lane instruction writes LDS
+// bytes [16L, 16L+16) of that instruction's 1 KB window, i.e. slot s = (row, position).
+// ---------------------------------------------------------------------------------------
+template <int D>
+__device__ inline int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ inline int swz_v(int r) {
+    return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+// LDS byte address of a __shared__ object (the low half of its generic address).
+__device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane L writes LDS bytes
+// [w + 16L, w + 16L + 16) where w = `lds_window` is the same for the whole wave.  Issued
+// as inline asm so the copies are invisible to the compiler's wait insertion: the caller
+// orders them with wait_vmcnt<>() and a barrier before reading the window.
+// M0 is saved and restored around the copy, since the compiler reserves it.
+__device__ inline void dma16(const void* gsrc, uint32_t lds_window) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_window), "v"(gsrc)
+        : "memory");
+}
+
+// s_waitcnt vmcnt(N) for the gfx9 encoding (expcnt/lgkmcnt left unconstrained).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace mars

@@ -89,19 +89,17 @@ def test_accept_ties_take_lowest_index():
 
 
 def test_accept_workspace_reuse_and_strided_rows():
-    """Two calls in a row on one workspace (counters reset), logits as a strided view."""
+    """Two calls in a row on one uninitialised workspace, logits as a strided view."""
     s = I.DECODE7B
     big = I.logits_inputs(s.batch, s.W + 1, s.vocab + 64, seed=99)
     view = big[:, 1:, 32:32 + s.vocab]
-    ws = torch.zeros(M.mars_accept_workspace_bytes(s.batch, s.W, s.vocab), dtype=torch.uint8, device=dev())
+    ws = torch.full((M.mars_accept_workspace_bytes(s.batch, s.W, s.vocab),), 0x7f, dtype=torch.uint8, device=dev())
     lg = big.to(dev())[:, 1:, 32:32 + s.vocab]
     r1 = M.mars_accept(lg, 0.95, ws=ws)
     r2 = M.mars_accept(lg, 0.95, ws=ws)
     torch.cuda.synchronize()
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
-    ncnt = s.batch
-    assert int(ws[:4 * ncnt].view(torch.int32).count_nonzero()) == 0
     rtok, rpmax, _ = O.accept(to_np64(view), 0.95)
     assert np.array_equal(r1[0].cpu().numpy(), rtok)
     assert np.abs(r1[1].cpu().numpy() - rpmax).max() <= PMAX_ABS
