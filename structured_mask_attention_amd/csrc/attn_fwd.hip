@@ -5,14 +5,17 @@
 // bf16 path (gfx950 MFMA):
 //   * Rows: the G = Hq/Hkv query heads of one KV head are packed as rows (row u of a
 //     (batch, kv head) pair = position u / G, head kvh*G + u % G), so every K/V tile a
-//     workgroup stages in LDS serves G heads.  A workgroup owns 256 such rows (4 waves x
-//     64 rows); a wave owns two 32-row column blocks.
+//     workgroup stages in LDS serves G heads.  A workgroup owns 128 such rows (4 waves x
+//     32 rows): small enough that the heaviest row tiles (the longest key ranges) finish
+//     early when dispatched first, and light enough on registers for 2 waves per SIMD.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the K
 //     tile is the A operand (read from LDS), the wave's Q rows the B operand (registers for
 //     the whole kernel).  In the output layout a lane owns one query row and 16 of the 32
 //     keys, its partner lane (l ^ 32) the other 16, so row max/sum need one permlane32 swap.
 //   * O^T += V^T P^T: P^T comes straight from the score registers (bf16, RNE); V^T is read
 //     from the natural [key][d] LDS tile with ds_read_b64_tr_b16 (transposing 16-bit read).
+//   * K/V tiles reach LDS by global_load_lds_dwordx4 into a 3-stage ring (two tiles in
+//     flight); 16-byte chunks are XOR-swizzled per row so operand reads are conflict-free.
 //   * Keys are walked in 32-key tiles over at most two intervals per workgroup (the union
 //     of its rows' visible keys, see mars_device.h); each wave classifies every tile for its
 //     own rows: skipped, computed with the element mask, or computed without it.
@@ -25,6 +28,7 @@
 // fp32 path: one thread per query row on the vector ALUs, fp32 throughout (for fp32
 // inputs; a correctness path, not a tuned one).
 #include <cmath>
+#include <type_traits>
 
 #include "mars_device.h"
 #include "mars_internal.h"
@@ -34,9 +38,9 @@ namespace mars {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kNcb = 2;                              // 32-row column blocks per wave
+constexpr int kNcb = 1;                              // 32-row column blocks per wave
 constexpr int kRowsPerWave = 32 * kNcb;              // == kAttnRowBlock
-constexpr int kRowsPerWG = kWaves * kRowsPerWave;    // 256
+constexpr int kRowsPerWG = kWaves * kRowsPerWave;    // 128
 constexpr int kKT = kAttnKeyBlock;                   // 32 keys per LDS tile
 static_assert(kRowsPerWave == kAttnRowBlock, "row block");
 
@@ -68,21 +72,64 @@ __device__ inline int rank_to_tile(int rank, int T, int tN0) {
     return (nN > m) ? (T - 1 - m - rr) : (tN0 - 1 - m - rr);
 }
 
+// K/V ring: 3 stages, one file-scope __shared__ object per stage, tensor and head_dim, so
+// every access names its array directly (no generic pointers to LDS).
+constexpr int kStages = 3;
+__shared__ __attribute__((aligned(16))) uint16_t g_ak0_128[kKT * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_ak1_128[kKT * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_ak2_128[kKT * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_av0_128[kKT * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_av1_128[kKT * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_av2_128[kKT * 128];
+__shared__ __attribute__((aligned(16))) uint16_t g_ak0_64[kKT * 64];
+__shared__ __attribute__((aligned(16))) uint16_t g_ak1_64[kKT * 64];
+__shared__ __attribute__((aligned(16))) uint16_t g_ak2_64[kKT * 64];
+__shared__ __attribute__((aligned(16))) uint16_t g_av0_64[kKT * 64];
+__shared__ __attribute__((aligned(16))) uint16_t g_av1_64[kKT * 64];
+__shared__ __attribute__((aligned(16))) uint16_t g_av2_64[kKT * 64];
+
+template <int D, int ST>
+__device__ inline uint16_t* att_k() {
+    if constexpr (D == 128) {
+        if constexpr (ST == 0) return g_ak0_128;
+        else if constexpr (ST == 1) return g_ak1_128;
+        else return g_ak2_128;
+    } else {
+        if constexpr (ST == 0) return g_ak0_64;
+        else if constexpr (ST == 1) return g_ak1_64;
+        else return g_ak2_64;
+    }
+}
+template <int D, int ST>
+__device__ inline uint16_t* att_v() {
+    if constexpr (D == 128) {
+        if constexpr (ST == 0) return g_av0_128;
+        else if constexpr (ST == 1) return g_av1_128;
+        else return g_av2_128;
+    } else {
+        if constexpr (ST == 0) return g_av0_64;
+        else if constexpr (ST == 1) return g_av1_64;
+        else return g_av2_64;
+    }
+}
+
 template <int D>
-__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(AttnKParams p) {
-    constexpr int KSTR = D + 8;         // K tile row stride (elements)
-    constexpr int VSTR = D + 32;        // V tile row stride (elements)
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
     constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
     constexpr int NDB = D / 32;         // 32-row d blocks of O^T
     constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
-    constexpr int LOADS = (kKT * CPR) / 256;
-    static_assert(LOADS >= 1 && (kKT * CPR) % 256 == 0, "tile load split");
-
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * VSTR];
+    constexpr int NINS = kKT * CPR / 64;            // 1 KB copy windows per tile and tensor
+    constexpr int PERW = NINS / kWaves;             // windows per wave and tensor
+    constexpr int GROUPW = 2 * PERW;                // copy instructions per wave and tile
+    static_assert(D <= 128 && NINS % kWaves == 0 && PERW >= 1, "tile copy split");
+    constexpr float kLazy = 8.f;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane & 31, g2 = lane >> 5;
 
     const int bg = blockIdx.x % p.bg_count;
@@ -120,6 +167,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
             }
         }
     }
+    // The copies below are invisible to the compiler's wait tracking: finish Q first.
+    wait_vmcnt<0>();
 
     // Union of the workgroup's visible keys: [0, endA) and [startC, endC).
     const int u_last = min(row0 + kRowsPerWG, p.rows_per_pair) - 1;
@@ -138,41 +187,27 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
     if (c0t < nA) c0t = nA;
     const int nCt = c1t > c0t ? c1t - c0t : 0;
     const int ntiles = nA + nCt;
+    auto tile_of = [&](int it) { return it < nA ? it : c0t + (it - nA); };
 
     const uint16_t* kbase = p.k + b * p.ks0 + (int64_t)g * p.ks2;
     const uint16_t* vbase = p.v + b * p.vs0 + (int64_t)g * p.vs2;
-    bf16x8_t kreg[LOADS], vreg[LOADS];
 
-    auto tile_of = [&](int it) { return it < nA ? it : c0t + (it - nA); };
-    auto gload = [&](int kt) {
+    // Copy of key tile kt into stage ST: this wave fills PERW 1 KB windows of K and of V.
+    // Window slot (row r, position pos) holds logical chunk pos ^ swz(r) of key kt*32 + r;
+    // rows past N repeat key N-1 (finite values; such keys are always masked).
+    auto issue = [&](int kt, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int idx = tid + 256 * i;
-            const int key = kt * kKT + idx / CPR;
-            const int ch = idx % CPR;
-            if (key < p.N) {
-                kreg[i] = *reinterpret_cast<const bf16x8_t*>(kbase + (int64_t)key * p.ks1 + 8 * ch);
-                vreg[i] = *reinterpret_cast<const bf16x8_t*>(vbase + (int64_t)key * p.vs1 + 8 * ch);
-            } else {
-                kreg[i] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-                vreg[i] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-    };
-    auto swrite = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int idx = tid + 256 * i;
-            const int kl = idx / CPR, ch = idx % CPR;
-            *reinterpret_cast<bf16x8_t*>(&sK[buf][kl * KSTR + 8 * ch]) = kreg[i];
-            *reinterpret_cast<bf16x8_t*>(&sV[buf][kl * VSTR + 8 * ch]) = vreg[i];
+        for (int jj = 0; jj < PERW; ++jj) {
+            const int j = wave * PERW + jj;
+            const int slot = 64 * j + lane;
+            const int r = slot / CPR, ps = slot % CPR;
+            const int key = min(kt * kKT + r, p.N - 1);
+            dma16(kbase + (int64_t)key * p.ks1 + 8 * (ps ^ swz_k<D>(r)), lds_addr(att_k<D, ST>()) + 1024 * j);
+            dma16(vbase + (int64_t)key * p.vs1 + 8 * (ps ^ swz_v<D>(r)), lds_addr(att_v<D, ST>()) + 1024 * j);
         }
     };
 
-    // Running row statistics in the log2 domain.  m_run is raised lazily: only when a tile's
-    // row max exceeds it by more than kLazy (so p = 2^(s*c - m_run) <= 2^kLazy stays exact
-    // in fp32/bf16) are O and l rescaled; otherwise the stale max is kept.
-    constexpr float kLazy = 8.f;
     float m_run[kNcb], l_run[kNcb];
     f32x16_t acc[kNcb][NDB];
 #pragma unroll
@@ -192,24 +227,41 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
     if (p.tilelog && wave_has_rows)
         logrow = p.tilelog + ((int64_t)bg * p.row_groups + wrow0 / kRowsPerWave) * p.key_tiles;
 
-    // Transposed-read addressing for V^T: lane (s16, grp) reads 4 bf16 at
-    // V[16kh + 4*(grp>>1) + s16/4 (+8)][32db + 16*(grp&1) + 4*(s16&3)].
+    // Per-lane LDS byte offsets of the MFMA operands (the same for every stage).
+    int koff[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) koff[cc] = hl * (2 * D) + 16 * ((2 * cc + g2) ^ swz_k<D>(hl));
     const int s16 = lane & 15, grp = lane >> 4;
-    const int vkey = 4 * (grp >> 1) + (s16 >> 2);
-    const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);
+    int voff[NDB][2][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int row = 16 * kh + 8 * hf + 4 * (grp >> 1) + (s16 >> 2);
+                const int col = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
+                voff[db][kh][hf] = row * (2 * D) + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
+            }
+        }
+    }
 
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
     const bf16x2v ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-    gload(tile_of(0));
-    swrite(0);
-    __syncthreads();
+    issue(tile_of(0), S0{});
+    if (ntiles > 1) issue(tile_of(1), S1{});
 
-    for (int it = 0; it < ntiles; ++it) {
+    auto body = [&](const int it, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        // Tile `it` is this wave's oldest copy group in flight; once every wave has it, the
+        // barrier also guarantees that the stage read in iteration it-1 is free for tile it+2.
+        if (it + 1 < ntiles) wait_vmcnt<GROUPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 2 < ntiles) issue(tile_of(it + 2), std::integral_constant<int, (ST + 2) % kStages>{});
+
         const int kt = tile_of(it);
-        const int buf = it & 1;
-        if (it + 1 < ntiles) gload(tile_of(it + 1));
-
         const int kb = kt * kKT;
         const int ke = min(kb + kKT, p.N);
         bool lany = false, lall = true;
@@ -224,113 +276,114 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void attn_fwd_bf16_kernel(A
         const int wany = __builtin_amdgcn_readfirstlane(__ballot(lany) != 0ull ? 1 : 0);
         const int wall = __builtin_amdgcn_readfirstlane((kb + kKT <= p.N) && (__ballot(!lall) == 0ull) ? 1 : 0);
         if (logrow && lane == 0 && wany) logrow[kt] = wall ? 2 : 1;
+        if (!wany) return;
 
-        if (wany) {
-            // S^T = K Q^T for this wave's two 32-row column blocks.
-            f32x16_t s[kNcb];
+        const char* kt_lds = reinterpret_cast<const char*>(att_k<D, ST>());
+        const char* vt_lds = reinterpret_cast<const char*>(att_v<D, ST>());
+
+        // S^T = K Q^T for this wave's two 32-row column blocks.
+        f32x16_t s[kNcb];
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[cb][e] = 0.f;
+        }
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt_lds + koff[cc]);
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb)
+                s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], s[cb], 0, 0, 0);
+        }
+        // Element mask on tiles that are not entirely visible.  Element e of this lane holds
+        // key kb + 4*g2 + o(e), o(e) = 8*(e/4) + e%4.
+        if (!wall) {
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb) {
+                const int base = kb + 4 * g2;
+                const int A = rb[cb].hi1 - base, Lo = rb[cb].lo2 - base, Hi = pos[cb] - base;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) s[cb][e] = 0.f;
-            }
-            const uint16_t* kl = &sK[buf][hl * KSTR + 8 * g2];
-#pragma unroll
-            for (int cc = 0; cc < NC; ++cc) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kl + 16 * cc);
-#pragma unroll
-                for (int cb = 0; cb < kNcb; ++cb)
-                    s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], s[cb], 0, 0, 0);
-            }
-            // Element mask on tiles that are not entirely visible.  Element e of this lane
-            // holds key kb + 4*g2 + o(e), o(e) = 8*(e/4) + e%4.
-            if (!wall) {
-#pragma unroll
-                for (int cb = 0; cb < kNcb; ++cb) {
-                    const int base = kb + 4 * g2;
-                    const int A = rb[cb].hi1 - base, Lo = rb[cb].lo2 - base, Hi = pos[cb] - base;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int o = 8 * (e >> 2) + (e & 3);
-                        const bool vis = (o < A) | ((o >= Lo) & (o <= Hi));
-                        s[cb][e] = vis ? s[cb][e] : -INFINITY;
-                    }
-                }
-            }
-            // Row max (this lane's 16 keys, then the partner half), lazy rescale.
-            float mx[kNcb];
-            bool need = false;
-#pragma unroll
-            for (int cb = 0; cb < kNcb; ++cb) {
-                float a = fmaxf(fmaxf(s[cb][0], s[cb][1]), s[cb][2]);
-                float b2 = fmaxf(fmaxf(s[cb][3], s[cb][4]), s[cb][5]);
-                float c2 = fmaxf(fmaxf(s[cb][6], s[cb][7]), s[cb][8]);
-                float d2 = fmaxf(fmaxf(s[cb][9], s[cb][10]), s[cb][11]);
-                float e2 = fmaxf(fmaxf(s[cb][12], s[cb][13]), s[cb][14]);
-                float m = fmaxf(fmaxf(a, b2), fmaxf(fmaxf(c2, d2), fmaxf(e2, s[cb][15])));
-                mx[cb] = half_swap_max(m) * c;
-                need |= mx[cb] > m_run[cb] + kLazy;
-            }
-            if (__builtin_amdgcn_readfirstlane(__ballot(need) != 0ull ? 1 : 0)) {
-#pragma unroll
-                for (int cb = 0; cb < kNcb; ++cb) {
-                    const float mnew = fmaxf(m_run[cb], mx[cb]);
-                    if (mnew > m_run[cb]) {
-                        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
-                        l_run[cb] *= alpha;
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                            for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
-                        }
-                        m_run[cb] = mnew;
-                    }
-                }
-            }
-            // P = 2^(s*c - m) in bf16; l += sum of the rounded P (dot2 with ones).
-            bf16x8_t pb[kNcb][2];
-#pragma unroll
-            for (int cb = 0; cb < kNcb; ++cb) {
-                const float msafe = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
-                float pv[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[cb][e], c, -msafe));
-                float lsum = l_run[cb];
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    // Scalar temporaries: element reads of a partially built vector in this
-                    // unrolled loop were miscompiled (every dot2 read element 0).
-                    const uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
-                    const uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
-                    const uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
-                    const uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w0), ones2, lsum, false);
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w1), ones2, lsum, false);
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w2), ones2, lsum, false);
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w3), ones2, lsum, false);
-                    typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
-                    const u32x4_t w = {w0, w1, w2, w3};
-                    pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
-                }
-                l_run[cb] = lsum;
-            }
-            // O^T += V^T P^T.
-            const uint16_t* vt = &sV[buf][0];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    const uint16_t* a0 = vt + (16 * kh + vkey) * VSTR + 32 * db + vcol;
-                    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(a0));
-                    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(a0 + 8 * VSTR));
-                    const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                    for (int cb = 0; cb < kNcb; ++cb)
-                        acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cb][kh], acc[cb][db], 0, 0, 0);
+                for (int e = 0; e < 16; ++e) {
+                    const int o = 8 * (e >> 2) + (e & 3);
+                    const bool vis = (o < A) | ((o >= Lo) & (o <= Hi));
+                    s[cb][e] = vis ? s[cb][e] : -INFINITY;
                 }
             }
         }
-        if (it + 1 < ntiles) swrite(buf ^ 1);
-        __syncthreads();
+        // Row max (this lane's 16 keys, then the partner half), lazy rescale.
+        float mx[kNcb];
+        bool need = false;
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) {
+            float m = fmaxf(fmaxf(fmaxf(s[cb][0], s[cb][1]), fmaxf(s[cb][2], s[cb][3])),
+                            fmaxf(fmaxf(s[cb][4], s[cb][5]), fmaxf(s[cb][6], s[cb][7])));
+            m = fmaxf(m, fmaxf(fmaxf(fmaxf(s[cb][8], s[cb][9]), fmaxf(s[cb][10], s[cb][11])),
+                               fmaxf(fmaxf(s[cb][12], s[cb][13]), fmaxf(s[cb][14], s[cb][15]))));
+            mx[cb] = half_swap_max(m) * c;
+            need |= mx[cb] > m_run[cb] + kLazy;
+        }
+        if (__builtin_amdgcn_readfirstlane(__ballot(need) != 0ull ? 1 : 0)) {
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) {
+                const float mnew = fmaxf(m_run[cb], mx[cb]);
+                if (mnew > m_run[cb]) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
+                    l_run[cb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                    }
+                    m_run[cb] = mnew;
+                }
+            }
+        }
+        // P = 2^(s*c - m) in bf16; l += sum of the rounded P (dot2 with ones).
+        bf16x8_t pb[kNcb][2];
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) {
+            const float msafe = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+            float pv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[cb][e], c, -msafe));
+            float lsum = l_run[cb];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                // Scalar temporaries: element reads of a partially built vector in this
+                // unrolled loop were miscompiled (every dot2 read element 0).
+                const uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
+                const uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
+                const uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
+                const uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w0), ones2, lsum, false);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w1), ones2, lsum, false);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w2), ones2, lsum, false);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w3), ones2, lsum, false);
+                typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+                const u32x4_t w = {w0, w1, w2, w3};
+                pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
+            }
+            l_run[cb] = lsum;
+        }
+        // O^T += V^T P^T.
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vt_lds + voff[db][kh][0]));
+                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vt_lds + voff[db][kh][1]));
+                const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int cb = 0; cb < kNcb; ++cb)
+                    acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cb][kh], acc[cb][db], 0, 0, 0);
+            }
+        }
+    };
+
+    for (int t0 = 0; t0 < ntiles; t0 += kStages) {
+        body(t0, S0{});
+        if (t0 + 1 < ntiles) body(t0 + 1, S1{});
+        if (t0 + 2 < ntiles) body(t0 + 2, S2{});
     }
 
     // Epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2.

@@ -21,7 +21,7 @@ struct AttnArgs {
 };
 
 // Geometry of the bf16 forward's row/key grouping (for the tile log).
-constexpr int kAttnRowBlock = 64;   // rows per wave
+constexpr int kAttnRowBlock = 32;   // rows per wave
 constexpr int kAttnKeyBlock = 32;   // keys per LDS tile
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s);
