@@ -167,7 +167,8 @@ typedef struct mars_decode_desc {
     int64_t qw_strides[3];  /* q_win [batch][window][n_q_heads][head_dim]: batch, row, head */
     int64_t kw_strides[3];  /* k_win [batch][window][n_kv_heads][head_dim] */
     int64_t vw_strides[3];  /* v_win */
-    int64_t kc_strides[3];  /* k_cache [batch][n_kv_heads][cache_capacity][head_dim]: batch, head, position */
+    int64_t kc_strides[3];  /* k_cache [batch][n_kv_heads][cache_capacity][head_dim]: batch, head, position
+                               (position stride <= 2^25 elements, else MARS_EUNSUPPORTED) */
     int64_t vc_strides[3];  /* v_cache */
     int64_t o_strides[3];   /* o [batch][window][n_q_heads][head_dim] */
 } mars_decode_desc;

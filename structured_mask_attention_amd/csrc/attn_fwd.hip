@@ -19,7 +19,12 @@
 //   * Keys are walked in 32-key tiles over at most two intervals per workgroup (the union
 //     of its rows' visible keys, see mars_device.h); each wave classifies every tile for its
 //     own rows: skipped, computed with the element mask, or computed without it.
-//   * Online softmax in the log2 domain, fp32 statistics, fp32 MFMA accumulation.
+//   * Online softmax in the log2 domain, fp32 statistics, fp32 MFMA accumulation.  Q is
+//     multiplied by scale*log2(e) and rounded to bf16 once per wave, and the first QK MFMA
+//     of a tile takes -m_run as its accumulator input, so scores arrive shifted and P = 2^s
+//     costs one v_exp_f32 per element.  O is rescaled lazily: only when a row max grows by
+//     more than 2^8 over the running one.
+//   * Copy addresses: one wave-uniform base per tile (SGPRs) plus fixed per-lane offsets.
 //   * Workgroup order: heaviest row tiles first (noisy and clean tiles from the far end,
 //     interleaved, then the prompt); the (batch, kv head) index is the fastest-varying part
 //     of the workgroup id, so the round-robin dispatch over the 8 XCDs keeps each pair's
@@ -153,18 +158,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
         rb[cb] = row_bounds(pos[cb], p.P, p.L, p.B);
     }
 
-    // Q^T operand: lane holds Q[row][16c + 8*g2 .. +7] for every chunk c.
+    // Q^T operand: lane holds Q[row][16c + 8*g2 .. +7] for every chunk c, multiplied by
+    // scale*log2(e) and rounded to bf16 once, so the MFMA yields scores in the log2 domain.
+    const float c = p.scale_log2;
     bf16x8_t qf[kNcb][NC];
 #pragma unroll
     for (int cb = 0; cb < kNcb; ++cb) {
         const uint16_t* qp = p.q + b * p.qs0 + (int64_t)pos[cb] * p.qs1 + (int64_t)head[cb] * p.qs2 + 8 * g2;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            if (valid[cb]) {
-                qf[cb][c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
-            } else {
-                qf[cb][c] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            }
+        for (int cc = 0; cc < NC; ++cc) {
+            typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+            u32x4_t w = {0u, 0u, 0u, 0u};
+            if (valid[cb]) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * cc);
+            u32x4_t ws;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ws[j] = pack_bf16x2(__uint_as_float(w[j] << 16) * c, __uint_as_float(w[j] & 0xffff0000u) * c);
+            qf[cb][cc] = __builtin_bit_cast(bf16x8_t, ws);
         }
     }
     // The copies below are invisible to the compiler's wait tracking: finish Q first.
@@ -194,33 +204,62 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
 
     // Copy of key tile kt into stage ST: this wave fills PERW 1 KB windows of K and of V.
     // Window slot (row r, position pos) holds logical chunk pos ^ swz(r) of key kt*32 + r;
-    // rows past N repeat key N-1 (finite values; such keys are always masked).
+    // rows past N repeat key N-1 (finite values; such keys are always masked).  The tile's
+    // first key row is a wave-uniform base; the per-lane byte offsets are fixed.
+    uint32_t kgo[PERW], vgo[PERW];
+#pragma unroll
+    for (int jj = 0; jj < PERW; ++jj) {
+        const int slot = 64 * (wave * PERW + jj) + lane;
+        const int r = slot / CPR, ps = slot % CPR;
+        kgo[jj] = (uint32_t)(r * p.ks1 * 2 + 16 * (ps ^ swz_k<D>(r)));
+        vgo[jj] = (uint32_t)(r * p.vs1 * 2 + 16 * (ps ^ swz_v<D>(r)));
+    }
     auto issue = [&](int kt, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
+        const int k0 = kt * kKT;
+        const uint16_t* kb = kbase + (int64_t)k0 * p.ks1;
+        const uint16_t* vb = vbase + (int64_t)k0 * p.vs1;
+        if (k0 + kKT <= p.N) {
 #pragma unroll
-        for (int jj = 0; jj < PERW; ++jj) {
-            const int j = wave * PERW + jj;
-            const int slot = 64 * j + lane;
-            const int r = slot / CPR, ps = slot % CPR;
-            const int key = min(kt * kKT + r, p.N - 1);
-            dma16(kbase + (int64_t)key * p.ks1 + 8 * (ps ^ swz_k<D>(r)), lds_addr(att_k<D, ST>()) + 1024 * j);
-            dma16(vbase + (int64_t)key * p.vs1 + 8 * (ps ^ swz_v<D>(r)), lds_addr(att_v<D, ST>()) + 1024 * j);
+            for (int jj = 0; jj < PERW; ++jj) {
+                const uint32_t w = lds_addr(att_k<D, ST>()) + 1024 * (wave * PERW + jj);
+                dma16_sv(kb, kgo[jj], w);
+                dma16_sv(vb, vgo[jj], lds_addr(att_v<D, ST>()) + 1024 * (wave * PERW + jj));
+            }
+        } else {
+            const int last = p.N - 1 - k0;
+#pragma unroll
+            for (int jj = 0; jj < PERW; ++jj) {
+                const int j = wave * PERW + jj;
+                const int slot = 64 * j + lane;
+                const int r = slot / CPR, ps = slot % CPR;
+                const int rr = min(r, last);
+                dma16_sv(kb, (uint32_t)(rr * p.ks1 * 2 + 16 * (ps ^ swz_k<D>(r))), lds_addr(att_k<D, ST>()) + 1024 * j);
+                dma16_sv(vb, (uint32_t)(rr * p.vs1 * 2 + 16 * (ps ^ swz_v<D>(r))), lds_addr(att_v<D, ST>()) + 1024 * j);
+            }
         }
     };
 
-    float m_run[kNcb], l_run[kNcb];
-    f32x16_t acc[kNcb][NDB];
+    // Online softmax state per row (log2 domain): m_run = running max (-inf before the first
+    // visible key), l_run = this lane's share of the sum, acc = O^T.  Scores leave the QK
+    // MFMA already shifted by -m_run (the accumulator input is negm = -m_run, or 0 while
+    // m_run = -inf), so P = 2^s needs no per-element subtraction.  thr is the largest
+    // shifted score that needs no rescale: kLazy once m_run is finite, -inf before.
+    float m_run[kNcb], l_run[kNcb], thr[kNcb];
+    f32x16_t acc[kNcb][NDB], negm[kNcb];
 #pragma unroll
     for (int cb = 0; cb < kNcb; ++cb) {
         m_run[cb] = -INFINITY;
         l_run[cb] = 0.f;
+        thr[cb] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) negm[cb][e] = 0.f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[cb][db][e] = 0.f;
         }
     }
-    const float c = p.scale_log2;
 
     const bool wave_has_rows = wrow0 < p.rows_per_pair;
     int8_t* logrow = nullptr;
@@ -272,28 +311,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
                 lall &= range_all(pos[cb], kb, ke, rb[cb]);
             }
         }
-        // Wave-uniform tile class, made scalar so the branches below are real branches.
-        const int wany = __builtin_amdgcn_readfirstlane(__ballot(lany) != 0ull ? 1 : 0);
-        const int wall = __builtin_amdgcn_readfirstlane((kb + kKT <= p.N) && (__ballot(!lall) == 0ull) ? 1 : 0);
+        // Wave-uniform tile class (ballots are scalar, so the branches below are real branches).
+        const bool wany = __builtin_amdgcn_ballot_w64(lany) != 0ull;
+        const bool wall = (kb + kKT <= p.N) && __builtin_amdgcn_ballot_w64(!lall) == 0ull;
         if (logrow && lane == 0 && wany) logrow[kt] = wall ? 2 : 1;
         if (!wany) return;
 
         const char* kt_lds = reinterpret_cast<const char*>(att_k<D, ST>());
         const char* vt_lds = reinterpret_cast<const char*>(att_v<D, ST>());
 
-        // S^T = K Q^T for this wave's two 32-row column blocks.
+        // S^T = K Q^T - m_run (log2 domain) for this wave's column blocks.
         f32x16_t s[kNcb];
-#pragma unroll
-        for (int cb = 0; cb < kNcb; ++cb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[cb][e] = 0.f;
-        }
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
             const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt_lds + koff[cc]);
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb)
-                s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], s[cb], 0, 0, 0);
+                s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], cc == 0 ? negm[cb] : s[cb], 0, 0, 0);
         }
         // Element mask on tiles that are not entirely visible.  Element e of this lane holds
         // key kb + 4*g2 + o(e), o(e) = 8*(e/4) + e%4.
@@ -310,7 +344,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
                 }
             }
         }
-        // Row max (this lane's 16 keys, then the partner half), lazy rescale.
+        // Row max of the shifted scores (this lane's 16 keys, then the partner half); lazy
+        // rescale when some row's max exceeds thr.
         float mx[kNcb];
         bool need = false;
 #pragma unroll
@@ -319,13 +354,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
                             fmaxf(fmaxf(s[cb][4], s[cb][5]), fmaxf(s[cb][6], s[cb][7])));
             m = fmaxf(m, fmaxf(fmaxf(fmaxf(s[cb][8], s[cb][9]), fmaxf(s[cb][10], s[cb][11])),
                                fmaxf(fmaxf(s[cb][12], s[cb][13]), fmaxf(s[cb][14], s[cb][15]))));
-            mx[cb] = half_swap_max(m) * c;
-            need |= mx[cb] > m_run[cb] + kLazy;
+            mx[cb] = half_swap_max(m);
+            need |= mx[cb] > thr[cb];
         }
-        if (__builtin_amdgcn_readfirstlane(__ballot(need) != 0ull ? 1 : 0)) {
+        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb) {
-                const float mnew = fmaxf(m_run[cb], mx[cb]);
+                // Offset currently applied to s: m_run, or 0 while m_run = -inf.
+                const float off = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+                const float mnew = fmaxf(m_run[cb], off + mx[cb]);
                 if (mnew > m_run[cb]) {
                     const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
                     l_run[cb] *= alpha;
@@ -334,18 +371,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
                     }
+                    const float delta = mnew - off;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) s[cb][e] -= delta;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) negm[cb][e] = -mnew;
                     m_run[cb] = mnew;
+                    thr[cb] = kLazy;
                 }
             }
         }
-        // P = 2^(s*c - m) in bf16; l += sum of the rounded P (dot2 with ones).
+        // P = 2^s in bf16; l += sum of the rounded P (dot2 with ones).
         bf16x8_t pb[kNcb][2];
 #pragma unroll
         for (int cb = 0; cb < kNcb; ++cb) {
-            const float msafe = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
             float pv[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[cb][e], c, -msafe));
+            for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(s[cb][e]);
             float lsum = l_run[cb];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {

@@ -5,11 +5,11 @@
 // Two kernels on the caller's stream:
 //   1. split: one wave per (sequence, kv head, CH-key cache chunk).  The G*W query rows
 //      of a kv head (G = Hq/Hkv query heads x W window rows, <= 64) form one or two
-//      32-column MFMA blocks; S^T = K Q^T (K fragments loaded straight from HBM as the A
-//      operand), online softmax, O^T += V^T P^T (V staged through LDS and read back
-//      transposed with ds_read_b64_tr_b16).  The next 32-key step is prefetched into
-//      registers while the current one computes.  Each chunk writes an unnormalised
-//      partial (acc, m, l) to the workspace.
+//      32-column MFMA blocks; S^T = K Q^T (K tile read from LDS as the A operand), online
+//      softmax, O^T += V^T P^T (V read back transposed with ds_read_b64_tr_b16).  K and V
+//      32-key steps stream into a 3-stage LDS ring by global_load_lds_dwordx4 (two steps
+//      in flight; a wave-uniform base per step plus fixed per-lane offsets).  Each chunk
+//      writes an unnormalised partial (acc, m, l) to the workspace.
 //   2. combine: one workgroup per (sequence, query head): the window keys (at most W dot
 //      products per row) and a log-sum-exp merge of the chunk partials.
 // Chunks past a sequence's length exit at once, so the grid is fixed while the work is
@@ -95,16 +95,38 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
     // DMA of step `step` into stage arrays (sk, sv): slot (row r, position pos) holds logical
     // chunk pos ^ swz(r) of key k0 + r (keys past the chunk end repeat its last key; they are
     // masked to -inf, and repeating a real row keeps V finite).
+    // Per-lane byte offsets of the copy windows relative to the step's first key row
+    // (row r of window j = (64 j + lane) / CPR); the step base is a uniform pointer.
+    uint32_t ko[NINS], vo[NINS];
+#pragma unroll
+    for (int j = 0; j < NINS; ++j) {
+        const int slot = 64 * j + lane;
+        const int r = slot / CPR, pos = slot % CPR;
+        ko[j] = (uint32_t)(r * p.kcs2 * 2 + 16 * (pos ^ swz_k<D>(r)));
+        vo[j] = (uint32_t)(r * p.vcs2 * 2 + 16 * (pos ^ swz_v<D>(r)));
+    }
     auto issue = [&](int step, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
         const int k0 = k_begin + step * kStep;
+        const uint16_t* kb = kbase + (int64_t)k0 * p.kcs2;
+        const uint16_t* vb = vbase + (int64_t)k0 * p.vcs2;
+        if (__builtin_amdgcn_readfirstlane(k0 + kStep <= k_end ? 1 : 0)) {
 #pragma unroll
-        for (int j = 0; j < NINS; ++j) {
-            const int slot = 64 * j + lane;
-            const int r = slot / CPR, pos = slot % CPR;
-            const int key = min(k0 + r, k_end - 1);
-            dma16(kbase + (int64_t)key * p.kcs2 + 8 * (pos ^ swz_k<D>(r)), lds_addr(dec_k<ST>()) + 1024 * j);
-            dma16(vbase + (int64_t)key * p.vcs2 + 8 * (pos ^ swz_v<D>(r)), lds_addr(dec_v<ST>()) + 1024 * j);
+            for (int j = 0; j < NINS; ++j) {
+                dma16_sv(kb, ko[j], lds_addr(dec_k<ST>()) + 1024 * j);
+                dma16_sv(vb, vo[j], lds_addr(dec_v<ST>()) + 1024 * j);
+            }
+        } else {
+            // Last, partial step of the chunk: rows past the end repeat the last key.
+            const int last = k_end - 1 - k0;
+#pragma unroll
+            for (int j = 0; j < NINS; ++j) {
+                const int slot = 64 * j + lane;
+                const int r = slot / CPR, pos = slot % CPR;
+                const int rr = min(r, last);
+                dma16_sv(kb, (uint32_t)(rr * p.kcs2 * 2 + 16 * (pos ^ swz_k<D>(r))), lds_addr(dec_k<ST>()) + 1024 * j);
+                dma16_sv(vb, (uint32_t)(rr * p.vcs2 * 2 + 16 * (pos ^ swz_v<D>(r))), lds_addr(dec_v<ST>()) + 1024 * j);
+            }
         }
     };
     using S0 = std::integral_constant<int, 0>;

@@ -186,6 +186,8 @@ int mars_tile_map(const mars_attn_desc* desc, int32_t bm, int32_t bn, int8_t* ma
 
 // ---------------------------------------------------------------------------------------
 
+constexpr int64_t kMaxCachePosStride = int64_t(1) << 25;
+
 static int check_decode_desc(const mars_decode_desc* d) {
     if (!d) return MARS_EINVAL;
     if (d->batch < 0 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->window < 1 || d->cache_capacity < 0)
@@ -222,6 +224,9 @@ int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void
     if (!strides_ok(desc->qw_strides, 2) || !strides_ok(desc->kw_strides, 2) || !strides_ok(desc->vw_strides, 2) ||
         !strides_ok(desc->kc_strides, 2) || !strides_ok(desc->vc_strides, 2) || !strides_ok(desc->o_strides, 2))
         return MARS_EINVAL;
+    // The cache copies address 32 positions from one base with 32-bit byte offsets.
+    if (desc->kc_strides[2] > kMaxCachePosStride || desc->vc_strides[2] > kMaxCachePosStride)
+        return MARS_EUNSUPPORTED;
     const size_t need = mars::decode_workspace_bytes(desc->batch, desc->n_kv_heads,
                                                      desc->n_q_heads / desc->n_kv_heads, desc->window,
                                                      desc->head_dim, desc->cache_capacity);

@@ -113,6 +113,20 @@ __device__ inline void dma16(const void* gsrc, uint32_t lds_window) {
         : "memory");
 }
 
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset
+// (global_load_lds_dwordx4 v_off, s_base): no per-lane 64-bit address arithmetic.
+__device__ inline void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_window) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_window), "v"(voff), "s"(sbase)
+        : "memory");
+}
+
 // s_waitcnt vmcnt(N) for the gfx9 encoding (expcnt/lgkmcnt left unconstrained).
 template <int N>
 __device__ inline void wait_vmcnt() {

@@ -11,6 +11,30 @@ PMAX_ABS = 1e-5
 TIE_ZONE = 1e-5
 
 
+def lse_bound(q, k, scale=None):
+    """Per-row bound [b, Hq, N] on |LSE_kernel - LSE_exact| (nats) for the bf16 kernel.
+
+    Two roundings enter the kernel's log-sum-exp beyond fp32 accumulation:
+      * every probability term is rounded to bf16 before it is summed, which moves log l
+        by at most u = 2^-9 (relative rounding of bf16, round to nearest);
+      * Q is multiplied by scale*log2(e) and rounded to bf16 once, which moves score j of
+        row r by at most u * c * sum_i |q_ri| |k_ji| (log2 units; c = scale*log2(e)), and
+        log-sum-exp moves by at most the largest score change.  The max is taken over
+        every key (a superset of the visible ones).
+    Plus 1e-5 for fp32 arithmetic.
+    """
+    qa, ka = np.abs(to_np64(q)), np.abs(to_np64(k))
+    b, N, hq, d = qa.shape
+    G = hq // ka.shape[2]
+    c = (1.0 / np.sqrt(d) if scale is None else scale) * np.log2(np.e)
+    u = 2.0 ** -9
+    out = np.empty((b, hq, N))
+    for bi in range(b):
+        for h in range(hq):
+            out[bi, h] = (qa[bi, :, h, :] @ ka[bi, :, h // G, :].T).max(axis=1)
+    return u + np.log(2.0) * u * c * out + 1e-5
+
+
 def dev():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
     return torch.device("cuda:0")
