@@ -91,7 +91,8 @@ typedef struct mars_attn_desc {
     float scale;         /* softmax scale; 0 means 1/sqrt(head_dim); must be finite */
     int32_t reserved;    /* must be 0 */
     int64_t q_strides[3]; /* q [batch][N][n_q_heads][head_dim]: batch, position, head */
-    int64_t k_strides[3]; /* k [batch][N][n_kv_heads][head_dim] */
+    int64_t k_strides[3]; /* k [batch][N][n_kv_heads][head_dim]; position stride (k and v)
+                             <= 2^25 elements, else MARS_EUNSUPPORTED */
     int64_t v_strides[3]; /* v [batch][N][n_kv_heads][head_dim] */
     int64_t o_strides[3]; /* o [batch][N][n_q_heads][head_dim] */
 } mars_attn_desc;

@@ -23,6 +23,8 @@ bool strides_ok(const int64_t s[3], int elem_bytes) {
     return true;
 }
 
+constexpr int64_t kMaxKeyPosStride = int64_t(1) << 25;
+
 int map_hip(hipError_t e) { return e == hipSuccess ? MARS_OK : MARS_EHIP; }
 
 int check_attn_desc(const mars_attn_desc* d) {
@@ -53,6 +55,8 @@ int check_attn_tensors(const mars_attn_desc* d, const void* q, const void* k, co
     if (!strides_ok(d->q_strides, eb) || !strides_ok(d->k_strides, eb) || !strides_ok(d->v_strides, eb) ||
         !strides_ok(d->o_strides, eb))
         return MARS_EINVAL;
+    // The K/V tile copies address 32 positions from one base with 32-bit byte offsets.
+    if (d->k_strides[1] > kMaxKeyPosStride || d->v_strides[1] > kMaxKeyPosStride) return MARS_EUNSUPPORTED;
     return MARS_OK;
 }
 

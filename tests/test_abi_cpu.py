@@ -59,6 +59,8 @@ def test_attn_validation_errors():
     assert _attn(d) == L.MARS_EINVAL                      # Hq % Hkv
     d = good(); d.head_dim = 96
     assert _attn(d) == L.MARS_EUNSUPPORTED
+    d = good(); d.v_strides[1] = (1 << 25) + 8             # 32 positions overflow 32-bit offsets
+    assert _attn(d) == L.MARS_EUNSUPPORTED
     d = good(); d.block = 0
     assert _attn(d) == L.MARS_EINVAL
     d = good(); d.resp_len = -1
