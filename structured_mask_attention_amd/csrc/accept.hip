@@ -5,11 +5,13 @@
 //
 // Two launches on the caller's stream; the kernel boundary orders them, so no device-scope
 // fences or counters are needed and the workspace needs no initialisation.
-//   1. slices: grid (rows = batch*W, slices); a 256-thread workgroup owns one 8192-entry
-//      slice of one row.  Each thread issues all four of its 16-byte loads before any
-//      math, converts bf16 -> fp32 with shifts/masks, takes the max with v_max3, finds the
-//      lowest index attaining it hierarchically (vector max first) and sums
-//      2^((l - m) log2 e) with the raw v_exp_f32.  (max, argmax, sum) triples are merged
+//   1. slices: grid (rows = batch*W, slices); a 256-thread workgroup owns one 16384-entry
+//      slice of one row (at the 152k vocabulary every workgroup is resident at once): all
+//      of its loads are issued up front, then four 4096-entry chunks are reduced in order
+//      as their data arrives.  Each thread keeps a
+//      running (max, lowest argmax, sum of 2^((l - m) log2 e)) over its entries; values
+//      stay packed bf16 until used (shift/mask to fp32), the sum uses the raw v_exp_f32
+//      and is rescaled when the max grows.  The (max, argmax, sum) triples are merged
 //      across the wave (shuffles) and the workgroup (LDS) and written to the workspace.
 //   2. finish: one workgroup per sequence merges the slices of each row in a fixed order
 //      (one wave per row), writes tokens and pmax, and applies the tau-prefix rule.
@@ -23,8 +25,10 @@ namespace mars {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 4;                              // 16-byte vectors per thread
-constexpr int kSlice = kThreads * 8 * kVec;          // 8192 vocabulary entries per workgroup
+constexpr int kVecPerChunk = 2;                      // 16-byte vectors per thread and chunk
+constexpr int kChunk = kThreads * 8 * kVecPerChunk;  // 4096 vocabulary entries per chunk
+constexpr int kChunks = 4;                           // chunks per workgroup
+constexpr int kSlice = kChunk * kChunks;             // 16384 vocabulary entries per workgroup
 constexpr int kMaxWindow = 64;
 
 struct AcceptKParams {
@@ -73,6 +77,56 @@ __device__ inline Part wave_reduce(Part x) {
 __device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Entry j (0..7) of a 16-byte vector held as four packed bf16 words, as fp32.
+__device__ inline float entry(const uint32_t (&w)[4], int j) {
+    return (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
+}
+
+// Vectors of chunk c of this thread's slice: vector v covers entries e0 .. e0+7 with
+// e0 = v0 + c*kChunk + 8*(tid + kThreads*v), increasing in (c, v).
+__device__ inline int vec_start(int v0, int c, int tid, int k) { return v0 + c * kChunk + 8 * (tid + kThreads * k); }
+
+// Issue the loads of chunk c; nothing here uses the loaded values, so no wait is needed
+// until the chunk is reduced.  V % 8 == 0: every vector is whole, and vectors at or past
+// v1 re-read the last vector (always in bounds); finish_chunk masks them to -inf.
+// Otherwise (ragged V) the partial vector is read entry by entry, entries past v1 as -inf.
+template <bool RAGGED>
+__device__ inline void load_chunk(const uint16_t* rowp, int v0, int v1, int c, int tid, uint32_t (&w)[kVecPerChunk][4]) {
+#pragma unroll
+    for (int k = 0; k < kVecPerChunk; ++k) {
+        const int e0 = vec_start(v0, c, tid, k);
+        if (!RAGGED) {
+            const uint4 q = *reinterpret_cast<const uint4*>(rowp + (e0 < v1 ? e0 : v1 - 8));
+            w[k][0] = q.x; w[k][1] = q.y; w[k][2] = q.z; w[k][3] = q.w;
+        } else if (e0 + 8 <= v1) {
+            const uint4 q = *reinterpret_cast<const uint4*>(rowp + e0);
+            w[k][0] = q.x; w[k][1] = q.y; w[k][2] = q.z; w[k][3] = q.w;
+        } else if (e0 >= v1) {
+            w[k][0] = w[k][1] = w[k][2] = w[k][3] = 0xff80ff80u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ea = e0 + 2 * j, eb = ea + 1;
+                const uint32_t lo = ea < v1 ? (uint32_t)rowp[ea] : 0xff80u;
+                const uint32_t hi = eb < v1 ? (uint32_t)rowp[eb] : 0xff80u;
+                w[k][j] = lo | (hi << 16);
+            }
+        }
+    }
+}
+
+// Replace the re-read vectors past v1 by -inf (bf16 0xff80 pairs); a no-op for ragged V.
+template <bool RAGGED>
+__device__ inline void finish_chunk(int v0, int v1, int c, int tid, uint32_t (&w)[kVecPerChunk][4]) {
+    if (RAGGED) return;
+#pragma unroll
+    for (int k = 0; k < kVecPerChunk; ++k) {
+        const bool in = vec_start(v0, c, tid, k) < v1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[k][j] = in ? w[k][j] : 0xff80ff80u;
+    }
+}
+
 // RAGGED: V is not a multiple of 8, so the last vector of a row is read entry by entry.
 template <bool RAGGED>
 __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p) {
@@ -85,77 +139,62 @@ __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p)
     const int v1 = min(p.V, v0 + kSlice);
     const uint16_t* rowp = p.logits + b * p.bstride + (int64_t)i * p.rstride;
 
-    // Loads: vector k of this thread covers entries e0(k) .. e0(k)+7, e0(k) increasing in k.
-    uint32_t w[kVec][4];
+    // All loads of the slice are issued first (32 KB in flight per workgroup); the chunks
+    // are then reduced in order as their data arrives, into this thread's running (max,
+    // lowest argmax, sum).  sched_barrier keeps the compiler from hoisting any use of the
+    // loaded words above the later loads (which would wait for the data and serialise them).
+    Part x{-INFINITY, 0.f, 0x7fffffff};
+    uint32_t w[kChunks][kVecPerChunk][4];
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-        const int e0 = v0 + 8 * (tid + kThreads * k);
-        if (!RAGGED) {
-            // V % 8 == 0: every vector is whole.  Vectors past the row end re-read the last
-            // vector (always in bounds) and are replaced by -inf (bf16 0xff80) without a branch.
-            const bool in = e0 < v1;
-            const uint4 q = *reinterpret_cast<const uint4*>(rowp + (in ? e0 : v1 - 8));
-            w[k][0] = in ? q.x : 0xff80ff80u;
-            w[k][1] = in ? q.y : 0xff80ff80u;
-            w[k][2] = in ? q.z : 0xff80ff80u;
-            w[k][3] = in ? q.w : 0xff80ff80u;
-        } else if (e0 + 8 <= v1) {
-            const uint4 q = *reinterpret_cast<const uint4*>(rowp + e0);
-            w[k][0] = q.x; w[k][1] = q.y; w[k][2] = q.z; w[k][3] = q.w;
-        } else if (e0 >= v1) {
-            w[k][0] = w[k][1] = w[k][2] = w[k][3] = 0xff80ff80u;
-        } else {
-            // Ragged last vector: entries past V read as -inf.
+    for (int c = 0; c < kChunks; ++c) load_chunk<RAGGED>(rowp, v0, v1, c, tid, w[c]);
+    __builtin_amdgcn_sched_barrier(0);
+    auto reduce_chunk = [&](const int c, uint32_t (&w)[kVecPerChunk][4]) __attribute__((always_inline)) {
+        finish_chunk<RAGGED>(v0, v1, c, tid, w);
+        float vmax[kVecPerChunk];
+#pragma unroll
+        for (int k = 0; k < kVecPerChunk; ++k) {
+            vmax[k] = fmaxf(fmaxf(fmaxf(entry(w[k], 0), entry(w[k], 1)), fmaxf(entry(w[k], 2), entry(w[k], 3))),
+                            fmaxf(fmaxf(entry(w[k], 4), entry(w[k], 5)), fmaxf(entry(w[k], 6), entry(w[k], 7))));
+        }
+        float cm = vmax[0];
+#pragma unroll
+        for (int k = 1; k < kVecPerChunk; ++k) cm = fmaxf(cm, vmax[k]);
+        if (cm > x.m) {
+            // New running max: its lowest index in this chunk (first vector, first entry),
+            // and the sum so far rescaled to it (0 while the old max is -inf).
+            int kk = kVecPerChunk - 1;
+#pragma unroll
+            for (int k = kVecPerChunk - 2; k >= 0; --k) kk = (vmax[k] == cm) ? k : kk;
+            uint32_t sel[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int ea = e0 + 2 * j, eb = ea + 1;
-                const uint32_t lo = ea < v1 ? (uint32_t)rowp[ea] : 0xff80u;
-                const uint32_t hi = eb < v1 ? (uint32_t)rowp[eb] : 0xff80u;
-                w[k][j] = lo | (hi << 16);
+                sel[j] = w[kVecPerChunk - 1][j];
+#pragma unroll
+                for (int k = kVecPerChunk - 2; k >= 0; --k) sel[j] = (kk == k) ? w[k][j] : sel[j];
             }
+            int ee = 7;
+#pragma unroll
+            for (int e = 6; e >= 0; --e) ee = (entry(sel, e) == cm) ? e : ee;
+            x.idx = v0 + c * kChunk + 8 * (tid + kThreads * kk) + ee;
+            x.s *= __builtin_amdgcn_exp2f((x.m - cm) * kLog2e);
+            x.m = cm;
         }
-    }
-
-    float f[kVec][8];
-    float vmax[kVec];
+        if (x.m != -INFINITY) {
+            const float mb = x.m * kLog2e;
+            float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) {
+            for (int k = 0; k < kVecPerChunk; ++k) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[k][2 * j] = lo_bf16(w[k][j]);
-            f[k][2 * j + 1] = hi_bf16(w[k][j]);
-        }
-        vmax[k] = fmaxf(fmaxf(fmaxf(f[k][0], f[k][1]), fmaxf(f[k][2], f[k][3])),
-                        fmaxf(fmaxf(f[k][4], f[k][5]), fmaxf(f[k][6], f[k][7])));
-    }
-    Part x;
-    x.m = fmaxf(fmaxf(vmax[0], vmax[1]), fmaxf(vmax[2], vmax[3]));
-    // Lowest index attaining the max: first vector holding it, then first entry in it.
-    int kk = kVec - 1;
-#pragma unroll
-    for (int k = kVec - 2; k >= 0; --k) kk = (vmax[k] == x.m) ? k : kk;
-    float gsel[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gsel[e] = kk == 0 ? f[0][e] : (kk == 1 ? f[1][e] : (kk == 2 ? f[2][e] : f[3][e]));
-    int ee = 7;
-#pragma unroll
-    for (int e = 6; e >= 0; --e) ee = (gsel[e] == x.m) ? e : ee;
-    x.idx = (x.m == -INFINITY) ? 0x7fffffff : v0 + 8 * (tid + kThreads * kk) + ee;
-    // Sum of 2^((l - m) log2 e) over the thread's entries (two partial sums).
-    x.s = 0.f;
-    if (x.m != -INFINITY) {
-        const float mb = x.m * kLog2e;
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                s0 += __builtin_amdgcn_exp2f(fmaf(f[k][e], kLog2e, -mb));
-                s1 += __builtin_amdgcn_exp2f(fmaf(f[k][e + 1], kLog2e, -mb));
+                for (int e = 0; e < 8; e += 2) {
+                    s0 += __builtin_amdgcn_exp2f(fmaf(entry(w[k], e), kLog2e, -mb));
+                    s1 += __builtin_amdgcn_exp2f(fmaf(entry(w[k], e + 1), kLog2e, -mb));
+                }
             }
+            x.s += s0 + s1;
         }
-        x.s = s0 + s1;
-    }
+    };
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) reduce_chunk(c, w[c]);
 
     x = wave_reduce(x);
     if (lane == 0) red[wave] = x;
