@@ -162,7 +162,7 @@ typedef struct mars_decode_desc {
     int32_t n_kv_heads;     /* >= 1 */
     int32_t head_dim;       /* 128 or 64 */
     int32_t window;         /* 1 <= window; (n_q_heads/n_kv_heads) * window <= 64 */
-    int32_t cache_capacity; /* >= 0: positions allocated per (sequence, kv head) */
+    int32_t cache_capacity; /* 0 ..= 65535*512: positions allocated per (sequence, kv head) */
     int32_t dtype;          /* MARS_DTYPE_BF16 */
     float scale;            /* 0 means 1/sqrt(head_dim); must be finite */
     int64_t qw_strides[3];  /* q_win [batch][window][n_q_heads][head_dim]: batch, row, head */

@@ -62,14 +62,32 @@ __device__ inline Part merge(Part a, Part b) {
     return r;
 }
 
+template <int CTRL>
+__device__ inline Part dpp_part(Part x) {
+    return Part{dpp_f32<CTRL>(x.m), dpp_f32<CTRL>(x.s), __float_as_int(dpp_f32<CTRL>(__int_as_float(x.idx)))};
+}
+
+// merge() is symmetric in its arguments, so each step may pair lanes by any involution:
+// quad swaps, half-row and row mirrors (DPP), then rows of 16 and halves of 32 exchanged
+// with v_permlane16_swap / v_permlane32_swap (which hand each lane both values).
 __device__ inline Part wave_reduce(Part x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        Part y;
-        y.m = __shfl_xor(x.m, off);
-        y.s = __shfl_xor(x.s, off);
-        y.idx = __shfl_xor(x.idx, off);
-        x = merge(x, y);
+    x = merge(x, dpp_part<0xB1>(x));
+    x = merge(x, dpp_part<0x4E>(x));
+    x = merge(x, dpp_part<0x141>(x));
+    x = merge(x, dpp_part<0x140>(x));
+    {
+        auto m = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.m), __float_as_uint(x.m), false, false);
+        auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.s), __float_as_uint(x.s), false, false);
+        auto i = __builtin_amdgcn_permlane16_swap((uint32_t)x.idx, (uint32_t)x.idx, false, false);
+        x = merge(Part{__uint_as_float(m[0]), __uint_as_float(s[0]), (int)i[0]},
+                  Part{__uint_as_float(m[1]), __uint_as_float(s[1]), (int)i[1]});
+    }
+    {
+        auto m = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.m), __float_as_uint(x.m), false, false);
+        auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.s), __float_as_uint(x.s), false, false);
+        auto i = __builtin_amdgcn_permlane32_swap((uint32_t)x.idx, (uint32_t)x.idx, false, false);
+        x = merge(Part{__uint_as_float(m[0]), __uint_as_float(s[0]), (int)i[0]},
+                  Part{__uint_as_float(m[1]), __uint_as_float(s[1]), (int)i[1]});
     }
     return x;
 }

@@ -24,7 +24,7 @@ namespace mars {
 
 namespace {
 
-constexpr int kCH = 512;      // cache keys per split workgroup
+constexpr int kCH = kDecodeChunk;   // cache keys per split workgroup
 constexpr int kStep = 32;     // keys per MFMA step
 constexpr int kStages = 3;    // LDS ring depth of the split kernel
 
@@ -79,7 +79,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
     constexpr float kLazy = 8.f;
     static_assert(D <= 128, "ring sized for head_dim <= 128");
 
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // Grid: x = (sequence, kv head) pair, y = chunk.  With x fastest, every pair's chunk 0
+    // is dispatched first, then chunk 1, ...: the chunks that exist (most have small c)
+    // spread over all CUs instead of piling up behind the empty ones.
+    const int c = blockIdx.y, b = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
     const int len = clamp_len(p.cache_len[b], p.cap);
     const int k_begin = c * kCH;
     if (k_begin >= len) return;
@@ -146,12 +149,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
         for (int cc = 0; cc < NC; ++cc)
             qf[cb][cc] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * cc) : bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    // Drain the Q loads before any copy is issued: the compiler does not count the copies,
-    // so a Q wait inside the loop would otherwise become a full vmcnt(0).
-    wait_vmcnt<0>();
-
     issue(0, S0{});
     if (nsteps > 1) issue(1, S1{});
+    // Drain the Q loads (issued before the copies, so their latencies overlap) here: the
+    // compiler does not count the copies, so a Q wait left to it inside the loop would
+    // become a full vmcnt(0).
+    wait_vmcnt<0>();
 
     float m_run[NCB], l_run[NCB];
     f32x16_t acc[NCB][NDB];
@@ -326,13 +329,34 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
     }
 }
 
+// DPT consecutive bf16 (DPT = 4 or 2) of one row, as fp32.
+template <int DPT>
+struct BfRow {
+    uint32_t w[DPT / 2];
+    __device__ inline void load(const uint16_t* src) {
+        if constexpr (DPT == 4) {
+            const uint2 q = *reinterpret_cast<const uint2*>(src);
+            w[0] = q.x;
+            w[1] = q.y;
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t*>(src);
+        }
+    }
+    __device__ inline float operator[](int e) const {
+        const uint32_t x = w[e >> 1];
+        return (e & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+    }
+};
+
 // One 256-thread workgroup per (sequence, kv head, group of 8 query rows u = i*G + hh);
-// 32 threads per row, each owning D/32 consecutive output columns.  The chunk partials are
-// merged online (max, rescale, accumulate) with independent loads per chunk, then the
-// window keys 0..i are added (dot products reduced over the row's 32 threads).
+// 32 threads per row, each owning D/32 consecutive output columns.  The chunk partials
+// and then the window keys 0..i (dot products reduced over the row's 32 threads) are
+// merged online (max, rescale, accumulate), in batches of kPre whose loads are all issued
+// before any of them is used.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeKParams p) {
     constexpr int DPT = D / 32;   // columns per thread (4 or 2)
+    constexpr int kPre = 8;       // chunk partials / window rows fetched per batch
     const int rg = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int t = threadIdx.x;
     const int u = rg * 8 + (t >> 5);
@@ -343,62 +367,74 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeKParams p) {
     const int nch = (len + kCH - 1) / kCH;
     const int d0 = l32 * DPT;
 
+    BfRow<DPT> qv;
+    qv.load(p.qw + b * p.qws0 + (int64_t)i * p.qws1 + (int64_t)h * p.qws2 + d0);
+    // Chunk partials (unnormalised acc, running max m, sum l) and window rows are fetched
+    // in batches of kPre; the first batch of each is issued before anything is used.
+    const int64_t slot0 = ((int64_t)(b * p.hkv + g) * p.nchunk) * p.R + u;
+    float a[kPre][DPT];
+    float2 ml[kPre];
+    auto load_chunks = [&](int c0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+            const int64_t sl = slot0 + (int64_t)min(c0 + k, nch - 1) * p.R;
+            ml[k] = *reinterpret_cast<const float2*>(p.ws_ml + sl * 2);
+            if constexpr (DPT == 4) {
+                const float4 q = *reinterpret_cast<const float4*>(p.ws_acc + sl * D + d0);
+                a[k][0] = q.x; a[k][1] = q.y; a[k][2] = q.z; a[k][3] = q.w;
+            } else {
+                const float2 q = *reinterpret_cast<const float2*>(p.ws_acc + sl * D + d0);
+                a[k][0] = q.x; a[k][1] = q.y;
+            }
+        }
+    };
+    if (nch > 0) load_chunks(0);
+    BfRow<DPT> kr[kPre], vr[kPre];
+    auto load_window = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+            const int j = min(j0 + k, i);
+            kr[k].load(p.kw + b * p.kws0 + (int64_t)j * p.kws1 + (int64_t)g * p.kws2 + d0);
+            vr[k].load(p.vw + b * p.vws0 + (int64_t)j * p.vws1 + (int64_t)g * p.vws2 + d0);
+        }
+    };
+    load_window(0);
+
     float M = -INFINITY, den = 0.f;
     float num[DPT];
 #pragma unroll
     for (int e = 0; e < DPT; ++e) num[e] = 0.f;
+    auto merge = [&](float mj, float lj, const float (&aj)[DPT]) __attribute__((always_inline)) {
+        const float Mn = fmaxf(M, mj);
+        const float r0 = __builtin_amdgcn_exp2f(M - Mn), rj = __builtin_amdgcn_exp2f(mj - Mn);
+        den = den * r0 + lj * rj;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) num[e] = num[e] * r0 + aj[e] * rj;
+        M = Mn;
+    };
 
-    const int64_t slot0 = ((int64_t)(b * p.hkv + g) * p.nchunk) * p.R + u;
-    int cc = 0;
-    for (; cc + 1 < nch; cc += 2) {   // two chunks per step: loads issued together
-        const int64_t sa = slot0 + (int64_t)cc * p.R, sb = sa + p.R;
-        const float2 mla = *reinterpret_cast<const float2*>(p.ws_ml + sa * 2);
-        const float2 mlb = *reinterpret_cast<const float2*>(p.ws_ml + sb * 2);
-        float aa[DPT], ab[DPT];
+    for (int c0 = 0; c0 < nch; c0 += kPre) {
+        if (c0 > 0) load_chunks(c0);
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) {
-            aa[e] = p.ws_acc[sa * D + d0 + e];
-            ab[e] = p.ws_acc[sb * D + d0 + e];
-        }
-        const float Mn = fmaxf(M, fmaxf(mla.x, mlb.x));
-        const float r0 = __builtin_amdgcn_exp2f(M - Mn), ra = __builtin_amdgcn_exp2f(mla.x - Mn),
-                    rb = __builtin_amdgcn_exp2f(mlb.x - Mn);
-        den = den * r0 + mla.y * ra + mlb.y * rb;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) num[e] = num[e] * r0 + aa[e] * ra + ab[e] * rb;
-        M = Mn;
-    }
-    if (cc < nch) {
-        const int64_t sa = slot0 + (int64_t)cc * p.R;
-        const float2 mla = *reinterpret_cast<const float2*>(p.ws_ml + sa * 2);
-        const float Mn = fmaxf(M, mla.x);
-        const float r0 = __builtin_amdgcn_exp2f(M - Mn), ra = __builtin_amdgcn_exp2f(mla.x - Mn);
-        den = den * r0 + mla.y * ra;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) num[e] = num[e] * r0 + p.ws_acc[sa * D + d0 + e] * ra;
-        M = Mn;
+        for (int k = 0; k < kPre; ++k)
+            if (c0 + k < nch) merge(ml[k].x, ml[k].y, a[k]);
     }
 
     // Window keys 0..i of this sequence (causal, self-inclusive).
-    const uint16_t* qp = p.qw + b * p.qws0 + (int64_t)i * p.qws1 + (int64_t)h * p.qws2 + d0;
-    float qv[DPT];
+    for (int j0 = 0; j0 <= i; j0 += kPre) {
+        if (j0 > 0) load_window(j0);
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) qv[e] = bf16_bits_to_f32(qp[e]);
-    for (int j = 0; j <= i; ++j) {
-        const uint16_t* kp = p.kw + b * p.kws0 + (int64_t)j * p.kws1 + (int64_t)g * p.kws2 + d0;
-        const uint16_t* vp = p.vw + b * p.vws0 + (int64_t)j * p.vws1 + (int64_t)g * p.vws2 + d0;
-        float part = 0.f;
+        for (int k = 0; k < kPre; ++k) {
+            if (j0 + k > i) break;
+            float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) part = fmaf(qv[e], bf16_bits_to_f32(kp[e]), part);
+            for (int e = 0; e < DPT; ++e) part = fmaf(qv[e], kr[k][e], part);
+            part = sum32(part);
+            float vj[DPT];
 #pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 32);
-        const float sj = part * p.scale_log2;
-        const float Mn = fmaxf(M, sj);
-        const float r0 = __builtin_amdgcn_exp2f(M - Mn), rj = __builtin_amdgcn_exp2f(sj - Mn);
-        den = den * r0 + rj;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) num[e] = num[e] * r0 + bf16_bits_to_f32(vp[e]) * rj;
-        M = Mn;
+            for (int e = 0; e < DPT; ++e) vj[e] = vr[k][e];
+            merge(part * p.scale_log2, 1.f, vj);
+        }
     }
     const float inv = 1.f / den;
     uint16_t* op = p.o + b * p.os0 + (int64_t)i * p.os1 + (int64_t)h * p.os2 + d0;
@@ -445,7 +481,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     p.scale_log2 = a.scale * kLog2e;
     if (a.batch == 0) return hipSuccess;
     if (p.nchunk > 0) {
-        dim3 grid(p.nchunk, a.hkv, a.batch);
+        dim3 grid((unsigned)(a.batch * a.hkv), (unsigned)p.nchunk);
         const bool two = p.R > 32;
         if (a.d == 128) {
             if (two) hipLaunchKernelGGL((decode_split_kernel<128, 2>), grid, dim3(64), 0, s, p);

@@ -202,6 +202,8 @@ static int check_decode_desc(const mars_decode_desc* d) {
     if (d->head_dim != 64 && d->head_dim != 128) return MARS_EUNSUPPORTED;
     if ((int64_t)(d->n_q_heads / d->n_kv_heads) * d->window > 64) return MARS_EUNSUPPORTED;
     if (d->batch > 65535 || d->n_kv_heads > 65535) return MARS_EUNSUPPORTED;
+    if ((int64_t)d->batch * d->n_kv_heads > INT32_MAX) return MARS_EUNSUPPORTED;
+    if (d->cache_capacity > mars::kDecodeMaxCapacity) return MARS_EUNSUPPORTED;
     return MARS_OK;
 }
 

@@ -76,6 +76,24 @@ __device__ inline float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Lane value from another lane of the same row of 16 by a DPP pattern (VALU, no LDS).
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 32 lanes, result in every lane of the group: quad swaps
+// (DPP quad_perm [1,0,3,2] and [2,3,0,1]), half-row and row mirrors (DPP), then the two
+// rows of 16 exchanged with v_permlane16_swap.
+__device__ inline float sum32(float x) {
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0x141>(x);
+    x += dpp_f32<0x140>(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------------------
 // K/V tiles in LDS: rows of D bf16 (2D bytes, no padding), 16-byte chunks XOR-swizzled by
 // row so that the MFMA operand reads are free of bank conflicts:

@@ -45,6 +45,10 @@ struct DecodeArgs {
     int batch, hq, hkv, d, W, cap;
     float scale;
 };
+// Decode split: keys per cache chunk (one workgroup each) and the largest cache capacity
+// whose chunk count fits the grid's y dimension.
+constexpr int kDecodeChunk = 512;
+constexpr int64_t kDecodeMaxCapacity = int64_t(65535) * kDecodeChunk;
 size_t decode_workspace_bytes(int batch, int hkv, int G, int W, int d, int cap);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 

@@ -117,6 +117,8 @@ def test_decode_validation_errors():
     assert need > 0
     assert call(good(), ws=None) == L.MARS_EWORKSPACE
     assert call(good(), ws_bytes=need - 1) == L.MARS_EWORKSPACE
+    d = good(); d.cache_capacity = 65535 * 512 + 1        # chunk count beyond the grid's y limit
+    assert call(d) == L.MARS_EUNSUPPORTED
     d = good(); d.kc_strides[2] = (1 << 25) + 8           # 32 positions overflow 32-bit offsets
     assert call(d) == L.MARS_EUNSUPPORTED
     d = good(); d.batch = 0
