@@ -291,6 +291,53 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
     issue(tile_of(0), S0{});
     if (ntiles > 1) issue(tile_of(1), S1{});
 
+    // Tile classes from the wave's row range.  The wave's valid rows are consecutive
+    // positions p_lo..p_hi, so the union U and the intersection I of their visible key
+    // sets are each at most two intervals:
+    //   U = [0, U_hi) u [C0, p_hi]      (C0 = lo2 of the first noisy row; empty if none)
+    //   I = [0, I_hi) u [I2lo, I2hi)    (the second part only when every row is noisy and
+    //                                    in one block: its causal own-block prefix)
+    // A tile is visited iff it meets U, and needs no element mask iff it lies inside I.
+    int U_hi = 0, C0 = 0, Cend = 0, I_hi = 0, I2lo = 1, I2hi = 0;
+    if (wave_has_rows) {
+        const int u_hi = min(wrow0 + kRowsPerWave, p.rows_per_pair) - 1;
+        const int p_lo = wrow0 / p.G, p_hi = u_hi / p.G;
+        I_hi = 0x7fffffff;
+        if (p_lo < PL) {
+            U_hi = min(p_hi, PL - 1) + 1;
+            I_hi = p_lo + 1;
+        }
+        if (p_hi >= PL) {
+            const int n_lo = max(p_lo, PL);
+            const int klo = (n_lo - PL) / p.B, khi = (p_hi - PL) / p.B;
+            U_hi = max(U_hi, p.P + khi * p.B);
+            I_hi = min(I_hi, p.P + klo * p.B);
+            C0 = PL + klo * p.B;
+            Cend = p_hi + 1;
+            if (p_lo >= PL && klo == khi) {
+                I2lo = C0;
+                I2hi = n_lo + 1;
+            }
+        }
+    }
+    // Class code of tile `it` (bit 0: visit, bit 1: no mask needed).
+    auto tile_class = [&](const int it) __attribute__((always_inline)) {
+        const int kb = tile_of(it) * kKT;
+        const int ke = kb + kKT;
+        const bool any = (kb < U_hi) || (kb < Cend && ke > C0);
+        const bool all = (ke <= p.N) && (ke <= I_hi || (kb >= I2lo && ke <= I2hi));
+        return (any ? 1 : 0) | (all ? 2 : 0);
+    };
+    // The codes of tiles lane + 64 j (j < 16) are precomputed, two bits each, in one
+    // register per lane; the loop reads them back with v_readlane (tiles beyond 1024 are
+    // classified on the spot).
+    uint32_t cls_bits = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int it = lane + 64 * j;
+        if (it < ntiles) cls_bits |= (uint32_t)tile_class(it) << (2 * j);
+    }
+
     auto body = [&](const int it, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
         // Tile `it` is this wave's oldest copy group in flight; once every wave has it, the
@@ -302,18 +349,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
 
         const int kt = tile_of(it);
         const int kb = kt * kKT;
-        const int ke = min(kb + kKT, p.N);
-        bool lany = false, lall = true;
-#pragma unroll
-        for (int cb = 0; cb < kNcb; ++cb) {
-            if (valid[cb]) {
-                lany |= range_any(pos[cb], kb, ke, rb[cb]);
-                lall &= range_all(pos[cb], kb, ke, rb[cb]);
-            }
-        }
-        // Wave-uniform tile class (ballots are scalar, so the branches below are real branches).
-        const bool wany = __builtin_amdgcn_ballot_w64(lany) != 0ull;
-        const bool wall = (kb + kKT <= p.N) && __builtin_amdgcn_ballot_w64(!lall) == 0ull;
+        const int cls = it < 1024 ? (int)(__builtin_amdgcn_readlane(cls_bits, it & 63) >> (2 * (it >> 6))) & 3
+                                  : __builtin_amdgcn_readfirstlane(tile_class(it));
+        const bool wany = cls & 1, wall = cls & 2;
         if (logrow && lane == 0 && wany) logrow[kt] = wall ? 2 : 1;
         if (!wany) return;
 
