@@ -158,27 +158,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
         rb[cb] = row_bounds(pos[cb], p.P, p.L, p.B);
     }
 
-    // Q^T operand: lane holds Q[row][16c + 8*g2 .. +7] for every chunk c, multiplied by
-    // scale*log2(e) and rounded to bf16 once, so the MFMA yields scores in the log2 domain.
-    const float c = p.scale_log2;
-    bf16x8_t qf[kNcb][NC];
+    // Q^T operand: lane holds Q[row][16c + 8*g2 .. +7] for every chunk c.  The raw rows are
+    // loaded here (padding rows read the clamped last row) and converted below, after the
+    // first K/V copies are issued, so the two latencies overlap.
+    typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+    u32x4_t qraw[kNcb][NC];
 #pragma unroll
     for (int cb = 0; cb < kNcb; ++cb) {
         const uint16_t* qp = p.q + b * p.qs0 + (int64_t)pos[cb] * p.qs1 + (int64_t)head[cb] * p.qs2 + 8 * g2;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-            typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (valid[cb]) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * cc);
-            u32x4_t ws;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ws[j] = pack_bf16x2(__uint_as_float(w[j] << 16) * c, __uint_as_float(w[j] & 0xffff0000u) * c);
-            qf[cb][cc] = __builtin_bit_cast(bf16x8_t, ws);
-        }
+        for (int cc = 0; cc < NC; ++cc) qraw[cb][cc] = *reinterpret_cast<const u32x4_t*>(qp + 16 * cc);
     }
-    // The copies below are invisible to the compiler's wait tracking: finish Q first.
-    wait_vmcnt<0>();
 
     // Union of the workgroup's visible keys: [0, endA) and [startC, endC).
     const int u_last = min(row0 + kRowsPerWG, p.rows_per_pair) - 1;
@@ -290,6 +280,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
 
     issue(tile_of(0), S0{});
     if (ntiles > 1) issue(tile_of(1), S1{});
+    // Drain Q (and the first copies) before Q is used: the compiler does not count the
+    // copies, so a Q wait left to it would land inside the loop as a full vmcnt(0).  The
+    // scheduling barrier keeps the conversion below the copies.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    // Q multiplied by scale*log2(e) and rounded to bf16 once, so the MFMA yields scores in
+    // the log2 domain (padding rows are zero).
+    const float c = p.scale_log2;
+    bf16x8_t qf[kNcb][NC];
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) {
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            u32x4_t ws;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = valid[cb] ? qraw[cb][cc][j] : 0u;
+                ws[j] = pack_bf16x2(__uint_as_float(w << 16) * c, __uint_as_float(w & 0xffff0000u) * c);
+            }
+            qf[cb][cc] = __builtin_bit_cast(bf16x8_t, ws);
+        }
+    }
 
     // Tile classes from the wave's row range.  The wave's valid rows are consecutive
     // positions p_lo..p_hi, so the union U and the intersection I of their visible key
