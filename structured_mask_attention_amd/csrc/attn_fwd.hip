@@ -46,6 +46,7 @@ constexpr int kWaves = 4;
 constexpr int kNcb = 1;                              // 32-row column blocks per wave
 constexpr int kRowsPerWave = 32 * kNcb;              // == kAttnRowBlock
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;    // 128
+constexpr int kThreads = 64 * kWaves;               // workgroup size
 constexpr int kKT = kAttnKeyBlock;                   // 32 keys per LDS tile
 static_assert(kRowsPerWave == kAttnRowBlock, "row block");
 
@@ -119,7 +120,7 @@ __device__ inline uint16_t* att_v() {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
     constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
     constexpr int NDB = D / 32;         // 32-row d blocks of O^T
     constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
@@ -256,23 +257,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
     if (p.tilelog && wave_has_rows)
         logrow = p.tilelog + ((int64_t)bg * p.row_groups + wrow0 / kRowsPerWave) * p.key_tiles;
 
-    // Per-lane LDS byte offsets of the MFMA operands (the same for every stage).
-    int koff[NC];
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) koff[cc] = hl * (2 * D) + 16 * ((2 * cc + g2) ^ swz_k<D>(hl));
+    // Per-lane LDS byte offsets of the MFMA operands (the same for every stage).  The
+    // swizzle only permutes 16-byte chunks within a row, so chunk pair cc of K sits at
+    // koff0 ^ (32 cc) and the V^T fragment of d block db at voff0 ^ (64 db); the key half
+    // (kh) and 8-row half (hf) of a V fragment are plain additive offsets.
+    const int koff0 = hl * (2 * D) + 16 * (g2 ^ swz_k<D>(hl));
     const int s16 = lane & 15, grp = lane >> 4;
-    int voff[NDB][2][2];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int row = 16 * kh + 8 * hf + 4 * (grp >> 1) + (s16 >> 2);
-                const int col = 32 * db + 16 * (grp & 1) + 4 * (s16 & 3);
-                voff[db][kh][hf] = row * (2 * D) + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
-            }
-        }
+    int voff0;
+    {
+        const int row = 4 * (grp >> 1) + (s16 >> 2);
+        const int col = 16 * (grp & 1) + 4 * (s16 & 3);
+        voff0 = row * (2 * D) + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
     }
 
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -344,8 +339,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
     // register per lane; the loop reads them back with v_readlane (tiles beyond 1024 are
     // classified on the spot).
     uint32_t cls_bits = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 16 && 64 * j < ntiles; ++j) {
         const int it = lane + 64 * j;
         if (it < ntiles) cls_bits |= (uint32_t)tile_class(it) << (2 * j);
     }
@@ -374,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
         f32x16_t s[kNcb];
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt_lds + koff[cc]);
+            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt_lds + (koff0 ^ (32 * cc)));
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb)
                 s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], cc == 0 ? negm[cb] : s[cb], 0, 0, 0);
@@ -384,13 +378,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
         if (!wall) {
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb) {
-                const int base = kb + 4 * g2;
-                const int A = rb[cb].hi1 - base, Lo = rb[cb].lo2 - base, Hi = pos[cb] - base;
+                // Bit o of vis: key kb + o is visible to this lane's row (o < 32).
+                const int A = rb[cb].hi1 - kb, Lo = rb[cb].lo2 - kb, Hi = pos[cb] - kb;
+                auto low = [](int x) __attribute__((always_inline)) {
+                    return x >= 32 ? 0xffffffffu : (1u << max(x, 0)) - 1u;
+                };
+                const uint32_t vis = (low(A) | (low(Hi + 1) & ~low(Lo))) >> (4 * g2);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int o = 8 * (e >> 2) + (e & 3);
-                    const bool vis = (o < A) | ((o >= Lo) & (o <= Hi));
-                    s[cb][e] = vis ? s[cb][e] : -INFINITY;
+                    const uint32_t t = (uint32_t)((int32_t)(vis << (31 - o)) >> 31);  // all ones iff visible
+                    s[cb][e] = __uint_as_float((__float_as_uint(s[cb][e]) & t) | (0xff800000u & ~t));
                 }
             }
         }
@@ -408,6 +406,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
             need |= mx[cb] > thr[cb];
         }
         if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+            // acc is still all zero while every row of the wave has m_run = -inf.
+            bool started = false;
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) started |= m_run[cb] != -INFINITY;
+            started = __builtin_amdgcn_ballot_w64(started) != 0ull;
 #pragma unroll
             for (int cb = 0; cb < kNcb; ++cb) {
                 // Offset currently applied to s: m_run, or 0 while m_run = -inf.
@@ -416,10 +419,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
                 if (mnew > m_run[cb]) {
                     const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
                     l_run[cb] *= alpha;
+                    if (started) {
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
+                        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                            for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                        }
                     }
                     const float delta = mnew - off;
 #pragma unroll
@@ -460,10 +465,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
         // O^T += V^T P^T.
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
+            const char* vb = vt_lds + (voff0 ^ (64 * db));
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vt_lds + voff[db][kh][0]));
-                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vt_lds + voff[db][kh][1]));
+                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vb + kh * 16 * (2 * D)));
+                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vb + kh * 16 * (2 * D) + 8 * (2 * D)));
                 const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int cb = 0; cb < kNcb; ++cb)
@@ -596,9 +602,9 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
     const int64_t grid = (int64_t)p.tiles_per_pair * p.bg_count;
     if (grid == 0) return hipSuccess;
     if (a.d == 128) {
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     } else {
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     }
     return hipGetLastError();
 }
