@@ -119,7 +119,7 @@ __device__ inline uint16_t* att_v() {
     }
 }
 
-template <int D>
+template <int D, bool LOG>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
     constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
     constexpr int NDB = D / 32;         // 32-row d blocks of O^T
@@ -205,12 +205,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams 
         kgo[jj] = (uint32_t)(r * p.ks1 * 2 + 16 * (ps ^ swz_k<D>(r)));
         vgo[jj] = (uint32_t)(r * p.vs1 * 2 + 16 * (ps ^ swz_v<D>(r)));
     }
-    auto issue = [&](int kt, auto stage) __attribute__((always_inline)) {
+    // Copies are issued in walk order; kq / vq point at the first key row of the next tile
+    // to copy (tile tile_of(nq)) and advance by one tile, or jump to the second interval.
+    const int64_t tbk = (int64_t)kKT * p.ks1, tbv = (int64_t)kKT * p.vs1;
+    const int nfull = p.N / kKT;        // tiles entirely inside [0, N)
+    int nq = 0;
+    const uint16_t* kq = kbase;
+    const uint16_t* vq = vbase;
+    if (nA == 0) {
+        kq = kbase + c0t * tbk;
+        vq = vbase + c0t * tbv;
+    }
+    auto issue = [&](auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
+        const int kt = tile_of(nq);
         const int k0 = kt * kKT;
-        const uint16_t* kb = kbase + (int64_t)k0 * p.ks1;
-        const uint16_t* vb = vbase + (int64_t)k0 * p.vs1;
-        if (k0 + kKT <= p.N) {
+        const uint16_t* kb = kq;
+        const uint16_t* vb = vq;
+        ++nq;
+        if (nq == nA) {
+            kq = kbase + c0t * tbk;
+            vq = vbase + c0t * tbv;
+        } else {
+            kq += tbk;
+            vq += tbv;
+        }
+        if (kt < nfull) {
 #pragma unroll
             for (int jj = 0; jj < PERW; ++jj) {
                 const uint32_t w = lds_addr(att_k<D, ST>()) + 1024 * (wave * PERW + jj);
@@ -254,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams 
 
     const bool wave_has_rows = wrow0 < p.rows_per_pair;
     int8_t* logrow = nullptr;
-    if (p.tilelog && wave_has_rows)
+    if (LOG && wave_has_rows)
         logrow = p.tilelog + ((int64_t)bg * p.row_groups + wrow0 / kRowsPerWave) * p.key_tiles;
 
     // Per-lane LDS byte offsets of the MFMA operands (the same for every stage).  The
@@ -273,8 +293,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams 
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
     const bf16x2v ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-    issue(tile_of(0), S0{});
-    if (ntiles > 1) issue(tile_of(1), S1{});
+    issue(S0{});
+    if (ntiles > 1) issue(S1{});
     // Drain Q (and the first copies) before Q is used: the compiler does not count the
     // copies, so a Q wait left to it would land inside the loop as a full vmcnt(0).  The
     // scheduling barrier keeps the conversion below the copies.
@@ -351,14 +371,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams 
         if (it + 1 < ntiles) wait_vmcnt<GROUPW>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (it + 2 < ntiles) issue(tile_of(it + 2), std::integral_constant<int, (ST + 2) % kStages>{});
+        if (it + 2 < ntiles) issue(std::integral_constant<int, (ST + 2) % kStages>{});
 
         const int kt = tile_of(it);
         const int kb = kt * kKT;
         const int cls = it < 1024 ? (int)(__builtin_amdgcn_readlane(cls_bits, it & 63) >> (2 * (it >> 6))) & 3
                                   : __builtin_amdgcn_readfirstlane(tile_class(it));
         const bool wany = cls & 1, wall = cls & 2;
-        if (logrow && lane == 0 && wany) logrow[kt] = wall ? 2 : 1;
+        if constexpr (LOG) {
+            if (logrow && lane == 0 && wany) logrow[kt] = wall ? 2 : 1;
+        }
         if (!wany) return;
 
         const char* kt_lds = reinterpret_cast<const char*>(att_k<D, ST>());
@@ -601,10 +623,13 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
     p.scale_log2 = a.scale * kLog2e;
     const int64_t grid = (int64_t)p.tiles_per_pair * p.bg_count;
     if (grid == 0) return hipSuccess;
+    const dim3 g((unsigned)grid), blk(kThreads);
     if (a.d == 128) {
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+        if (p.tilelog) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), g, blk, 0, s, p);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), g, blk, 0, s, p);
     } else {
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+        if (p.tilelog) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), g, blk, 0, s, p);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), g, blk, 0, s, p);
     }
     return hipGetLastError();
 }
