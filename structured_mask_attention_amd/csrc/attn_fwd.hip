@@ -120,7 +120,7 @@ __device__ inline uint16_t* att_v() {
 }
 
 template <int D, bool LOG>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kernel(AttnKParams p) {
     constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
     constexpr int NDB = D / 32;         // 32-row d blocks of O^T
     constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
@@ -386,104 +386,135 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(AttnKParams 
         const char* kt_lds = reinterpret_cast<const char*>(att_k<D, ST>());
         const char* vt_lds = reinterpret_cast<const char*>(att_v<D, ST>());
 
-        // S^T = K Q^T - m_run (log2 domain) for this wave's column blocks.
+        // S^T = K Q^T - m_run (log2 domain) for this wave's column blocks, then the element
+        // mask on tiles that are not entirely visible.  Element e of this lane holds key
+        // kb + 4*g2 + o(e), o(e) = 8*(e/4) + e%4.
         f32x16_t s[kNcb];
+        auto scores = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt_lds + (koff0 ^ (32 * cc)));
+            for (int cc = 0; cc < NC; ++cc) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt_lds + (koff0 ^ (32 * cc)));
 #pragma unroll
-            for (int cb = 0; cb < kNcb; ++cb)
-                s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], cc == 0 ? negm[cb] : s[cb], 0, 0, 0);
-        }
-        // Element mask on tiles that are not entirely visible.  Element e of this lane holds
-        // key kb + 4*g2 + o(e), o(e) = 8*(e/4) + e%4.
-        if (!wall) {
-#pragma unroll
-            for (int cb = 0; cb < kNcb; ++cb) {
-                // Bit o of vis: key kb + o is visible to this lane's row (o < 32).
-                const int A = rb[cb].hi1 - kb, Lo = rb[cb].lo2 - kb, Hi = pos[cb] - kb;
-                auto low = [](int x) __attribute__((always_inline)) {
-                    return x >= 32 ? 0xffffffffu : (1u << max(x, 0)) - 1u;
-                };
-                const uint32_t vis = (low(A) | (low(Hi + 1) & ~low(Lo))) >> (4 * g2);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int o = 8 * (e >> 2) + (e & 3);
-                    const uint32_t t = (uint32_t)((int32_t)(vis << (31 - o)) >> 31);  // all ones iff visible
-                    s[cb][e] = __uint_as_float((__float_as_uint(s[cb][e]) & t) | (0xff800000u & ~t));
-                }
+                for (int cb = 0; cb < kNcb; ++cb)
+                    s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], cc == 0 ? negm[cb] : s[cb], 0, 0, 0);
             }
-        }
-        // Row max of the shifted scores (this lane's 16 keys, then the partner half); lazy
-        // rescale when some row's max exceeds thr.
-        float mx[kNcb];
-        bool need = false;
+            if (!wall) {
 #pragma unroll
-        for (int cb = 0; cb < kNcb; ++cb) {
-            float m = fmaxf(fmaxf(fmaxf(s[cb][0], s[cb][1]), fmaxf(s[cb][2], s[cb][3])),
-                            fmaxf(fmaxf(s[cb][4], s[cb][5]), fmaxf(s[cb][6], s[cb][7])));
-            m = fmaxf(m, fmaxf(fmaxf(fmaxf(s[cb][8], s[cb][9]), fmaxf(s[cb][10], s[cb][11])),
-                               fmaxf(fmaxf(s[cb][12], s[cb][13]), fmaxf(s[cb][14], s[cb][15]))));
-            mx[cb] = half_swap_max(m);
-            need |= mx[cb] > thr[cb];
-        }
-        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-            // acc is still all zero while every row of the wave has m_run = -inf.
-            bool started = false;
+                for (int cb = 0; cb < kNcb; ++cb) {
+                    // Bit o of vis: key kb + o is visible to this lane's row (o < 32).
+                    const int A = rb[cb].hi1 - kb, Lo = rb[cb].lo2 - kb, Hi = pos[cb] - kb;
+                    auto low = [](int x) __attribute__((always_inline)) {
+                        return x >= 32 ? 0xffffffffu : (1u << max(x, 0)) - 1u;
+                    };
+                    const uint32_t vis = (low(A) | (low(Hi + 1) & ~low(Lo))) >> (4 * g2);
 #pragma unroll
-            for (int cb = 0; cb < kNcb; ++cb) started |= m_run[cb] != -INFINITY;
-            started = __builtin_amdgcn_ballot_w64(started) != 0ull;
-#pragma unroll
-            for (int cb = 0; cb < kNcb; ++cb) {
-                // Offset currently applied to s: m_run, or 0 while m_run = -inf.
-                const float off = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
-                const float mnew = fmaxf(m_run[cb], off + mx[cb]);
-                if (mnew > m_run[cb]) {
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
-                    l_run[cb] *= alpha;
-                    if (started) {
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                            for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
-                        }
+                    for (int e = 0; e < 16; ++e) {
+                        const int o = 8 * (e >> 2) + (e & 3);
+                        const uint32_t t = (uint32_t)((int32_t)(vis << (31 - o)) >> 31);  // all ones iff visible
+                        s[cb][e] = __uint_as_float((__float_as_uint(s[cb][e]) & t) | (0xff800000u & ~t));
                     }
-                    const float delta = mnew - off;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) s[cb][e] -= delta;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) negm[cb][e] = -mnew;
-                    m_run[cb] = mnew;
-                    thr[cb] = kLazy;
                 }
             }
-        }
-        // P = 2^s in bf16; l += sum of the rounded P (dot2 with ones).
-        bf16x8_t pb[kNcb][2];
+        };
+        scores();
+        // Lazy rescale.  The row max is computed while some row of the wave has no finite
+        // running max yet (its first visible keys), or when this tile's P could overflow:
+        // P = 2^s is formed first and its row sum checked against 2^64, which bounds every
+        // term of acc and l far from the fp32 limit.  Otherwise scores above the running
+        // max just give P > 1, which bf16 and the fp32 accumulators hold exactly as well.
+        auto rescale = [&]() __attribute__((always_inline)) {
+            float mx[kNcb];
+            bool need = false;
 #pragma unroll
-        for (int cb = 0; cb < kNcb; ++cb) {
-            float pv[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(s[cb][e]);
-            float lsum = l_run[cb];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                // Scalar temporaries: element reads of a partially built vector in this
-                // unrolled loop were miscompiled (every dot2 read element 0).
-                const uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
-                const uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
-                const uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
-                const uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w0), ones2, lsum, false);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w1), ones2, lsum, false);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w2), ones2, lsum, false);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w3), ones2, lsum, false);
-                typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
-                const u32x4_t w = {w0, w1, w2, w3};
-                pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
+            for (int cb = 0; cb < kNcb; ++cb) {
+                float m = fmaxf(fmaxf(fmaxf(s[cb][0], s[cb][1]), fmaxf(s[cb][2], s[cb][3])),
+                                fmaxf(fmaxf(s[cb][4], s[cb][5]), fmaxf(s[cb][6], s[cb][7])));
+                m = fmaxf(m, fmaxf(fmaxf(fmaxf(s[cb][8], s[cb][9]), fmaxf(s[cb][10], s[cb][11])),
+                                   fmaxf(fmaxf(s[cb][12], s[cb][13]), fmaxf(s[cb][14], s[cb][15]))));
+                mx[cb] = half_swap_max(m);
+                need |= mx[cb] > thr[cb];
             }
-            l_run[cb] = lsum;
+            if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+                // acc is still all zero while every row of the wave has m_run = -inf.
+                bool started = false;
+#pragma unroll
+                for (int cb = 0; cb < kNcb; ++cb) started |= m_run[cb] != -INFINITY;
+                started = __builtin_amdgcn_ballot_w64(started) != 0ull;
+#pragma unroll
+                for (int cb = 0; cb < kNcb; ++cb) {
+                    // Offset currently applied to s: m_run, or 0 while m_run = -inf.
+                    const float off = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+                    const float mnew = fmaxf(m_run[cb], off + mx[cb]);
+                    if (mnew > m_run[cb]) {
+                        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
+                        l_run[cb] *= alpha;
+                        if (started) {
+#pragma unroll
+                            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                                for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                            }
+                        }
+                        const float delta = mnew - off;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) s[cb][e] -= delta;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) negm[cb][e] = -mnew;
+                        m_run[cb] = mnew;
+                        thr[cb] = kLazy;
+                    }
+                }
+            }
+        };
+        bf16x8_t pb[kNcb][2];
+        float lt[kNcb];
+        // P = 2^s in bf16 and its row sum (of the rounded P, dot2 with ones).
+        auto make_p = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) {
+                float pv[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) pv[e] = __builtin_amdgcn_exp2f(s[cb][e]);
+                float lsum = 0.f;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    // Scalar temporaries: element reads of a partially built vector in this
+                    // unrolled loop were miscompiled (every dot2 read element 0).
+                    const uint32_t w0 = pack_bf16x2(pv[8 * kh + 0], pv[8 * kh + 1]);
+                    const uint32_t w1 = pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]);
+                    const uint32_t w2 = pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]);
+                    const uint32_t w3 = pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7]);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w0), ones2, lsum, false);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w1), ones2, lsum, false);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w2), ones2, lsum, false);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w3), ones2, lsum, false);
+                    typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+                    const u32x4_t w = {w0, w1, w2, w3};
+                    pb[cb][kh] = __builtin_bit_cast(bf16x8_t, w);
+                }
+                lt[cb] = lsum;
+            }
+        };
+        bool fresh = false;
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) fresh |= m_run[cb] == -INFINITY;
+        fresh = __builtin_amdgcn_ballot_w64(fresh) != 0ull;
+        if (fresh) rescale();
+        make_p();
+        if (!fresh) {
+            bool big = false;
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) big |= !(lt[cb] <= 0x1p64f);
+            if (__builtin_amdgcn_ballot_w64(big) != 0ull) {
+                // Rare: the scores are formed again (the tile is still in LDS) rather than
+                // kept alive next to P.
+                scores();
+                rescale();
+                make_p();
+            }
         }
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) l_run[cb] += lt[cb];
         // O^T += V^T P^T.
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {

@@ -16,7 +16,8 @@ def lse_bound(q, k, scale=None):
 
     Two roundings enter the kernel's log-sum-exp beyond fp32 accumulation:
       * every probability term is rounded to bf16 before it is summed, which moves log l
-        by at most u = 2^-9 (relative rounding of bf16, round to nearest);
+        by at most u = 2^-8 (the unit roundoff of bf16: an 8-bit significand, so
+        round-to-nearest changes a value by at most 2^-8 of itself);
       * Q is multiplied by scale*log2(e) and rounded to bf16 once, which moves score j of
         row r by at most u * c * sum_i |q_ri| |k_ji| (log2 units; c = scale*log2(e)), and
         log-sum-exp moves by at most the largest score change.  The max is taken over
@@ -27,7 +28,7 @@ def lse_bound(q, k, scale=None):
     b, N, hq, d = qa.shape
     G = hq // ka.shape[2]
     c = (1.0 / np.sqrt(d) if scale is None else scale) * np.log2(np.e)
-    u = 2.0 ** -9
+    u = 2.0 ** -8
     out = np.empty((b, hq, N))
     for bi in range(b):
         for h in range(hq):

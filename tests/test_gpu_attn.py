@@ -151,3 +151,31 @@ def test_empty_inputs_are_noops():
     q2 = torch.zeros((1, 0, 2, 64), dtype=torch.bfloat16, device=dev())
     M.mars_attn_fwd(q2, q2[:, :, :1], q2[:, :, :1], 0, 0, 2)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d,low", [(64, 1000.0), (128, 1000.0), (64, 200.0), (128, 200.0)])
+def test_bf16_running_max_moves_late(d, low):
+    """Keys 0..31 (the first key tile of every row) score far below all later keys: every
+    q has component 0 equal to 1 and those keys have component 0 equal to -low.  A row's
+    running max then comes from tile 0 and the later tiles' P exceed it by up to ~2^180
+    (low = 1000: the kernel must move the max in a later tile) or ~2^40 (low = 200: P > 1
+    without a rescale).  The dominant scores stay moderate, so the single bf16 rounding of
+    Q*scale keeps its usual small effect; checked against the fp64 oracle on every output."""
+    b, hq, hkv, P, L, B = 1, 7, 1, 24, 72, 4
+    print(f"case running max d={d} low={low}", flush=True)
+    q, k, v = I.small_train_inputs(b, hq, hkv, d, P, L, seed=777 + d, dtype="bf16", in_scale=0.5)
+    N = P + 2 * L
+    qf, kf = q.float(), k.float()
+    qf[..., 0] = 1.0
+    kf[..., 0] = 0.0
+    kf[:, :32, :, 0] = -low
+    q, k = qf.to(torch.bfloat16), kf.to(torch.bfloat16)
+    lse_t = torch.empty((b, hq, N), dtype=torch.float32, device=dev())
+    out = M.mars_attn_fwd(q.to(dev()), k.to(dev()), v.to(dev()), P, L, B, lse=lse_t)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.attn(to_np64(q), to_np64(k), to_np64(v), P, L, B)
+    check_close(to_np64(out), ref, f"O running max d{d} low{low}")
+    err = np.abs(lse_t.cpu().numpy().astype(np.float64) - ref_lse)
+    bound = lse_bound(q, k)
+    print(f"  lse max_abs={err.max():.3e} max_abs/bound={np.max(err / bound):.3f}", flush=True)
+    assert np.all(err <= bound)
