@@ -64,7 +64,8 @@ struct AttnKParams {
     int tN0;             // first row tile whose first row is a noisy position
     int bg_count;        // batch * hkv
     int key_tiles;       // ceil(N / 32)
-    int row_groups;      // ceil(rows_per_pair / 64)
+    int row_groups;      // ceil(rows_per_pair / 32)
+    int lead;            // lightest items dispatched first
     float scale_log2;    // scale * log2(e)
 };
 
@@ -138,8 +139,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane & 31, g2 = lane >> 5;
 
-    const int bg = blockIdx.x % p.bg_count;
-    const int rank = blockIdx.x / p.bg_count;
+    // Work item in heaviest-first order ((batch, kv head) fastest); the first p.lead
+    // workgroups take the lightest items instead (see the launcher).
+    const int nitems = p.tiles_per_pair * p.bg_count;
+    const int gi = (int)blockIdx.x < p.lead ? nitems - p.lead + (int)blockIdx.x : (int)blockIdx.x - p.lead;
+    const int bg = gi % p.bg_count;
+    const int rank = gi / p.bg_count;
     const int tile = rank_to_tile(rank, p.tiles_per_pair, p.tN0);
     const int b = bg / p.hkv, g = bg % p.hkv;
     const int row0 = tile * kRowsPerWG;
@@ -417,6 +422,24 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
             }
         };
         scores();
+        // V^T fragments of this tile.  With head_dim 128 they are read now (into the
+        // registers the K fragments just released) so that their LDS latency overlaps the
+        // softmax below; with head_dim 64 the registers are needed to keep 4 waves per SIMD,
+        // and they are read after the softmax.
+        bf16x8_t va[NDB][2];
+        auto read_v = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const char* vb = vt_lds + (voff0 ^ (64 * db));
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vb + kh * 16 * (2 * D)));
+                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vb + kh * 16 * (2 * D) + 8 * (2 * D)));
+                va[db][kh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+        };
+        if constexpr (D == 128) read_v();
         // Lazy rescale.  The row max is computed while some row of the wave has no finite
         // running max yet (its first visible keys), or when this tile's P could overflow:
         // P = 2^s is formed first and its row sum checked against 2^64, which bounds every
@@ -516,17 +539,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
 #pragma unroll
         for (int cb = 0; cb < kNcb; ++cb) l_run[cb] += lt[cb];
         // O^T += V^T P^T.
+        if constexpr (D != 128) read_v();
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const char* vb = vt_lds + (voff0 ^ (64 * db));
+        for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vb + kh * 16 * (2 * D)));
-                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(vb + kh * 16 * (2 * D) + 8 * (2 * D)));
-                const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                 for (int cb = 0; cb < kNcb; ++cb)
-                    acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cb][kh], acc[cb][db], 0, 0, 0);
+                    acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kh], pb[cb][kh], acc[cb][db], 0, 0, 0);
             }
         }
     };
@@ -654,6 +674,27 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
     p.scale_log2 = a.scale * kLog2e;
     const int64_t grid = (int64_t)p.tiles_per_pair * p.bg_count;
     if (grid == 0) return hipSuccess;
+    // When the grid is a little larger than what is resident at once, the items that do not
+    // fit would start only when a first-round workgroup ends (late: the oldest waves have
+    // issue priority).  Those lightest items are dispatched first instead; they finish
+    // early and their slots take the rest.
+    static int slot_cache[2][64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int di = a.d == 128 ? 1 : 0;
+    int slots = (dev >= 0 && dev < 64) ? slot_cache[di][dev] : 0;
+    if (slots <= 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = a.d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<128, false>, kThreads, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<64, false>, kThreads, 0);
+        if (e != hipSuccess) return e;
+        slots = cus * (per_cu > 0 ? per_cu : 1);
+        if (dev >= 0 && dev < 64) slot_cache[di][dev] = slots;
+    }
+    p.lead = (grid > slots && grid < 2 * (int64_t)slots) ? (int)(grid - slots) : 0;
     const dim3 g((unsigned)grid), blk(kThreads);
     if (a.d == 128) {
         if (p.tilelog) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), g, blk, 0, s, p);
