@@ -20,10 +20,11 @@
 //     of its rows' visible keys, see mars_device.h); each wave classifies every tile for its
 //     own rows: skipped, computed with the element mask, or computed without it.
 //   * Online softmax in the log2 domain, fp32 statistics, fp32 MFMA accumulation.  Q is
-//     multiplied by scale*log2(e) and rounded to bf16 once per wave, and the first QK MFMA
-//     of a tile takes -m_run as its accumulator input, so scores arrive shifted and P = 2^s
-//     costs one v_exp_f32 per element.  O is rescaled lazily: only when a row max grows by
-//     more than 2^8 over the running one.
+//     multiplied by scale*log2(e) and rounded to bf16 once per wave, so P = 2^(s - off)
+//     costs one v_exp_f32 per element.  The per-row offset `off` stays 0 while a row's
+//     scores are moderate (|first max| <= 64, no tile whose P sum passes 2^64): the QK MFMA
+//     output is then exponentiated as it is, with no max and no subtraction.  Rows with
+//     larger scores move their offset to their max (and rescale O) only when needed.
 //   * Copy addresses: one wave-uniform base per tile (SGPRs) plus fixed per-lane offsets.
 //   * Workgroup order: heaviest row tiles first (noisy and clean tiles from the far end,
 //     interleaved, then the prompt); the (batch, kv head) index is the fastest-varying part
@@ -129,7 +130,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
     constexpr int PERW = NINS / kWaves;             // windows per wave and tensor
     constexpr int GROUPW = 2 * PERW;                // copy instructions per wave and tile
     static_assert(D <= 128 && NINS % kWaves == 0 && PERW >= 1, "tile copy split");
-    constexpr float kLazy = 8.f;
+    constexpr float kLazy = 32.f;   // shifted score that moves a started row's offset
+    constexpr float kMod = 64.f;    // first max within +-kMod: the row keeps offset 0
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
@@ -256,20 +258,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
         }
     };
 
-    // Online softmax state per row (log2 domain): m_run = running max (-inf before the first
-    // visible key), l_run = this lane's share of the sum, acc = O^T.  Scores leave the QK
-    // MFMA already shifted by -m_run (the accumulator input is negm = -m_run, or 0 while
-    // m_run = -inf), so P = 2^s needs no per-element subtraction.  thr is the largest
-    // shifted score that needs no rescale: kLazy once m_run is finite, -inf before.
-    float m_run[kNcb], l_run[kNcb], thr[kNcb];
-    f32x16_t acc[kNcb][NDB], negm[kNcb];
+    // Online softmax state per row (log2 domain): off = offset subtracted from the raw
+    // scores, l_run = this lane's share of sum 2^(s - off), acc = O^T on the same scale,
+    // m_run = -inf until the row's first visible key.  The offset stays 0 while a row's
+    // scores are moderate (first visible tile's max within +-kMod, no later tile pushing a
+    // P sum past 2^64): the QK MFMA output is then used as it is, and only a wave holding a
+    // shifted row (`shifted`) subtracts.  thr is the largest shifted score that keeps the
+    // offset: kLazy once the row has started, -inf before.
+    float m_run[kNcb], l_run[kNcb], thr[kNcb], off[kNcb];
+    bool shifted = false;
+    f32x16_t acc[kNcb][NDB];
 #pragma unroll
     for (int cb = 0; cb < kNcb; ++cb) {
         m_run[cb] = -INFINITY;
         l_run[cb] = 0.f;
         thr[cb] = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) negm[cb][e] = 0.f;
+        off[cb] = 0.f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -401,7 +405,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
                 const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt_lds + (koff0 ^ (32 * cc)));
 #pragma unroll
                 for (int cb = 0; cb < kNcb; ++cb)
-                    s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], cc == 0 ? negm[cb] : s[cb], 0, 0, 0);
+                    s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cb][cc], cc == 0 ? f32x16_t{} : s[cb], 0, 0, 0);
+            }
+            if (shifted) {
+#pragma unroll
+                for (int cb = 0; cb < kNcb; ++cb) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) s[cb][e] -= off[cb];
+                }
             }
             if (!wall) {
 #pragma unroll
@@ -422,10 +433,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
             }
         };
         scores();
-        // V^T fragments of this tile.  With head_dim 128 they are read now (into the
-        // registers the K fragments just released) so that their LDS latency overlaps the
-        // softmax below; with head_dim 64 the registers are needed to keep 4 waves per SIMD,
-        // and they are read after the softmax.
+        // V^T fragments of this tile, read now (into the registers the K fragments just
+        // released) so that their LDS latency overlaps the softmax below.
         bf16x8_t va[NDB][2];
         auto read_v = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
             }
         }
         };
-        if constexpr (D == 128) read_v();
+        read_v();
         // Lazy rescale.  The row max is computed while some row of the wave has no finite
         // running max yet (its first visible keys), or when this tile's P could overflow:
         // P = 2^s is formed first and its row sum checked against 2^64, which bounds every
@@ -463,13 +472,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
 #pragma unroll
                 for (int cb = 0; cb < kNcb; ++cb) started |= m_run[cb] != -INFINITY;
                 started = __builtin_amdgcn_ballot_w64(started) != 0ull;
+                bool any_off = false;
 #pragma unroll
                 for (int cb = 0; cb < kNcb; ++cb) {
-                    // Offset currently applied to s: m_run, or 0 while m_run = -inf.
-                    const float off = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
-                    const float mnew = fmaxf(m_run[cb], off + mx[cb]);
-                    if (mnew > m_run[cb]) {
-                        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - mnew);  // 0 when m_run = -inf
+                    if (mx[cb] > thr[cb]) {
+                        // New offset: the row's max raw score in this tile, or 0 for a row
+                        // starting with a moderate max.  A started row rescales its sums.
+                        const float mnew = off[cb] + mx[cb];
+                        const bool first = m_run[cb] == -INFINITY;
+                        const float noff = (first && fabsf(mnew) <= kMod) ? 0.f : mnew;
+                        const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(off[cb] - noff);
                         l_run[cb] *= alpha;
                         if (started) {
 #pragma unroll
@@ -478,15 +490,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
                                 for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
                             }
                         }
-                        const float delta = mnew - off;
+                        const float delta = noff - off[cb];
 #pragma unroll
                         for (int e = 0; e < 16; ++e) s[cb][e] -= delta;
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) negm[cb][e] = -mnew;
+                        off[cb] = noff;
                         m_run[cb] = mnew;
                         thr[cb] = kLazy;
                     }
+                    any_off |= off[cb] != 0.f;
                 }
+                shifted = __builtin_amdgcn_ballot_w64(any_off) != 0ull;
             }
         };
         bf16x8_t pb[kNcb][2];
@@ -539,7 +552,6 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
 #pragma unroll
         for (int cb = 0; cb < kNcb; ++cb) l_run[cb] += lt[cb];
         // O^T += V^T P^T.
-        if constexpr (D != 128) read_v();
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -576,7 +588,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
                 }
             }
             if (p.lse && g2 == 0)
-                p.lse[((int64_t)b * p.hq + head[cb]) * p.N + pos[cb]] = (m_run[cb] + log2f(lt)) * kLn2;
+                p.lse[((int64_t)b * p.hq + head[cb]) * p.N + pos[cb]] = (off[cb] + log2f(lt)) * kLn2;
         }
     }
 }

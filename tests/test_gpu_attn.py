@@ -179,3 +179,35 @@ def test_bf16_running_max_moves_late(d, low):
     bound = lse_bound(q, k)
     print(f"  lse max_abs={err.max():.3e} max_abs/bound={np.max(err / bound):.3f}", flush=True)
     assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("d,high,where", [(64, 600.0, "late"), (128, 600.0, "late"), (64, 600.0, "all"),
+                                          (128, 600.0, "all"), (64, -600.0, "all")])
+def test_bf16_large_scores(d, high, where):
+    """Scores far from 0 in the log2 domain: every q has component 0 equal to 1 and keys get
+    component 0 equal to `high` (scale*log2(e)*600 ~ 108).  "late": only keys 64..95, so rows
+    start with moderate scores and a later tile's P sum passes 2^64 (the row's offset must
+    move there); "all": every key, so rows start with a first max beyond +-64 (large
+    positive, or large negative for high < 0) and carry a nonzero offset from their first
+    tile.  Checked against the fp64 oracle on every output and on the LSE."""
+    b, hq, hkv, P, L, B = 1, 7, 1, 24, 72, 4
+    print(f"case large scores d={d} high={high} {where}", flush=True)
+    q, k, v = I.small_train_inputs(b, hq, hkv, d, P, L, seed=991 + d, dtype="bf16", in_scale=0.5)
+    N = P + 2 * L
+    qf, kf = q.float(), k.float()
+    qf[..., 0] = 1.0
+    kf[..., 0] = 0.0
+    if where == "late":
+        kf[:, 64:96, :, 0] = high
+    else:
+        kf[..., 0] = high
+    q, k = qf.to(torch.bfloat16), kf.to(torch.bfloat16)
+    lse_t = torch.empty((b, hq, N), dtype=torch.float32, device=dev())
+    out = M.mars_attn_fwd(q.to(dev()), k.to(dev()), v.to(dev()), P, L, B, lse=lse_t)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.attn(to_np64(q), to_np64(k), to_np64(v), P, L, B)
+    check_close(to_np64(out), ref, f"O large scores d{d} high{high} {where}")
+    err = np.abs(lse_t.cpu().numpy().astype(np.float64) - ref_lse)
+    bound = lse_bound(q, k)
+    print(f"  lse max_abs={err.max():.3e} max_abs/bound={np.max(err / bound):.3f}", flush=True)
+    assert np.all(err <= bound)
