@@ -47,6 +47,7 @@ __all__ = [
     "mask_nnz",
     "attn",
     "attn_scalar",
+    "attn_bwd",
     "tile_map",
     "tile_map_rules",
     "visible_tile_elems",
@@ -213,6 +214,76 @@ def attn(q, k, v, P, L, B, scale=None, rows=None, row_chunk=1024, mask_fn=mask_r
                 out[bi, c0:c0 + len(rr), h, :] = (p @ v[bi, :, g, :]) / den
                 lse[bi, h, c0:c0 + len(rr)] = m[:, 0] + np.log(den[:, 0])
     return out, lse
+
+
+def attn_bwd(q, k, v, do, P, L, B, scale=None, rows=None, keys=None, mask_fn=mask_rules):
+    """Gradients of :func:`attn` with respect to q, k and v for an upstream gradient dO.
+
+    Training needs the gradient of this exact forward ([MARS] §3.2-3.3: the loss of
+    Eq. 3/5 is taken through the Eq. 2 attention).  For one (batch, head), with
+    S = scale Q K^T + M, P = softmax(S) row-wise and O = P V, the chain rule through
+    the row softmax gives, in float64:
+
+        D_i  = sum_d dO_id O_id                      (= sum_j P_ij dP_ij)
+        dP   = dO V^T,   dS = P o (dP - D)           (masked entries: P = 0, dS = 0)
+        dQ   = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
+
+    and dK, dV of KV head g are summed over the query heads h with h // G = g.
+    ``rows`` restricts dQ to those query positions; ``keys`` restricts dK and dV to
+    those key positions (only the rows that see one of them are evaluated, each
+    with its full softmax).  Returns (dq [b, R, Hq, D], dk [b, K, Hkv, D],
+    dv [b, K, Hkv, D]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    b, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert N == P + 2 * L and k.shape == (b, N, Hkv, D) and v.shape == k.shape and do.shape == q.shape
+    G = _gqa_group(Hq, Hkv)
+    if scale is None or scale == 0:
+        scale = 1.0 / math.sqrt(D)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = np.arange(N) if keys is None else np.asarray(keys, dtype=np.int64)
+    dq = np.zeros((b, len(rows), Hq, D))
+    dk = np.zeros((b, len(keys), Hkv, D))
+    dv = np.zeros((b, len(keys), Hkv, D))
+
+    def probs(bi, h, rr):
+        """Row-normalised P and O for query rows rr of (bi, h)."""
+        g = h // G
+        vis = mask_fn(P, L, B, rr)
+        s = scale * (q[bi, rr, h, :] @ k[bi, :, g, :].T)
+        s = np.where(vis, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / e.sum(axis=1, keepdims=True)
+        return p, p @ v[bi, :, g, :]
+
+    # Query rows that see at least one requested key (the only rows with dS in those columns).
+    kr = np.unique(keys)
+    cols = np.zeros(N, dtype=bool)
+    cols[kr] = True
+    krows = np.array([i for i in range(N) if np.any(mask_fn(P, L, B, np.array([i]))[0] & cols)], dtype=np.int64)
+    for bi in range(b):
+        for h in range(Hq):
+            g = h // G
+            if len(rows):
+                p, o = probs(bi, h, rows)
+                dO = do[bi, rows, h, :]
+                Dv = np.sum(dO * o, axis=1, keepdims=True)
+                ds = p * (dO @ v[bi, :, g, :].T - Dv)
+                dq[bi, :, h, :] = scale * (ds @ k[bi, :, g, :])
+            if len(krows):
+                p, o = probs(bi, h, krows)
+                dO = do[bi, krows, h, :]
+                Dv = np.sum(dO * o, axis=1, keepdims=True)
+                pk = p[:, keys]
+                ds = pk * (dO @ v[bi, keys, g, :].T - Dv)
+                dk[bi, :, g, :] += scale * (ds.T @ q[bi, krows, h, :])
+                dv[bi, :, g, :] += pk.T @ dO
+    return dq, dk, dv
 
 
 def attn_scalar(q, k, v, vis, scale):

@@ -183,3 +183,113 @@ def test_closed_forms():
     c = np.full((1, N, 1, D), 0.375)
     out2, _ = O.attn(q, rand((1, N, 1, D), 31), c, P, L, B)
     assert np.max(np.abs(out2 - 0.375)) <= 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Backward (gradients of the forward)
+# ---------------------------------------------------------------------------
+
+def _fd_grads(q, k, v, w, P, L, B, eps=1e-6):
+    """Central differences of f = sum(O * w) with respect to every entry of q, k, v."""
+    def f():
+        return float(np.sum(O.attn(q, k, v, P, L, B)[0] * w))
+    out = []
+    for x in (q, k, v):
+        g = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            fp = f()
+            x[idx] = old - eps
+            fm = f()
+            x[idx] = old
+            g[idx] = (fp - fm) / (2 * eps)
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize("b,Hq,Hkv,D,P,L,B", [
+    (1, 2, 1, 4, 3, 5, 2),     # GQA, ragged last block
+    (2, 2, 2, 3, 0, 4, 4),     # no prompt, one block
+    (1, 3, 1, 2, 2, 3, 1),     # B = 1
+    (1, 1, 1, 3, 4, 2, 5),     # B > L
+])
+def test_attn_bwd_matches_finite_differences(b, Hq, Hkv, D, P, L, B):
+    """The analytic gradients equal central differences of the forward (a scalar loss
+    sum(O * W) with random W = dO), to the truncation error of the differences."""
+    N = P + 2 * L
+    q, k, v = rand((b, N, Hq, D), 1), rand((b, N, Hkv, D), 2), rand((b, N, Hkv, D), 3)
+    w = rand((b, N, Hq, D), 4)
+    dq, dk, dv = O.attn_bwd(q, k, v, w, P, L, B)
+    fq, fk, fv = _fd_grads(q, k, v, w, P, L, B)
+    for name, a, n in (("dq", dq, fq), ("dk", dk, fk), ("dv", dv, fv)):
+        assert np.max(np.abs(a - n)) < 1e-7 * max(1.0, np.max(np.abs(n))), name
+
+
+def test_attn_bwd_matches_torch_autograd():
+    """torch float64 autograd through SDPA with the same explicit mask (library cross-check,
+    GQA by repeating K/V, whose gradients are then summed back per KV head)."""
+    b, Hq, Hkv, D, P, L, B = 2, 6, 2, 16, 7, 21, 4
+    N = P + 2 * L
+    q, k, v, do = rand((b, N, Hq, D), 11), rand((b, N, Hkv, D), 12), rand((b, N, Hkv, D), 13), rand((b, N, Hq, D), 14)
+    dq, dk, dv = O.attn_bwd(q, k, v, do, P, L, B)
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    ke = kt.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    ve = vt.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    vis = torch.from_numpy(O.mask_rules(P, L, B).astype(bool))
+    o = F.scaled_dot_product_attention(qt, ke, ve, attn_mask=vis, scale=1.0 / math.sqrt(D))
+    o.backward(torch.from_numpy(do).permute(0, 2, 1, 3))
+    assert np.max(np.abs(qt.grad.permute(0, 2, 1, 3).numpy() - dq)) < 1e-12
+    assert np.max(np.abs(kt.grad.numpy() - dk)) < 1e-12
+    assert np.max(np.abs(vt.grad.numpy() - dv)) < 1e-12
+
+
+def test_attn_bwd_constant_v_closed_form():
+    """Every key carries the same value vector c: O = c whatever P is, so dQ = dK = 0 and
+    dV_j = sum_i P_ij dO_i (the column sums of P weight dO)."""
+    b, Hq, Hkv, D, P, L, B = 1, 2, 1, 5, 4, 6, 3
+    N = P + 2 * L
+    q, k, do = rand((b, N, Hq, D), 21), rand((b, N, Hkv, D), 22), rand((b, N, Hq, D), 23)
+    v = np.broadcast_to(rand((1, 1, 1, D), 24), (b, N, Hkv, D)).copy()
+    dq, dk, dv = O.attn_bwd(q, k, v, do, P, L, B)
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+    vis = O.mask_rules(P, L, B)
+    want = np.zeros((N, D))
+    for h in range(Hq):
+        s = (q[0, :, h] @ k[0, :, 0].T) / math.sqrt(D)
+        s = np.where(vis, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        want += p.T @ do[0, :, h]
+    assert np.max(np.abs(dv[0, :, 0] - want)) < 1e-12
+
+
+def test_attn_bwd_clean_rows_equal_causal_gradient():
+    """With dO zero on the noisy stream, only clean and prompt rows carry gradient, and the
+    gradients with respect to [prompt; x] equal those of plain causal attention over
+    [prompt; x] (the noisy stream only reads clean keys, it never feeds them)."""
+    b, Hq, Hkv, D, P, L, B = 1, 2, 1, 6, 5, 9, 3
+    N, PL = P + 2 * L, P + L
+    q, k, v, do = rand((b, N, Hq, D), 31), rand((b, N, Hkv, D), 32), rand((b, N, Hkv, D), 33), rand((b, N, Hq, D), 34)
+    do[:, PL:] = 0.0
+    dq, dk, dv = O.attn_bwd(q, k, v, do, P, L, B)
+    causal = lambda P_, L_, B_, rr=None: np.tril(np.ones((PL, PL), dtype=bool))[rr if rr is not None else slice(None)]
+    cq, ck, cv = O.attn_bwd(q[:, :PL], k[:, :PL], v[:, :PL], do[:, :PL], PL, 0, 1, mask_fn=causal)
+    assert np.max(np.abs(dq[:, :PL] - cq)) < 1e-12
+    assert np.max(np.abs(dk[:, :PL] - ck)) < 1e-12 and np.max(np.abs(dv[:, :PL] - cv)) < 1e-12
+    assert np.max(np.abs(dq[:, PL:])) == 0.0 and np.max(np.abs(dk[:, PL:])) == 0.0
+
+
+def test_attn_bwd_row_and_key_subsets():
+    """Restricting dQ to some rows and dK/dV to some keys returns exactly those slices."""
+    b, Hq, Hkv, D, P, L, B = 2, 4, 2, 8, 6, 10, 4
+    N = P + 2 * L
+    q, k, v, do = rand((b, N, Hq, D), 41), rand((b, N, Hkv, D), 42), rand((b, N, Hkv, D), 43), rand((b, N, Hq, D), 44)
+    dq, dk, dv = O.attn_bwd(q, k, v, do, P, L, B)
+    rows, keys = np.array([0, 5, 7, 17, 25]), np.array([1, 6, 16, 20, 25])
+    sq, sk, sv = O.attn_bwd(q, k, v, do, P, L, B, rows=rows, keys=keys)
+    assert np.max(np.abs(sq - dq[:, rows])) < 1e-13
+    assert np.max(np.abs(sk - dk[:, keys])) < 1e-13 and np.max(np.abs(sv - dv[:, keys])) < 1e-13
