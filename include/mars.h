@@ -5,6 +5,8 @@
  * (arXiv 2604.07023):
  *   - mars_attn_fwd:    one forward of attention over [prompt ; x ; x~] with the
  *                       structured mask M of §3.2, Eq. 2 (training layout);
+ *   - mars_attn_bwd:    its gradients dQ, dK, dV (training needs them for the losses of
+ *                       §3.2-3.3, Eq. 3 and Eq. 5);
  *   - mars_decode_step: the sliding-window inference step of Fig. 2 (right): B appended
  *                       window rows attend to a per-sequence KV cache and, causally, to
  *                       the window itself;
@@ -145,6 +147,44 @@ int mars_attn_tilelog_geometry(const mars_attn_desc* desc, int32_t* row_block,
 int mars_attn_fwd_tilelog(const mars_attn_desc* desc, const void* q, const void* k,
                           const void* v, void* o, float* lse, int8_t* tile_log,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Training backward: dQ, dK, dV of mars_attn_fwd (bf16 only).
+ *
+ * Training takes the losses of MARS §3.2-3.3 (Eq. 3, Eq. 5) through the Eq. 2 attention,
+ * so it needs the gradients of that forward.  For one (batch, query head), with P the
+ * forward's row probabilities (from the saved LSE), D_i = sum_d dO_id O_id and the chain
+ * rule through the row softmax:
+ *   dV = P^T dO,   dS = P o (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q;
+ * dK and dV of KV head g sum the contributions of its query heads h (g = h / G).
+ * Rows and keys outside the mask contribute nothing; skipped tiles are never computed.
+ * ------------------------------------------------------------------------------------ */
+typedef struct mars_attn_bwd_strides {
+    int64_t do_strides[3]; /* d_o [batch][N][n_q_heads][head_dim]: batch, position, head */
+    int64_t dq_strides[3]; /* dq  [batch][N][n_q_heads][head_dim] */
+    int64_t dk_strides[3]; /* dk  [batch][N][n_kv_heads][head_dim] */
+    int64_t dv_strides[3]; /* dv  [batch][N][n_kv_heads][head_dim] */
+} mars_attn_bwd_strides;
+
+/* Workspace bytes of mars_attn_bwd for desc (bf16 only; MARS_EUNSUPPORTED for fp32). */
+int mars_attn_bwd_workspace_bytes(const mars_attn_desc* desc, size_t* bytes);
+
+/*
+ * desc: the forward's descriptor (q/k/v/o strides); dtype must be MARS_DTYPE_BF16.
+ * gs:   strides of d_o, dq, dk, dv (same alignment rules as q/k/v/o).
+ * q, k, v: the forward's inputs; o and lse: the forward's outputs (lse fp32
+ *   [batch][n_q_heads][N], contiguous, as mars_attn_fwd writes it); d_o: dL/dO (bf16).
+ * dq, dk, dv: outputs (bf16, rounded to nearest even), fully overwritten; they must not
+ *   alias any input or each other.
+ * ws: device workspace of at least mars_attn_bwd_workspace_bytes, 16-byte aligned; no
+ *   initialisation needed (it holds Q * scale * log2(e) in bf16 and two fp32 scalars per
+ *   row); MARS_EWORKSPACE if null or too small.
+ * Errors as mars_attn_fwd; key position strides (k, v) <= 2^25 elements and the d_o
+ *   position stride <= 2^25 elements, else MARS_EUNSUPPORTED.
+ */
+int mars_attn_bwd(const mars_attn_desc* desc, const mars_attn_bwd_strides* gs, const void* q,
+                  const void* k, const void* v, const void* o, const float* lse, const void* d_o,
+                  void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Sliding-window decode step (MARS Fig. 2, right).

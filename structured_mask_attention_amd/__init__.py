@@ -22,6 +22,8 @@ __all__ = [
     "mars_tile_map",
     "mars_attn_tilelog_geometry",
     "mars_attn_fwd_tilelog",
+    "mars_attn_bwd_workspace_bytes",
+    "mars_attn_bwd",
     "mars_decode_workspace_bytes",
     "mars_decode_step",
     "mars_accept_workspace_bytes",
@@ -115,6 +117,44 @@ def mars_attn_fwd(q, k, v, prompt_len, resp_len, block, scale=0.0, out=None, lse
     _check(L.load().mars_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                   _stream(q)), "mars_attn_fwd")
     return out
+
+
+def mars_attn_bwd_workspace_bytes(batch, hq, hkv, d, P, Lr, B, dtype=torch.bfloat16):
+    """Workspace bytes of :func:`mars_attn_bwd` (see mars.h)."""
+    desc = attn_desc(batch, hq, hkv, d, P, Lr, B, dtype)
+    n = ctypes.c_size_t()
+    _check(L.load().mars_attn_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "mars_attn_bwd_workspace_bytes")
+    return n.value
+
+
+def mars_attn_bwd(q, k, v, o, lse, dout, prompt_len, resp_len, block, scale=0.0, dq=None, dk=None, dv=None,
+                  ws=None):
+    """Gradients (dq, dk, dv) of mars_attn_fwd for the upstream gradient ``dout``.
+
+    q/k/v: the forward's inputs; o, lse: its outputs (lse fp32 [b, Hq, N]); dout like o.
+    ``ws``: optional uint8 device tensor of at least mars_attn_bwd_workspace_bytes.
+    """
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    desc = _attn_desc_from(q, k, v, o, prompt_len, resp_len, block, scale)
+    for name, t, ref in (("dout", dout, o), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of its forward tensor")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or \
+            lse.shape != (q.shape[0], q.shape[2], q.shape[1]):
+        raise ValueError("lse must be a contiguous fp32 [b, Hq, N] tensor")
+    gs = L.AttnBwdStrides()
+    gs.do_strides, gs.dq_strides, gs.dk_strides, gs.dv_strides = _s3(dout), _s3(dq), _s3(dk), _s3(dv)
+    n = ctypes.c_size_t()
+    _check(L.load().mars_attn_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "mars_attn_bwd_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device)
+    _check(L.load().mars_attn_bwd(ctypes.byref(desc), ctypes.byref(gs), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                  _stream(q)), "mars_attn_bwd")
+    return dq, dk, dv
 
 
 def mars_attn_work(batch, hq, hkv, d, P, Lr, B, bm=128, bn=128, dtype=torch.bfloat16):

@@ -28,6 +28,10 @@ class AttnDesc(ctypes.Structure):
     ]
 
 
+class AttnBwdStrides(ctypes.Structure):
+    _fields_ = [("do_strides", I64x3), ("dq_strides", I64x3), ("dk_strides", I64x3), ("dv_strides", I64x3)]
+
+
 class DecodeDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
@@ -58,6 +62,9 @@ _SIGNATURES = {
     "mars_attn_tilelog_geometry": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_int32),
                                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
     "mars_attn_fwd_tilelog": (ctypes.c_int, [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]),
+    "mars_attn_bwd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "mars_attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnBwdStrides), P, P, P, P, P, P,
+                                     P, P, P, P, ctypes.c_size_t, P]),
     "mars_decode_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "mars_accept_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), ctypes.POINTER(ctypes.c_size_t)]),

@@ -1,0 +1,777 @@
+// Training-layout backward of the MARS structured-mask attention: dQ, dK, dV of the
+// forward in attn_fwd.hip ("MARS: Enabling Autoregressive Models Multi-Token Generation",
+// §3.2 Eq. 2 and Fig. 2 left; training takes the losses of Eq. 3 and Eq. 5 through this
+// attention, so it needs these gradients).
+//
+// With P the forward's row probabilities, D_i = sum_d dO_id O_id, and in the log2 domain
+// of the forward (scores s = c q.k, c = scale*log2(e); P = 2^(s - LSE*log2(e))):
+//   dV = P^T dO,   dS = P o (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q,
+// dK and dV of a KV head summed over its G query heads.  Three kernels, no atomics:
+//   1. prep (per row): Qc = bf16(Q*c) exactly as the forward rounds it, -D and
+//      -LSE*log2(e), into the workspace, positions padded to a multiple of 32 (zeros);
+//   2. dK/dV (key-stationary): a workgroup owns 128 keys of one (batch, kv head), 32 per
+//      wave with K and V fragments in registers, and walks the (32-position, head) tiles
+//      of every row that sees one of its keys (a union of at most three position
+//      intervals).  Qc and dO tiles plus the two per-row scalars stream through a 3-stage
+//      LDS ring (global_load_lds_dwordx4, XOR-swizzled chunks).  Per tile and wave:
+//      S = Qc K^T and dP = dO V^T (MFMA accumulators start at -LSE2 and -D), P = 2^S,
+//      dS = P dP, then dV^T += dO^T P and dK^T += Qc^T dS with the transposed operands read
+//      by ds_read_b64_tr_b16.  The element mask is a per-key bitmask over the tile's 32
+//      positions.
+//   3. dQ (row-stationary): the forward's row packing, tile walk, tile classes and K/V
+//      ring; per tile S^T = K Qc^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+// P and dS enter the MFMAs as bf16 (round to nearest even); statistics and accumulation
+// are fp32; gradients are stored as bf16.
+#include <cmath>
+#include <type_traits>
+
+#include "mars_device.h"
+#include "mars_internal.h"
+
+namespace mars {
+
+namespace {
+
+constexpr int kWavesB = 4;
+constexpr int kThreadsB = 64 * kWavesB;
+constexpr int kT = 32;               // keys per dQ tile; positions per dK/dV tile; rows or keys per wave
+constexpr int kStagesB = 3;
+constexpr int kKeysPerWG = kWavesB * kT;   // dK/dV: 128 keys per workgroup
+constexpr int kRowsPerWGB = kWavesB * kT;  // dQ: 128 packed rows per workgroup
+
+// ---------------------------------------------------------------------------------------
+// LDS rings.  One file-scope object per stage, array and head_dim.
+//   dK/dV: Qc tile, dO tile ([32 positions][D] bf16 each) and the scalars of the tile's
+//          rows ([-LSE2 x 32][-D x 32] fp32).
+//   dQ:    K tile and V tile ([32 keys][D] bf16 each).
+// ---------------------------------------------------------------------------------------
+#define MARS_BRING(NAME, ELEMS)                                                         \
+    __shared__ __attribute__((aligned(16))) uint16_t NAME##0[ELEMS];                    \
+    __shared__ __attribute__((aligned(16))) uint16_t NAME##1[ELEMS];                    \
+    __shared__ __attribute__((aligned(16))) uint16_t NAME##2[ELEMS];
+MARS_BRING(g_bq128_, kT * 128)
+MARS_BRING(g_bo128_, kT * 128)
+MARS_BRING(g_bq64_, kT * 64)
+MARS_BRING(g_bo64_, kT * 64)
+MARS_BRING(g_bs128_, 128)        // 256 bytes of fp32 scalars per stage
+MARS_BRING(g_bs64_, 128)
+MARS_BRING(g_dk128_, kT * 128)
+MARS_BRING(g_dv128_, kT * 128)
+MARS_BRING(g_dk64_, kT * 64)
+MARS_BRING(g_dv64_, kT * 64)
+#undef MARS_BRING
+
+#define MARS_SEL(FN, N128, N64)                                                          \
+    template <int D, int ST>                                                             \
+    __device__ inline uint16_t* FN() {                                                   \
+        static_assert(ST >= 0 && ST < kStagesB, "stage");                                \
+        if constexpr (D == 128) {                                                        \
+            if constexpr (ST == 0) return N128##0;                                       \
+            else if constexpr (ST == 1) return N128##1;                                  \
+            else return N128##2;                                                         \
+        } else {                                                                         \
+            if constexpr (ST == 0) return N64##0;                                        \
+            else if constexpr (ST == 1) return N64##1;                                   \
+            else return N64##2;                                                          \
+        }                                                                                \
+    }
+MARS_SEL(ring_q, g_bq128_, g_bq64_)
+MARS_SEL(ring_o, g_bo128_, g_bo64_)
+MARS_SEL(ring_s, g_bs128_, g_bs64_)
+MARS_SEL(ring_k, g_dk128_, g_dk64_)
+MARS_SEL(ring_v, g_dv128_, g_dv64_)
+#undef MARS_SEL
+
+typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Element e of an MFMA 32x32 accumulator sits at row (or key) 4*g2 + o(e) of the tile.
+__device__ constexpr int acc_off(int e) { return 8 * (e >> 2) + (e & 3); }
+
+// The 16 accumulator elements as two bf16x8 B operands (k = the accumulator's row index,
+// in the order acc_off gives; the A operands are read to match).
+__device__ inline void pack_b(const f32x16_t& x, bf16x8_t out[2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+        u32x4_t w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[8 * kh + 2 * i], x[8 * kh + 2 * i + 1]);
+        out[kh] = __builtin_bit_cast(bf16x8_t, w);
+    }
+}
+
+// Element mask of a tile: vis bit o (o < 32) says whether tile row (or key) o is visible;
+// elements of this lane (rows/keys 4*g2 + acc_off(e)) outside it become -inf.
+__device__ inline void apply_mask(f32x16_t& s, uint32_t vis, int g2) {
+    const uint32_t v = vis >> (4 * g2);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int o = acc_off(e);
+        const uint32_t t = (uint32_t)((int32_t)(v << (31 - o)) >> 31);
+        s[e] = __uint_as_float((__float_as_uint(s[e]) & t) | (0xff800000u & ~t));
+    }
+}
+
+// Bits [a - base, b - base) of a 32-bit mask (clipped to [0, 32)).
+__device__ inline uint32_t span_bits(int a, int b, int base) {
+    auto low = [](int x) { return x >= 32 ? 0xffffffffu : (1u << (x > 0 ? x : 0)) - 1u; };
+    return low(b - base) & ~low(a - base);
+}
+
+// A operand (rows of a [32][D] tile, lane = row hl, 8 columns per lane) and transposed A
+// operand (ds_read_b64_tr_b16: 16 tile rows x 32 columns per instruction pair) offsets.
+template <int D>
+__device__ inline int row_read_off(int hl, int g2, int swz) {
+    return hl * (2 * D) + 16 * (g2 ^ swz);
+}
+template <int D>
+__device__ inline int tr_read_off(int lane) {
+    const int s16 = lane & 15, grp = lane >> 4;
+    const int row = 4 * (grp >> 1) + (s16 >> 2);
+    const int col = 16 * (grp & 1) + 4 * (s16 & 3);
+    return row * (2 * D) + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
+}
+// Transposed fragment of column block db, 16-row chunk kh (rows in acc_off order).
+template <int D>
+__device__ inline bf16x8_t tr_frag(const char* tile, int off0, int db, int kh) {
+    const char* p = tile + (off0 ^ (64 * db)) + kh * 16 * (2 * D);
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)p);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(p + 8 * (2 * D)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------------------------------
+// 1. Row prologue.
+// ---------------------------------------------------------------------------------------
+struct PrepParams {
+    const uint16_t* q;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    uint16_t* qc;
+    float* nlse;
+    float* ndelta;
+    int64_t qs0, qs1, qs2, os0, os1, os2, ds0, ds1, ds2;
+    int batch, hq, N, Npad;
+    float c;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(PrepParams p) {
+    constexpr int TPR = D / 8;   // lanes per (batch, position, head) row, 8 elements each
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = t / TPR;
+    const int c8 = (int)(t % TPR);
+    const int64_t rows = (int64_t)p.batch * p.Npad * p.hq;
+    if (row >= rows) return;   // whole TPR-lane groups leave together
+    const int h = (int)(row % p.hq);
+    const int64_t bp = row / p.hq;
+    const int pos = (int)(bp % p.Npad);
+    const int b = (int)(bp / p.Npad);
+    u32x4_t qc4 = {0u, 0u, 0u, 0u};
+    float dot = 0.f;
+    if (pos < p.N) {
+        const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(p.q + b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)h * p.qs2 + 8 * c8);
+        const u32x4_t ow = *reinterpret_cast<const u32x4_t*>(p.o + b * p.os0 + (int64_t)pos * p.os1 + (int64_t)h * p.os2 + 8 * c8);
+        const u32x4_t dw = *reinterpret_cast<const u32x4_t*>(p.dout + b * p.ds0 + (int64_t)pos * p.ds1 + (int64_t)h * p.ds2 + 8 * c8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // Same rounding as the forward's Q operand: fp32 product, then bf16 RNE.
+            qc4[i] = pack_bf16x2(__uint_as_float(qw[i] << 16) * p.c, __uint_as_float(qw[i] & 0xffff0000u) * p.c);
+            dot = fmaf(__uint_as_float(ow[i] << 16), __uint_as_float(dw[i] << 16), dot);
+            dot = fmaf(__uint_as_float(ow[i] & 0xffff0000u), __uint_as_float(dw[i] & 0xffff0000u), dot);
+        }
+    }
+    *reinterpret_cast<u32x4_t*>(p.qc + ((int64_t)(b * (int64_t)p.Npad + pos) * p.hq + h) * D + 8 * c8) = qc4;
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+    if (c8 == 0) {
+        const int64_t idx = ((int64_t)b * p.hq + h) * p.Npad + pos;
+        p.nlse[idx] = pos < p.N ? -p.lse[((int64_t)b * p.hq + h) * p.N + pos] * kLog2e : 0.f;
+        p.ndelta[idx] = pos < p.N ? -dot : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// 2. dK / dV.
+// ---------------------------------------------------------------------------------------
+struct DkvParams {
+    const uint16_t* qc;      // workspace [batch][Npad][hq][D]
+    const uint16_t* dout;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* nlse;       // workspace [batch][hq][Npad]
+    const float* ndelta;
+    uint16_t* dk;
+    uint16_t* dv;
+    int64_t ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
+    int hq, hkv, G, P, L, B, N, Npad;
+    int bg_count;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p) {
+    constexpr int NC = D / 16;                    // 16-wide d chunks of the S / dP contractions
+    constexpr int NDB = D / 32;                   // 32-row d blocks of dK^T / dV^T
+    constexpr int CPR = D / 8;                    // 16-byte chunks per tile row
+    constexpr int PERW = kT * CPR / 64 / kWavesB; // 1 KB copy windows per wave and tile array
+    constexpr int GROUPW = 2 * PERW + 1;          // copy instructions per wave and step
+    static_assert(PERW >= 1 && (kT * CPR / 64) % kWavesB == 0, "tile copy split");
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane & 31, g2 = lane >> 5;
+    const int bg = blockIdx.x % p.bg_count;
+    const int kblk = blockIdx.x / p.bg_count;
+    const int b = bg / p.hkv, g = bg % p.hkv;
+    const int PL = p.P + p.L;
+    const int kb0 = kblk * kKeysPerWG;
+    const int kb1 = min(kb0 + kKeysPerWG, p.N);
+
+    // This lane's key and its K / V rows as B operands (k = d: 8 values per lane per chunk).
+    const int j = kb0 + wave * kT + hl;
+    const bool kvalid = j < p.N;
+    const int jj = kvalid ? j : p.N - 1;
+    bf16x8_t kf[NC], vf[NC];
+    {
+        const uint16_t* kp = p.k + b * p.ks0 + (int64_t)jj * p.ks1 + (int64_t)g * p.ks2 + 8 * g2;
+        const uint16_t* vp = p.v + b * p.vs0 + (int64_t)jj * p.vs1 + (int64_t)g * p.vs2 + 8 * g2;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            kf[cc] = *reinterpret_cast<const bf16x8_t*>(kp + 16 * cc);
+            vf[cc] = *reinterpret_cast<const bf16x8_t*>(vp + 16 * cc);
+        }
+    }
+    // Positions that see key j: [a1, b1) u [a2, b2).  A prompt or clean key is seen by the
+    // later prompt/clean rows and by the noisy rows of the blocks after its own (every
+    // block, for a prompt key); a noisy key by the later rows of its own block.
+    int a1 = 0, b1 = 0, a2 = 0, b2 = 0;
+    if (kvalid) {
+        if (j < PL) {
+            a1 = j;
+            b1 = PL;
+            a2 = min(PL + (j < p.P ? 0 : p.B * ((j - p.P) / p.B + 1)), p.N);
+            b2 = p.N;
+        } else {
+            a1 = j;
+            b1 = min(p.N, PL + ((j - PL) / p.B + 1) * p.B);
+        }
+    }
+
+    // Position tiles of the workgroup: union over its keys, as up to three ranges of
+    // 32-position tiles, sorted and merged.
+    int r0s = 0, r0e = 0, r1s = 0, r1e = 0, r2s = 0, r2e = 0;
+    {
+        int s[3], e[3], n = 0;
+        if (kb0 < PL) {
+            s[n] = kb0; e[n] = PL; ++n;
+            const int n0 = PL + (kb0 < p.P ? 0 : p.B * ((kb0 - p.P) / p.B + 1));
+            if (n0 < p.N) { s[n] = n0; e[n] = p.N; ++n; }
+        }
+        if (kb1 > PL) {
+            const int kl = (kb1 - 1 - PL) / p.B;
+            s[n] = max(kb0, PL); e[n] = min(p.N, PL + (kl + 1) * p.B); ++n;
+        }
+        // tile units, insertion sort by start, merge overlapping or adjacent ranges
+        for (int i = 0; i < n; ++i) { s[i] = s[i] / kT; e[i] = (e[i] + kT - 1) / kT; }
+        for (int i = 1; i < n; ++i)
+            for (int m = i; m > 0 && s[m] < s[m - 1]; --m) {
+                const int ts = s[m], te = e[m];
+                s[m] = s[m - 1]; e[m] = e[m - 1]; s[m - 1] = ts; e[m - 1] = te;
+            }
+        int ms[3], me[3], nm = 0;
+        for (int i = 0; i < n; ++i) {
+            if (nm > 0 && s[i] <= me[nm - 1]) me[nm - 1] = max(me[nm - 1], e[i]);
+            else { ms[nm] = s[i]; me[nm] = e[i]; ++nm; }
+        }
+        if (nm > 0) { r0s = ms[0]; r0e = me[0]; }
+        if (nm > 1) { r1s = ms[1]; r1e = me[1]; }
+        if (nm > 2) { r2s = ms[2]; r2e = me[2]; }
+    }
+    const int n0t = r0e - r0s, n1t = r1e - r1s, n2t = r2e - r2s;
+    const int nsteps = (n0t + n1t + n2t) * p.G;
+    auto pos_tile = [&](int ti) __attribute__((always_inline)) {
+        return ti < n0t ? r0s + ti : (ti < n0t + n1t ? r1s + (ti - n0t) : r2s + (ti - n0t - n1t));
+    };
+
+    // Copy of step `it` (position tile, head) into stage ST.  Window slot (row r,
+    // position ps) holds logical chunk ps ^ swz_v(r) of row r; dO rows past N repeat row
+    // N-1 (finite; such rows are always masked).  The scalar copy: wave w moves bytes
+    // [64w, 64w + 64) of [-LSE2 x 32][-D x 32] with four lanes.
+    const int64_t qc_row = (int64_t)p.hq * D;   // Qc position stride (elements)
+    uint32_t qgo[PERW], ogo[PERW];
+#pragma unroll
+    for (int w = 0; w < PERW; ++w) {
+        const int slot = 64 * (wave * PERW + w) + lane;
+        const int r = slot / CPR, ps = slot % CPR;
+        qgo[w] = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_v<D>(r)));
+        ogo[w] = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_v<D>(r)));
+    }
+    auto issue = [&](const int it, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        const int ti = it / p.G, hh = it - ti * p.G;
+        const int p0 = pos_tile(ti) * kT;
+        const int head = g * p.G + hh;
+        const uint16_t* qb = p.qc + ((int64_t)b * p.Npad + p0) * qc_row + (int64_t)head * D;
+        const uint16_t* ob = p.dout + b * p.ds0 + (int64_t)p0 * p.ds1 + (int64_t)head * p.ds2;
+        const bool full = p0 + kT <= p.N;
+#pragma unroll
+        for (int w = 0; w < PERW; ++w) {
+            const int jw = wave * PERW + w;
+            dma16_sv(qb, qgo[w], lds_addr(ring_q<D, ST>()) + 1024 * jw);
+            if (full) {
+                dma16_sv(ob, ogo[w], lds_addr(ring_o<D, ST>()) + 1024 * jw);
+            } else {
+                const int slot = 64 * jw + lane;
+                const int r = slot / CPR, ps = slot % CPR;
+                const int rr = min(r, p.N - 1 - p0);
+                dma16_sv(ob, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_v<D>(r))), lds_addr(ring_o<D, ST>()) + 1024 * jw);
+            }
+        }
+        const float* sb = (wave < 2 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + p0 + 16 * (wave & 1);
+        if (lane < 4) dma16_sv(sb, (uint32_t)(16 * lane), lds_addr(ring_s<D, ST>()) + 64 * wave);
+    };
+
+    f32x16_t dva[NDB], dka[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            dva[db][e] = 0.f;
+            dka[db][e] = 0.f;
+        }
+    }
+    const int roff = row_read_off<D>(hl, g2, swz_v<D>(hl));
+    const int troff = tr_read_off<D>(lane);
+
+    issue(0, S0{});
+    if (nsteps > 1) issue(1, S1{});
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+
+    uint32_t vis = 0;
+    bool any = false, all = false;
+    auto body = [&](const int it, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        if (it + 1 < nsteps) wait_vmcnt<GROUPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 2 < nsteps) issue(it + 2, std::integral_constant<int, (ST + 2) % kStagesB>{});
+
+        const int ti = it / p.G;
+        if (it - ti * p.G == 0) {
+            // New position tile: this lane's visibility bits and the wave's tile class.
+            const int p0 = pos_tile(ti) * kT;
+            vis = span_bits(a1, b1, p0) | span_bits(a2, b2, p0);
+            any = __builtin_amdgcn_ballot_w64(kvalid && vis != 0u) != 0ull;
+            all = __builtin_amdgcn_ballot_w64(kvalid && vis != 0xffffffffu) == 0ull;
+        }
+        if (!any) return;
+
+        const char* qt = reinterpret_cast<const char*>(ring_q<D, ST>());
+        const char* ot = reinterpret_cast<const char*>(ring_o<D, ST>());
+        const char* st = reinterpret_cast<const char*>(ring_s<D, ST>());
+        // S = Qc K^T - LSE2 and dP = dO V^T - D; element e is tile row 4*g2 + acc_off(e).
+        f32x16_t s, dp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(st + 4 * (4 * g2 + 8 * i));
+            const f32x4_t c = *reinterpret_cast<const f32x4_t*>(st + 128 + 4 * (4 * g2 + 8 * i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s[4 * i + e] = a[e];
+                dp[4 * i + e] = c[e];
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + (roff ^ (32 * cc)));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[cc], s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ot + (roff ^ (32 * cc)));
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[cc], dp, 0, 0, 0);
+        }
+        if (!all) apply_mask(s, vis, g2);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            s[e] = __builtin_amdgcn_exp2f(s[e]);   // P
+            dp[e] *= s[e];                          // dS
+        }
+        bf16x8_t pb[2], sb[2];
+        pack_b(s, pb);
+        pack_b(dp, sb);
+        // dV^T += dO^T P,  dK^T += Qc^T dS  (A operands: transposed tile reads).
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ot, troff, db, kh), pb[kh], dva[db], 0, 0, 0);
+                dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt, troff, db, kh), sb[kh], dka[db], 0, 0, 0);
+            }
+        }
+    };
+    for (int t0 = 0; t0 < nsteps; t0 += kStagesB) {
+        body(t0, S0{});
+        if (t0 + 1 < nsteps) body(t0 + 1, S1{});
+        if (t0 + 2 < nsteps) body(t0 + 2, S2{});
+    }
+
+    // dV = dV^T^T; dK = ln2 * dK^T^T (Qc carries scale*log2(e) where dK needs scale).
+    if (kvalid) {
+        uint16_t* vo = p.dv + b * p.dvs0 + (int64_t)j * p.dvs1 + (int64_t)g * p.dvs2;
+        uint16_t* ko = p.dk + b * p.dks0 + (int64_t)j * p.dks1 + (int64_t)g * p.dks2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int d = 32 * db + 8 * bb + 4 * g2;
+                uint2 wv, wk;
+                wv.x = pack_bf16x2(dva[db][4 * bb + 0], dva[db][4 * bb + 1]);
+                wv.y = pack_bf16x2(dva[db][4 * bb + 2], dva[db][4 * bb + 3]);
+                wk.x = pack_bf16x2(dka[db][4 * bb + 0] * kLn2, dka[db][4 * bb + 1] * kLn2);
+                wk.y = pack_bf16x2(dka[db][4 * bb + 2] * kLn2, dka[db][4 * bb + 3] * kLn2);
+                *reinterpret_cast<uint2*>(vo + d) = wv;
+                *reinterpret_cast<uint2*>(ko + d) = wk;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// 3. dQ.
+// ---------------------------------------------------------------------------------------
+struct DqParams {
+    const uint16_t* qc;
+    const uint16_t* dout;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* nlse;
+    const float* ndelta;
+    uint16_t* dq;
+    int64_t ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, qs0, qs1, qs2;
+    int hq, hkv, G, P, L, B, N, Npad;
+    int rows_per_pair, tiles_per_pair, tN0, bg_count;
+    float scale;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
+    constexpr int NC = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int CPR = D / 8;
+    constexpr int NINS = kT * CPR / 64;
+    constexpr int PERW = NINS / kWavesB;
+    constexpr int GROUPW = 2 * PERW;
+    static_assert(PERW >= 1 && NINS % kWavesB == 0, "tile copy split");
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane & 31, g2 = lane >> 5;
+    const int bg = blockIdx.x % p.bg_count;
+    const int rank = blockIdx.x / p.bg_count;
+    const int tile = rank_to_tile(rank, p.tiles_per_pair, p.tN0);
+    const int b = bg / p.hkv, g = bg % p.hkv;
+    const int row0 = tile * kRowsPerWGB;
+    const int wrow0 = row0 + wave * kT;
+
+    // This lane's packed row: position u / G, head g*G + u % G (as in the forward).
+    const int u = wrow0 + hl;
+    const bool valid = u < p.rows_per_pair;
+    const int uu = valid ? u : p.rows_per_pair - 1;
+    const int pos = uu / p.G;
+    const int head = g * p.G + uu % p.G;
+    const RowBounds rb = row_bounds(pos, p.P, p.L, p.B);
+    bf16x8_t qf[NC], of[NC];
+    {
+        const uint16_t* qp = p.qc + ((int64_t)b * p.Npad + pos) * ((int64_t)p.hq * D) + (int64_t)head * D + 8 * g2;
+        const uint16_t* op = p.dout + b * p.ds0 + (int64_t)pos * p.ds1 + (int64_t)head * p.ds2 + 8 * g2;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            qf[cc] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * cc);
+            of[cc] = *reinterpret_cast<const bf16x8_t*>(op + 16 * cc);
+        }
+    }
+    const int64_t sidx = ((int64_t)b * p.hq + head) * p.Npad + pos;
+    const float nl = p.nlse[sidx];
+    const float nd = p.ndelta[sidx];
+
+    // Key walk of the workgroup's rows: [0, endA) and [startC, endC) (forward's schedule).
+    const int u_last = min(row0 + kRowsPerWGB, p.rows_per_pair) - 1;
+    const int pf = row0 / p.G, pl = u_last / p.G;
+    const int PL = p.P + p.L;
+    int endA = 0, startC = 0, endC = 0;
+    if (pf < PL) endA = min(pl, PL - 1) + 1;
+    if (pl >= PL) {
+        endA = max(endA, p.P + ((pl - PL) / p.B) * p.B);
+        startC = PL + ((max(pf, PL) - PL) / p.B) * p.B;
+        endC = pl + 1;
+    }
+    const int nA = (endA + kT - 1) / kT;
+    int c0t = startC / kT;
+    const int c1t = (endC + kT - 1) / kT;
+    if (c0t < nA) c0t = nA;
+    const int nCt = c1t > c0t ? c1t - c0t : 0;
+    const int ntiles = nA + nCt;
+    auto tile_of = [&](int it) { return it < nA ? it : c0t + (it - nA); };
+
+    const uint16_t* kbase = p.k + b * p.ks0 + (int64_t)g * p.ks2;
+    const uint16_t* vbase = p.v + b * p.vs0 + (int64_t)g * p.vs2;
+    // K tile: row reads and transposed reads (swz_v); V tile: row reads only (swz_k).
+    uint32_t kgo[PERW], vgo[PERW];
+#pragma unroll
+    for (int w = 0; w < PERW; ++w) {
+        const int slot = 64 * (wave * PERW + w) + lane;
+        const int r = slot / CPR, ps = slot % CPR;
+        kgo[w] = (uint32_t)(r * p.ks1 * 2 + 16 * (ps ^ swz_v<D>(r)));
+        vgo[w] = (uint32_t)(r * p.vs1 * 2 + 16 * (ps ^ swz_k<D>(r)));
+    }
+    const int nfull = p.N / kT;
+    auto issue = [&](const int it, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        const int kt = tile_of(it);
+        const int k0 = kt * kT;
+        const uint16_t* kb = kbase + (int64_t)k0 * p.ks1;
+        const uint16_t* vb = vbase + (int64_t)k0 * p.vs1;
+#pragma unroll
+        for (int w = 0; w < PERW; ++w) {
+            const int jw = wave * PERW + w;
+            if (kt < nfull) {
+                dma16_sv(kb, kgo[w], lds_addr(ring_k<D, ST>()) + 1024 * jw);
+                dma16_sv(vb, vgo[w], lds_addr(ring_v<D, ST>()) + 1024 * jw);
+            } else {
+                const int slot = 64 * jw + lane;
+                const int r = slot / CPR, ps = slot % CPR;
+                const int rr = min(r, p.N - 1 - k0);
+                dma16_sv(kb, (uint32_t)(rr * p.ks1 * 2 + 16 * (ps ^ swz_v<D>(r))), lds_addr(ring_k<D, ST>()) + 1024 * jw);
+                dma16_sv(vb, (uint32_t)(rr * p.vs1 * 2 + 16 * (ps ^ swz_k<D>(r))), lds_addr(ring_v<D, ST>()) + 1024 * jw);
+            }
+        }
+    };
+
+    // Tile classes of the wave's rows (the forward's union / intersection intervals).
+    const bool wave_has_rows = wrow0 < p.rows_per_pair;
+    int U_hi = 0, C0 = 0, Cend = 0, I_hi = 0, I2lo = 1, I2hi = 0;
+    if (wave_has_rows) {
+        const int u_hi = min(wrow0 + kT, p.rows_per_pair) - 1;
+        const int p_lo = wrow0 / p.G, p_hi = u_hi / p.G;
+        I_hi = 0x7fffffff;
+        if (p_lo < PL) {
+            U_hi = min(p_hi, PL - 1) + 1;
+            I_hi = p_lo + 1;
+        }
+        if (p_hi >= PL) {
+            const int n_lo = max(p_lo, PL);
+            const int klo = (n_lo - PL) / p.B, khi = (p_hi - PL) / p.B;
+            U_hi = max(U_hi, p.P + khi * p.B);
+            I_hi = min(I_hi, p.P + klo * p.B);
+            C0 = PL + klo * p.B;
+            Cend = p_hi + 1;
+            if (p_lo >= PL && klo == khi) {
+                I2lo = C0;
+                I2hi = n_lo + 1;
+            }
+        }
+    }
+    auto tile_class = [&](const int it) __attribute__((always_inline)) {
+        const int kb = tile_of(it) * kT;
+        const int ke = kb + kT;
+        const bool any = (kb < U_hi) || (kb < Cend && ke > C0);
+        const bool all = (ke <= p.N) && (ke <= I_hi || (kb >= I2lo && ke <= I2hi));
+        return (any ? 1 : 0) | (all ? 2 : 0);
+    };
+
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
+    }
+    const int kroff = row_read_off<D>(hl, g2, swz_v<D>(hl));
+    const int vroff = row_read_off<D>(hl, g2, swz_k<D>(hl));
+    const int troff = tr_read_off<D>(lane);
+
+    issue(0, S0{});
+    if (ntiles > 1) issue(1, S1{});
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+
+    auto body = [&](const int it, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        if (it + 1 < ntiles) wait_vmcnt<GROUPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 2 < ntiles) issue(it + 2, std::integral_constant<int, (ST + 2) % kStagesB>{});
+        const int cls = __builtin_amdgcn_readfirstlane(tile_class(it));
+        if (!(cls & 1)) return;
+        const int kb = tile_of(it) * kT;
+        const char* kt_lds = reinterpret_cast<const char*>(ring_k<D, ST>());
+        const char* vt_lds = reinterpret_cast<const char*>(ring_v<D, ST>());
+        // S^T = K Qc^T - LSE2, dP^T = V dO^T - D; element e is key kb + 4*g2 + acc_off(e).
+        f32x16_t s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            s[e] = nl;
+            dp[e] = nd;
+        }
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kt_lds + (kroff ^ (32 * cc)));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vt_lds + (vroff ^ (32 * cc)));
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[cc], dp, 0, 0, 0);
+        }
+        if (!(cls & 2)) {
+            auto low = [](int x) { return x >= 32 ? 0xffffffffu : (1u << max(x, 0)) - 1u; };
+            const int A = rb.hi1 - kb, Lo = rb.lo2 - kb, Hi = pos - kb;
+            apply_mask(s, low(A) | (low(Hi + 1) & ~low(Lo)), g2);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dp[e] *= __builtin_amdgcn_exp2f(s[e]);   // dS = P (dP - D)
+        bf16x8_t sb[2];
+        pack_b(dp, sb);
+        // dQ^T += K^T dS^T.
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_lds, troff, db, kh), sb[kh], acc[db], 0, 0, 0);
+        }
+    };
+    for (int t0 = 0; t0 < ntiles; t0 += kStagesB) {
+        body(t0, S0{});
+        if (t0 + 1 < ntiles) body(t0 + 1, S1{});
+        if (t0 + 2 < ntiles) body(t0 + 2, S2{});
+    }
+
+    // dQ = scale * dQ^T^T (bf16).
+    if (valid) {
+        uint16_t* qo = p.dq + b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)head * p.qs2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int d = 32 * db + 8 * bb + 4 * g2;
+                uint2 w;
+                w.x = pack_bf16x2(acc[db][4 * bb + 0] * p.scale, acc[db][4 * bb + 1] * p.scale);
+                w.y = pack_bf16x2(acc[db][4 * bb + 2] * p.scale, acc[db][4 * bb + 3] * p.scale);
+                *reinterpret_cast<uint2*>(qo + d) = w;
+            }
+        }
+    }
+}
+
+int pad32(int n) { return (n + kT - 1) / kT * kT; }
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int batch, int hq, int N, int d) {
+    const size_t Np = (size_t)pad32(N);
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    return r256((size_t)batch * Np * hq * d * 2) + 2 * r256((size_t)batch * hq * Np * 4);
+}
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
+    const int Npad = pad32(a.N);
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* ws = static_cast<char*>(a.ws);
+    uint16_t* qc = reinterpret_cast<uint16_t*>(ws);
+    float* nlse = reinterpret_cast<float*>(ws + r256((size_t)a.batch * Npad * a.hq * a.d * 2));
+    float* ndelta = reinterpret_cast<float*>(reinterpret_cast<char*>(nlse) + r256((size_t)a.batch * a.hq * Npad * 4));
+    const int G = a.hq / a.hkv;
+    const float c = a.scale * kLog2e;
+
+    PrepParams pp;
+    pp.q = static_cast<const uint16_t*>(a.q);
+    pp.o = static_cast<const uint16_t*>(a.o);
+    pp.dout = static_cast<const uint16_t*>(a.dout);
+    pp.lse = a.lse;
+    pp.qc = qc;
+    pp.nlse = nlse;
+    pp.ndelta = ndelta;
+    pp.qs0 = a.qs[0]; pp.qs1 = a.qs[1]; pp.qs2 = a.qs[2];
+    pp.os0 = a.os[0]; pp.os1 = a.os[1]; pp.os2 = a.os[2];
+    pp.ds0 = a.dos[0]; pp.ds1 = a.dos[1]; pp.ds2 = a.dos[2];
+    pp.batch = a.batch;
+    pp.hq = a.hq;
+    pp.N = a.N;
+    pp.Npad = Npad;
+    pp.c = c;
+    const int64_t prep_threads = (int64_t)a.batch * Npad * a.hq * (a.d / 8);
+    const dim3 pg((unsigned)((prep_threads + 255) / 256));
+    if (a.d == 128) hipLaunchKernelGGL((attn_bwd_prep_kernel<128>), pg, dim3(256), 0, s, pp);
+    else hipLaunchKernelGGL((attn_bwd_prep_kernel<64>), pg, dim3(256), 0, s, pp);
+
+    DkvParams kp;
+    kp.qc = qc;
+    kp.dout = pp.dout;
+    kp.k = static_cast<const uint16_t*>(a.k);
+    kp.v = static_cast<const uint16_t*>(a.v);
+    kp.nlse = nlse;
+    kp.ndelta = ndelta;
+    kp.dk = static_cast<uint16_t*>(a.dk);
+    kp.dv = static_cast<uint16_t*>(a.dv);
+    kp.ds0 = a.dos[0]; kp.ds1 = a.dos[1]; kp.ds2 = a.dos[2];
+    kp.ks0 = a.ks[0]; kp.ks1 = a.ks[1]; kp.ks2 = a.ks[2];
+    kp.vs0 = a.vs[0]; kp.vs1 = a.vs[1]; kp.vs2 = a.vs[2];
+    kp.dks0 = a.dks[0]; kp.dks1 = a.dks[1]; kp.dks2 = a.dks[2];
+    kp.dvs0 = a.dvs[0]; kp.dvs1 = a.dvs[1]; kp.dvs2 = a.dvs[2];
+    kp.hq = a.hq;
+    kp.hkv = a.hkv;
+    kp.G = G;
+    kp.P = a.P;
+    kp.L = a.L;
+    kp.B = a.B;
+    kp.N = a.N;
+    kp.Npad = Npad;
+    kp.bg_count = a.batch * a.hkv;
+    const int kblocks = (a.N + kKeysPerWG - 1) / kKeysPerWG;
+    const dim3 kg((unsigned)((int64_t)kblocks * kp.bg_count));
+    if (a.d == 128) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128>), kg, dim3(kThreadsB), 0, s, kp);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), kg, dim3(kThreadsB), 0, s, kp);
+
+    DqParams qp;
+    qp.qc = qc;
+    qp.dout = pp.dout;
+    qp.k = kp.k;
+    qp.v = kp.v;
+    qp.nlse = nlse;
+    qp.ndelta = ndelta;
+    qp.dq = static_cast<uint16_t*>(a.dq);
+    qp.ds0 = a.dos[0]; qp.ds1 = a.dos[1]; qp.ds2 = a.dos[2];
+    qp.ks0 = a.ks[0]; qp.ks1 = a.ks[1]; qp.ks2 = a.ks[2];
+    qp.vs0 = a.vs[0]; qp.vs1 = a.vs[1]; qp.vs2 = a.vs[2];
+    qp.qs0 = a.dqs[0]; qp.qs1 = a.dqs[1]; qp.qs2 = a.dqs[2];
+    qp.hq = a.hq;
+    qp.hkv = a.hkv;
+    qp.G = G;
+    qp.P = a.P;
+    qp.L = a.L;
+    qp.B = a.B;
+    qp.N = a.N;
+    qp.Npad = Npad;
+    qp.rows_per_pair = a.N * G;
+    qp.tiles_per_pair = (qp.rows_per_pair + kRowsPerWGB - 1) / kRowsPerWGB;
+    const int64_t noisy_row0 = (int64_t)(a.P + a.L) * G;
+    int tN0 = (int)((noisy_row0 + kRowsPerWGB - 1) / kRowsPerWGB);
+    if (tN0 > qp.tiles_per_pair) tN0 = qp.tiles_per_pair;
+    qp.tN0 = tN0;
+    qp.bg_count = a.batch * a.hkv;
+    qp.scale = a.scale;
+    const dim3 qg((unsigned)((int64_t)qp.tiles_per_pair * qp.bg_count));
+    if (a.d == 128) hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), qg, dim3(kThreadsB), 0, s, qp);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<64>), qg, dim3(kThreadsB), 0, s, qp);
+    return hipGetLastError();
+}
+
+}  // namespace mars

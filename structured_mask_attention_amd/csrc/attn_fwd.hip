@@ -70,15 +70,6 @@ struct AttnKParams {
     float scale_log2;    // scale * log2(e)
 };
 
-// Workgroup rank -> row tile: noisy tiles from the end interleaved with the other tiles
-// from the end of the clean stream, then whatever remains, in descending order.
-__device__ inline int rank_to_tile(int rank, int T, int tN0) {
-    const int nN = T - tN0, nR = tN0;
-    const int m = nN < nR ? nN : nR;
-    if (rank < 2 * m) return (rank & 1) ? (tN0 - 1 - (rank >> 1)) : (T - 1 - (rank >> 1));
-    const int rr = rank - 2 * m;
-    return (nN > m) ? (T - 1 - m - rr) : (tN0 - 1 - m - rr);
-}
 
 // K/V ring: 3 stages, one file-scope __shared__ object per stage, tensor and head_dim, so
 // every access names its array directly (no generic pointers to LDS).

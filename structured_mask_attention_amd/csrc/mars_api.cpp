@@ -116,6 +116,66 @@ int mars_attn_fwd(const mars_attn_desc* desc, const void* q, const void* k, cons
     return map_hip(mars::launch_attn_fwd_f32(a, stream));
 }
 
+int mars_attn_bwd_workspace_bytes(const mars_attn_desc* desc, size_t* bytes) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (!bytes) return MARS_EINVAL;
+    if (desc->dtype != MARS_DTYPE_BF16) return MARS_EUNSUPPORTED;
+    *bytes = mars::attn_bwd_workspace_bytes(desc->batch, desc->n_q_heads, (int)attn_N(desc), desc->head_dim);
+    return MARS_OK;
+}
+
+int mars_attn_bwd(const mars_attn_desc* desc, const mars_attn_bwd_strides* gs, const void* q, const void* k,
+                  const void* v, const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (!gs) return MARS_EINVAL;
+    if (desc->dtype != MARS_DTYPE_BF16) return MARS_EUNSUPPORTED;
+    if (desc->batch == 0 || attn_N(desc) == 0) return MARS_OK;
+    st = check_attn_tensors(desc, q, k, v, o, lse);
+    if (st) return st;
+    if (!lse || !d_o || !dq || !dk || !dv) return MARS_EINVAL;
+    if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return MARS_EINVAL;
+    if (!strides_ok(gs->do_strides, 2) || !strides_ok(gs->dq_strides, 2) || !strides_ok(gs->dk_strides, 2) ||
+        !strides_ok(gs->dv_strides, 2))
+        return MARS_EINVAL;
+    if (gs->do_strides[1] > kMaxKeyPosStride) return MARS_EUNSUPPORTED;
+    const size_t need = mars::attn_bwd_workspace_bytes(desc->batch, desc->n_q_heads, (int)attn_N(desc), desc->head_dim);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MARS_EWORKSPACE;
+    mars::AttnBwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.dout = d_o;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.ws = ws;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = desc->q_strides[i];
+        a.ks[i] = desc->k_strides[i];
+        a.vs[i] = desc->v_strides[i];
+        a.os[i] = desc->o_strides[i];
+        a.dos[i] = gs->do_strides[i];
+        a.dqs[i] = gs->dq_strides[i];
+        a.dks[i] = gs->dk_strides[i];
+        a.dvs[i] = gs->dv_strides[i];
+    }
+    a.batch = desc->batch;
+    a.hq = desc->n_q_heads;
+    a.hkv = desc->n_kv_heads;
+    a.d = desc->head_dim;
+    a.P = desc->prompt_len;
+    a.L = desc->resp_len;
+    a.B = desc->block;
+    a.N = (int)attn_N(desc);
+    a.scale = eff_scale(desc->scale, desc->head_dim);
+    return map_hip(mars::launch_attn_bwd_bf16(a, stream));
+}
+
 int mars_attn_tilelog_geometry(const mars_attn_desc* desc, int32_t* row_block, int32_t* key_block,
                                int64_t* rows_per_pair) {
     int st = check_attn_desc(desc);

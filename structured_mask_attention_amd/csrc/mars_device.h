@@ -111,6 +111,18 @@ __device__ inline int swz_v(int r) {
     return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
+// Row-tile order of the training-layout kernels that walk keys per row tile (heaviest
+// first): rank -> row tile, with T row tiles per (batch, kv head) and tN0 the first tile
+// that starts at a noisy position.  Noisy tiles from the end interleaved with the other
+// tiles from the end of the clean stream, then whatever remains, in descending order.
+__device__ inline int rank_to_tile(int rank, int T, int tN0) {
+    const int nN = T - tN0, nR = tN0;
+    const int m = nN < nR ? nN : nR;
+    if (rank < 2 * m) return (rank & 1) ? (tN0 - 1 - (rank >> 1)) : (T - 1 - (rank >> 1));
+    const int rr = rank - 2 * m;
+    return (nN > m) ? (T - 1 - m - rr) : (tN0 - 1 - m - rr);
+}
+
 // LDS byte address of a __shared__ object (the low half of its generic address).
 __device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 

@@ -27,6 +27,25 @@ constexpr int kAttnKeyBlock = 32;   // keys per LDS tile
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t s);
 
+// Training-layout backward (attn_bwd.hip): gradients of the bf16 forward.
+struct AttnBwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;    // fp32 [batch][hq][N], natural log (the forward's output)
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    void* ws;
+    int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];
+    int batch, hq, hkv, d, P, L, B, N;
+    float scale;         // > 0
+};
+size_t attn_bwd_workspace_bytes(int batch, int hq, int N, int d);
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
+
 // Debug mask kernels (mask_kernels.hip).
 hipError_t launch_mask_materialize(int P, int L, int B, uint8_t* mask, hipStream_t s);
 hipError_t launch_tile_map(int P, int L, int B, int bm, int bn, int8_t* map, hipStream_t s);

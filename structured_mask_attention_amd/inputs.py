@@ -96,6 +96,20 @@ def small_train_inputs(batch, hq, hkv, d, P, L, seed, dtype="bf16", in_scale=0.5
     return train_inputs(s)
 
 
+def grad_output(s: TrainShape, seed: int | None = None, scale: float = 0.5):
+    """dL/dO for the backward: [b, N, Hq, D] ~ N(0, 1) * scale in the workload's dtype, drawn
+    from its own stream (seed + 7919) so that Q/K/V stay those of :func:`train_inputs`."""
+    rng = np.random.default_rng((s.seed if seed is None else seed) + 7919)
+    x = rng.standard_normal((s.batch, s.N, s.hq, s.d), dtype=np.float32) * np.float32(scale)
+    return to_bf16(x) if s.dtype == "bf16" else torch.from_numpy(x)
+
+
+def small_grad_output(batch, hq, d, P, L, seed, dtype="bf16", scale=0.5):
+    """Like :func:`grad_output` for an ad-hoc shape."""
+    s = TrainShape("adhoc", batch, hq, 1, d, P, L, 1, dtype, 0.5, seed)
+    return grad_output(s, scale=scale)
+
+
 @dataclass
 class DecodeInputs:
     cache_len: torch.Tensor   # int32 [b]

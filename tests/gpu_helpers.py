@@ -86,3 +86,84 @@ def sample_rows(P, L, B, n_random, seed):
     rows = set(r for r in fixed if 0 <= r < N)
     rows.update(rng.integers(0, N, size=n_random).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def bwd_bounds(q, k, v, do, o_in, lse_err, P, L, B, rows=None, keys=None, scale=None):
+    """Per-element bounds on |grad_kernel - grad_exact| for the bf16 backward.
+
+    q, k, v, do: float64 copies of the bf16 inputs; o_in: the O handed to the kernel;
+    lse_err: [b, Hq, N] bound on |LSE_in - LSE_exact| (nats).  Sources of error, each bounded
+    by its largest effect (u = 2^-8, bf16's unit roundoff):
+      * the scores use bf16(Q*scale*log2 e) as the forward does: score (i, j) moves by at
+        most u*c*sum_d |q_id||k_jd| (log2 units), so P_ij by a relative 2^(u c m_i) - 1 with
+        m_i the max over keys; the LSE input adds e^lse_err - 1;
+      * D_i = sum dO.O from the given O: |dD_i| <= sum_d |dO_id||O_in - O_exact|_id;
+      * P (for dV) and dS (for dQ, dK) are rounded to bf16 (u each), Q*c as well (dK);
+      * fp32 accumulation over n terms: n*2^-24 of the sum of absolute terms;
+      * the bf16 output rounding: u |grad|.
+    Returns (bq [b,R,Hq,D], bk [b,K,Hkv,D], bv [b,K,Hkv,D]) for rows / keys (all by default).
+    """
+    b, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    c = scale * np.log2(np.e)
+    u = 2.0 ** -8
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    keys = np.arange(N) if keys is None else np.asarray(keys)
+    cols = np.zeros(N, dtype=bool)
+    cols[keys] = True
+    vis_all = O.mask_rules(P, L, B)
+    krows = np.nonzero((vis_all & cols[None, :]).any(axis=1))[0]
+    gam = N * 2.0 ** -24
+    bq = np.zeros((b, len(rows), Hq, D))
+    bk = np.zeros((b, len(keys), Hkv, D))
+    bv = np.zeros((b, len(keys), Hkv, D))
+    for bi in range(b):
+        for h in range(Hq):
+            g = h // G
+            for rr, want_q in ((rows, True), (krows, False)):
+                if len(rr) == 0:
+                    continue
+                vis = vis_all[rr]
+                qa = q[bi, rr, h]
+                s = scale * (qa @ k[bi, :, g].T)
+                s = np.where(vis, s, -np.inf)
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                o = p @ v[bi, :, g]
+                dO = do[bi, rr, h]
+                x = dO @ v[bi, :, g].T - np.sum(dO * o, axis=1, keepdims=True)      # dP - D
+                m = (np.abs(qa) @ np.abs(k[bi, :, g]).T).max(axis=1)
+                rel = 2.0 ** (u * c * m) - 1.0 + np.expm1(lse_err[bi, h, rr])       # relative error of P
+                eD = np.sum(np.abs(dO) * np.abs(o_in[bi, rr, h] - o), axis=1)        # |dD|
+                rel, eD = rel[:, None], eD[:, None]
+                ds = p * x
+                dds = p * (rel * np.abs(x) + (1 + rel) * eD) + u * (1 + rel) * p * (np.abs(x) + eD) \
+                    + gam * p * (np.abs(dO) @ np.abs(v[bi, :, g]).T)
+                if want_q:
+                    dq = scale * (ds @ k[bi, :, g])
+                    bq[bi, :, h] = scale * (dds @ np.abs(k[bi, :, g])) * (1 + gam) \
+                        + gam * scale * (np.abs(ds) @ np.abs(k[bi, :, g])) + u * np.abs(dq) + 1e-6
+                else:
+                    pk, dsk, ddsk = p[:, keys], ds[:, keys], dds[:, keys]
+                    relv = rel + u * (1 + rel)
+                    bv[bi, :, g] += (pk * relv).T @ np.abs(dO) + gam * (pk.T @ np.abs(dO))
+                    bk[bi, :, g] += scale * ((ddsk + u * np.abs(dsk)).T @ np.abs(qa)) \
+                        + gam * scale * (np.abs(dsk).T @ np.abs(qa))
+    # output rounding of dK / dV (relative to the exact value, bounded by the sums above)
+    return bq, bk, bv
+
+
+def check_bounded(got, ref, bound, what, extra_rel=2.0 ** -8):
+    """|got - ref| <= bound + extra_rel*|ref| elementwise (extra_rel: output rounding)."""
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    tol = bound + extra_rel * np.abs(ref) + 1e-6
+    ratio = float(np.max(err / tol)) if err.size else 0.0
+    print(f"[{what}] max_abs={float(err.max()) if err.size else 0:.3e} max|ref|={float(np.abs(ref).max()) if err.size else 0:.3e} "
+          f"max err/bound={ratio:.3f}", flush=True)
+    assert ratio <= 1.0, f"{what}: error exceeds its bound (ratio {ratio:.3f})"
+    return ratio

@@ -94,6 +94,47 @@ def test_attn_validation_errors():
     assert lib.mars_mask_materialize(ctypes.byref(good()), None, None) == L.MARS_EINVAL
 
 
+def _bwd(desc, gs, ws=FAKE, ws_bytes=1 << 30, lse=FAKE, dout=FAKE, dq=FAKE):
+    return L.load().mars_attn_bwd(ctypes.byref(desc), ctypes.byref(gs) if gs is not None else None, FAKE, FAKE,
+                                  FAKE, FAKE, lse, dout, dq, FAKE, FAKE, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_attn_bwd_validation_errors():
+    lib = L.load()
+    good = lambda: M.attn_desc(2, 14, 2, 64, 10, 20, 4)
+
+    def strides():
+        gs = L.AttnBwdStrides()
+        d = good()
+        gs.do_strides, gs.dq_strides, gs.dk_strides, gs.dv_strides = d.o_strides, d.q_strides, d.k_strides, d.v_strides
+        return gs
+    n = ctypes.c_size_t()
+    assert lib.mars_attn_bwd_workspace_bytes(ctypes.byref(good()), ctypes.byref(n)) == L.MARS_OK
+    N, Np = 50, 64                                           # positions padded to a multiple of 32
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert n.value == r256(2 * Np * 14 * 64 * 2) + 2 * r256(2 * 14 * Np * 4)
+    assert lib.mars_attn_bwd_workspace_bytes(ctypes.byref(good()), None) == L.MARS_EINVAL
+    d = good(); d.dtype = L.MARS_DTYPE_FP32
+    assert lib.mars_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == L.MARS_EUNSUPPORTED
+    assert _bwd(d, strides()) == L.MARS_EUNSUPPORTED
+    assert _bwd(good(), None) == L.MARS_EINVAL
+    assert _bwd(good(), strides(), lse=None) == L.MARS_EINVAL
+    assert _bwd(good(), strides(), dout=None) == L.MARS_EINVAL
+    assert _bwd(good(), strides(), dq=MISALIGNED) == L.MARS_EINVAL
+    gs = strides(); gs.dk_strides[1] = 2 * 64 + 4
+    assert _bwd(good(), gs) == L.MARS_EINVAL
+    gs = strides(); gs.do_strides[1] = (1 << 25) + 8
+    assert _bwd(good(), gs) == L.MARS_EUNSUPPORTED
+    d = good(); d.head_dim = 96
+    assert _bwd(d, strides()) == L.MARS_EUNSUPPORTED
+    assert _bwd(good(), strides(), ws=None) == L.MARS_EWORKSPACE
+    assert _bwd(good(), strides(), ws_bytes=n.value - 1 if n.value else 0) == L.MARS_EWORKSPACE
+    assert _bwd(good(), strides(), ws=MISALIGNED) == L.MARS_EWORKSPACE
+    d = good(); d.batch = 0
+    assert L.load().mars_attn_bwd(ctypes.byref(d), ctypes.byref(strides()), None, None, None, None, None, None,
+                                  None, None, None, None, ctypes.c_size_t(0), None) == L.MARS_OK
+
+
 def test_decode_validation_errors():
     lib = L.load()
     good = lambda: M.decode_desc(4, 28, 4, 128, 4, 4096)
