@@ -6,7 +6,7 @@
 // With P the forward's row probabilities, D_i = sum_d dO_id O_id, and in the log2 domain
 // of the forward (scores s = c q.k, c = scale*log2(e); P = 2^(s - LSE*log2(e))):
 //   dV = P^T dO,   dS = P o (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q,
-// dK and dV of a KV head summed over its G query heads.  Three kernels, no atomics:
+// dK and dV of a KV head summed over its G query heads.  Three kernels:
 //   1. prep (per row): Qc = bf16(Q*c) exactly as the forward rounds it, -D and
 //      -LSE*log2(e), into the workspace, positions padded to a multiple of 32 (zeros);
 //   2. dK/dV (key-stationary): a workgroup owns 128 keys of one (batch, kv head), 32 per
@@ -17,7 +17,11 @@
 //      S = Qc K^T and dP = dO V^T (MFMA accumulators start at -LSE2 and -D), P = 2^S,
 //      dS = P dP, then dV^T += dO^T P and dK^T += Qc^T dS with the transposed operands read
 //      by ds_read_b64_tr_b16.  The element mask is a per-key bitmask over the tile's 32
-//      positions.
+//      positions.  A heavy key block (prompt keys are seen by every row) splits its walk
+//      into up to 8 chunks on separate workgroups (chunk size from the layout's total work);
+//      their fp32 partials are written through to memory and summed in chunk order by
+//      whichever wave of a 32-key slice arrives last (one counter per slice), so the result
+//      does not depend on the arrival order.
 //   3. dQ (row-stationary): the forward's row packing, tile walk, tile classes and K/V
 //      ring; per tile S^T = K Qc^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 // P and dS enter the MFMAs as bf16 (round to nearest even); statistics and accumulation
@@ -38,6 +42,10 @@ constexpr int kT = 32;               // keys per dQ tile; positions per dK/dV ti
 constexpr int kStagesB = 3;
 constexpr int kKeysPerWG = kWavesB * kT;   // dK/dV: 128 keys per workgroup
 constexpr int kRowsPerWGB = kWavesB * kT;  // dQ: 128 packed rows per workgroup
+constexpr int kChunkMax = 8;               // dK/dV: a key block's walk splits into at most 8 chunks
+constexpr int kChunkMinTiles = 4;          //        of at least 4 position tiles each
+constexpr int kNominalSlots64 = 512;       // resident dK/dV workgroups the chunk size aims at
+constexpr int kNominalSlots128 = 256;      // (256 CUs x 2 or 1 per CU, by head_dim)
 
 // ---------------------------------------------------------------------------------------
 // LDS rings.  One file-scope object per stage, array and head_dim.
@@ -140,6 +148,43 @@ __device__ inline bf16x8_t tr_frag(const char* tile, int off0, int db, int kh) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Position tiles (32 positions) that see some key of [kb0, kb1): sorted, merged ranges
+// [rs[i], re[i]) of tile indices; returns their number (<= 3).  Prompt/clean keys are seen
+// by the later prompt/clean rows and by the noisy rows of the blocks after the smallest
+// key's own (every block for a prompt key); noisy keys by the later rows of their block.
+__host__ __device__ inline int kblock_tile_ranges(int kb0, int kb1, int P, int L, int B, int N, int rs[3], int re[3]) {
+    const int PL = P + L;
+    int s[3], e[3], n = 0;
+    if (kb0 < PL) {
+        s[n] = kb0; e[n] = PL; ++n;
+        const int n0 = PL + (kb0 < P ? 0 : B * ((kb0 - P) / B + 1));
+        if (n0 < N) { s[n] = n0; e[n] = N; ++n; }
+    }
+    if (kb1 > PL) {
+        const int kl = (kb1 - 1 - PL) / B;
+        const int hi = PL + (kl + 1) * B;
+        s[n] = kb0 > PL ? kb0 : PL; e[n] = hi < N ? hi : N; ++n;
+    }
+    for (int i = 0; i < n; ++i) { s[i] = s[i] / kT; e[i] = (e[i] + kT - 1) / kT; }
+    for (int i = 1; i < n; ++i)
+        for (int m = i; m > 0 && s[m] < s[m - 1]; --m) {
+            const int ts = s[m], te = e[m];
+            s[m] = s[m - 1]; e[m] = e[m - 1]; s[m - 1] = ts; e[m - 1] = te;
+        }
+    int nm = 0;
+    for (int i = 0; i < n; ++i) {
+        if (nm > 0 && s[i] <= re[nm - 1]) re[nm - 1] = re[nm - 1] > e[i] ? re[nm - 1] : e[i];
+        else { rs[nm] = s[i]; re[nm] = e[i]; ++nm; }
+    }
+    return nm;
+}
+
+// Chunks of a key block's walk of npt position tiles, at most tc tiles per chunk.
+__host__ __device__ inline int walk_chunks(int npt, int tc) {
+    const int c = (npt + tc - 1) / tc;
+    return c < 1 ? 1 : (c > kChunkMax ? kChunkMax : c);
+}
+
 // ---------------------------------------------------------------------------------------
 // 1. Row prologue.
 // ---------------------------------------------------------------------------------------
@@ -151,8 +196,9 @@ struct PrepParams {
     uint16_t* qc;
     float* nlse;
     float* ndelta;
+    int* cnt;            // dK/dV arrival counters, zeroed here
     int64_t qs0, qs1, qs2, os0, os1, os2, ds0, ds1, ds2;
-    int batch, hq, N, Npad;
+    int batch, hq, N, Npad, ncnt;
     float c;
 };
 
@@ -163,6 +209,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(PrepParams p) {
     const int64_t row = t / TPR;
     const int c8 = (int)(t % TPR);
     const int64_t rows = (int64_t)p.batch * p.Npad * p.hq;
+    if (t < p.ncnt) p.cnt[t] = 0;
     if (row >= rows) return;   // whole TPR-lane groups leave together
     const int h = (int)(row % p.hq);
     const int64_t bp = row / p.hq;
@@ -204,13 +251,15 @@ struct DkvParams {
     const float* ndelta;
     uint16_t* dk;
     uint16_t* dv;
+    float* part;             // workspace [nch_max][kblocks][bg][4 waves][32 keys x 2D] fp32
+    int* cnt;                // workspace [kblocks][bg][4 waves], zero on entry
     int64_t ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
     int hq, hkv, G, P, L, B, N, Npad;
-    int bg_count;
+    int bg_count, kblocks, nch_max, tc;
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p) {
+__global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kernel(DkvParams p) {
     constexpr int NC = D / 16;                    // 16-wide d chunks of the S / dP contractions
     constexpr int NDB = D / 32;                   // 32-row d blocks of dK^T / dV^T
     constexpr int CPR = D / 8;                    // 16-byte chunks per tile row
@@ -224,12 +273,29 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane & 31, g2 = lane >> 5;
-    const int bg = blockIdx.x % p.bg_count;
-    const int kblk = blockIdx.x / p.bg_count;
+    // Work item: chunk c (fastest) of the walk of key block kblk of pair bg.
+    const int c = blockIdx.x % p.nch_max;
+    const int rest = blockIdx.x / p.nch_max;
+    const int bg = rest % p.bg_count;
+    const int kblk = rest / p.bg_count;
     const int b = bg / p.hkv, g = bg % p.hkv;
     const int PL = p.P + p.L;
     const int kb0 = kblk * kKeysPerWG;
     const int kb1 = min(kb0 + kKeysPerWG, p.N);
+
+    // Position tiles of the key block (union over its keys), then this chunk's share.
+    int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
+    kblock_tile_ranges(kb0, kb1, p.P, p.L, p.B, p.N, rs, re);
+    const int n0t = re[0] - rs[0], n1t = re[1] - rs[1], n2t = re[2] - rs[2];
+    const int npt = n0t + n1t + n2t;
+    const int nch = walk_chunks(npt, p.tc);
+    if (c >= nch) return;
+    const int ct0 = (int)((int64_t)c * npt / nch), ct1 = (int)((int64_t)(c + 1) * npt / nch);
+    const int nsteps = (ct1 - ct0) * p.G;
+    auto pos_tile = [&](int ti) __attribute__((always_inline)) {
+        ti += ct0;
+        return ti < n0t ? rs[0] + ti : (ti < n0t + n1t ? rs[1] + (ti - n0t) : rs[2] + (ti - n0t - n1t));
+    };
 
     // This lane's key and its K / V rows as B operands (k = d: 8 values per lane per chunk).
     const int j = kb0 + wave * kT + hl;
@@ -261,42 +327,6 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p
         }
     }
 
-    // Position tiles of the workgroup: union over its keys, as up to three ranges of
-    // 32-position tiles, sorted and merged.
-    int r0s = 0, r0e = 0, r1s = 0, r1e = 0, r2s = 0, r2e = 0;
-    {
-        int s[3], e[3], n = 0;
-        if (kb0 < PL) {
-            s[n] = kb0; e[n] = PL; ++n;
-            const int n0 = PL + (kb0 < p.P ? 0 : p.B * ((kb0 - p.P) / p.B + 1));
-            if (n0 < p.N) { s[n] = n0; e[n] = p.N; ++n; }
-        }
-        if (kb1 > PL) {
-            const int kl = (kb1 - 1 - PL) / p.B;
-            s[n] = max(kb0, PL); e[n] = min(p.N, PL + (kl + 1) * p.B); ++n;
-        }
-        // tile units, insertion sort by start, merge overlapping or adjacent ranges
-        for (int i = 0; i < n; ++i) { s[i] = s[i] / kT; e[i] = (e[i] + kT - 1) / kT; }
-        for (int i = 1; i < n; ++i)
-            for (int m = i; m > 0 && s[m] < s[m - 1]; --m) {
-                const int ts = s[m], te = e[m];
-                s[m] = s[m - 1]; e[m] = e[m - 1]; s[m - 1] = ts; e[m - 1] = te;
-            }
-        int ms[3], me[3], nm = 0;
-        for (int i = 0; i < n; ++i) {
-            if (nm > 0 && s[i] <= me[nm - 1]) me[nm - 1] = max(me[nm - 1], e[i]);
-            else { ms[nm] = s[i]; me[nm] = e[i]; ++nm; }
-        }
-        if (nm > 0) { r0s = ms[0]; r0e = me[0]; }
-        if (nm > 1) { r1s = ms[1]; r1e = me[1]; }
-        if (nm > 2) { r2s = ms[2]; r2e = me[2]; }
-    }
-    const int n0t = r0e - r0s, n1t = r1e - r1s, n2t = r2e - r2s;
-    const int nsteps = (n0t + n1t + n2t) * p.G;
-    auto pos_tile = [&](int ti) __attribute__((always_inline)) {
-        return ti < n0t ? r0s + ti : (ti < n0t + n1t ? r1s + (ti - n0t) : r2s + (ti - n0t - n1t));
-    };
-
     // Copy of step `it` (position tile, head) into stage ST.  Window slot (row r,
     // position ps) holds logical chunk ps ^ swz_v(r) of row r; dO rows past N repeat row
     // N-1 (finite; such rows are always masked).  The scalar copy: wave w moves bytes
@@ -310,29 +340,47 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p
         qgo[w] = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_v<D>(r)));
         ogo[w] = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_v<D>(r)));
     }
-    auto issue = [&](const int it, auto stage) __attribute__((always_inline)) {
+    // Running position of the next copy (walk order: position tile, then head): tile index
+    // iti, head ih, and that step's base pointers; a head step adds one head stride, a tile
+    // step recomputes them.
+    int iti = 0, ih = 0, ip0 = 0;
+    const uint16_t* iq = nullptr;
+    const uint16_t* io = nullptr;
+    const float* isl = nullptr;
+    auto seek = [&]() __attribute__((always_inline)) {
+        ip0 = pos_tile(iti) * kT;
+        const int head = g * p.G;
+        iq = p.qc + ((int64_t)b * p.Npad + ip0) * qc_row + (int64_t)head * D;
+        io = p.dout + b * p.ds0 + (int64_t)ip0 * p.ds1 + (int64_t)head * p.ds2;
+        isl = (wave < 2 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + ip0 + 16 * (wave & 1);
+    };
+    seek();
+    auto issue = [&](auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        const int ti = it / p.G, hh = it - ti * p.G;
-        const int p0 = pos_tile(ti) * kT;
-        const int head = g * p.G + hh;
-        const uint16_t* qb = p.qc + ((int64_t)b * p.Npad + p0) * qc_row + (int64_t)head * D;
-        const uint16_t* ob = p.dout + b * p.ds0 + (int64_t)p0 * p.ds1 + (int64_t)head * p.ds2;
-        const bool full = p0 + kT <= p.N;
+        const bool full = ip0 + kT <= p.N;
 #pragma unroll
         for (int w = 0; w < PERW; ++w) {
             const int jw = wave * PERW + w;
-            dma16_sv(qb, qgo[w], lds_addr(ring_q<D, ST>()) + 1024 * jw);
+            dma16_sv(iq, qgo[w], lds_addr(ring_q<D, ST>()) + 1024 * jw);
             if (full) {
-                dma16_sv(ob, ogo[w], lds_addr(ring_o<D, ST>()) + 1024 * jw);
+                dma16_sv(io, ogo[w], lds_addr(ring_o<D, ST>()) + 1024 * jw);
             } else {
                 const int slot = 64 * jw + lane;
                 const int r = slot / CPR, ps = slot % CPR;
-                const int rr = min(r, p.N - 1 - p0);
-                dma16_sv(ob, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_v<D>(r))), lds_addr(ring_o<D, ST>()) + 1024 * jw);
+                const int rr = min(r, p.N - 1 - ip0);
+                dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_v<D>(r))), lds_addr(ring_o<D, ST>()) + 1024 * jw);
             }
         }
-        const float* sb = (wave < 2 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + p0 + 16 * (wave & 1);
-        if (lane < 4) dma16_sv(sb, (uint32_t)(16 * lane), lds_addr(ring_s<D, ST>()) + 64 * wave);
+        if (lane < 4) dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(ring_s<D, ST>()) + 64 * wave);
+        if (++ih == p.G) {
+            ih = 0;
+            ++iti;
+            seek();
+        } else {
+            iq += D;
+            io += p.ds2;
+            isl += p.Npad;
+        }
     };
 
     f32x16_t dva[NDB], dka[NDB];
@@ -347,27 +395,31 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p
     const int roff = row_read_off<D>(hl, g2, swz_v<D>(hl));
     const int troff = tr_read_off<D>(lane);
 
-    issue(0, S0{});
-    if (nsteps > 1) issue(1, S1{});
+    issue(S0{});
+    if (nsteps > 1) issue(S1{});
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
 
     uint32_t vis = 0;
     bool any = false, all = false;
+    int cti = 0, ch = 0;   // position tile and head of the step being computed
     auto body = [&](const int it, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
         if (it + 1 < nsteps) wait_vmcnt<GROUPW>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (it + 2 < nsteps) issue(it + 2, std::integral_constant<int, (ST + 2) % kStagesB>{});
+        if (it + 2 < nsteps) issue(std::integral_constant<int, (ST + 2) % kStagesB>{});
 
-        const int ti = it / p.G;
-        if (it - ti * p.G == 0) {
+        if (ch == 0) {
             // New position tile: this lane's visibility bits and the wave's tile class.
-            const int p0 = pos_tile(ti) * kT;
+            const int p0 = pos_tile(cti) * kT;
             vis = span_bits(a1, b1, p0) | span_bits(a2, b2, p0);
             any = __builtin_amdgcn_ballot_w64(kvalid && vis != 0u) != 0ull;
             all = __builtin_amdgcn_ballot_w64(kvalid && vis != 0xffffffffu) == 0ull;
+        }
+        if (++ch == p.G) {
+            ch = 0;
+            ++cti;
         }
         if (!any) return;
 
@@ -422,7 +474,11 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p
     }
 
     // dV = dV^T^T; dK = ln2 * dK^T^T (Qc carries scale*log2(e) where dK needs scale).
-    if (kvalid) {
+    // A walk in several chunks: every chunk stores its fp32 partial for its 32 keys; the
+    // wave that arrives last for this 32-key slice (per-slice counter) sums the partials in
+    // chunk order (the same order whoever is last) and stores the result.
+    auto store_final = [&](const f32x16_t* gv, const f32x16_t* gk) __attribute__((always_inline)) {
+        if (!kvalid) return;
         uint16_t* vo = p.dv + b * p.dvs0 + (int64_t)j * p.dvs1 + (int64_t)g * p.dvs2;
         uint16_t* ko = p.dk + b * p.dks0 + (int64_t)j * p.dks1 + (int64_t)g * p.dks2;
 #pragma unroll
@@ -431,15 +487,77 @@ __global__ __launch_bounds__(kThreadsB, 1) void attn_bwd_dkdv_kernel(DkvParams p
             for (int bb = 0; bb < 4; ++bb) {
                 const int d = 32 * db + 8 * bb + 4 * g2;
                 uint2 wv, wk;
-                wv.x = pack_bf16x2(dva[db][4 * bb + 0], dva[db][4 * bb + 1]);
-                wv.y = pack_bf16x2(dva[db][4 * bb + 2], dva[db][4 * bb + 3]);
-                wk.x = pack_bf16x2(dka[db][4 * bb + 0] * kLn2, dka[db][4 * bb + 1] * kLn2);
-                wk.y = pack_bf16x2(dka[db][4 * bb + 2] * kLn2, dka[db][4 * bb + 3] * kLn2);
+                wv.x = pack_bf16x2(gv[db][4 * bb + 0], gv[db][4 * bb + 1]);
+                wv.y = pack_bf16x2(gv[db][4 * bb + 2], gv[db][4 * bb + 3]);
+                wk.x = pack_bf16x2(gk[db][4 * bb + 0] * kLn2, gk[db][4 * bb + 1] * kLn2);
+                wk.y = pack_bf16x2(gk[db][4 * bb + 2] * kLn2, gk[db][4 * bb + 3] * kLn2);
                 *reinterpret_cast<uint2*>(vo + d) = wv;
                 *reinterpret_cast<uint2*>(ko + d) = wk;
             }
         }
+    };
+    if (nch == 1) {
+        store_final(dva, dka);
+        return;
     }
+    // Partial of this wave: [dV | dK][d block][4 element groups][64 lanes] x 16 bytes, so
+    // every store / load instruction moves 1 KB of contiguous memory.  Both are system
+    // coherent (sc0 sc1): written through to memory and read from it, so chunks on other
+    // XCDs see them without cache maintenance.
+    constexpr int kSlotBytes = 2 * NDB * 4 * 64 * 16;
+    auto slot_rsrc = [&](int cc) __attribute__((always_inline)) {
+        char* base = reinterpret_cast<char*>(p.part) +
+                     ((((int64_t)cc * p.kblocks + kblk) * p.bg_count + bg) * kWavesB + wave) * (int64_t)kSlotBytes;
+        return __builtin_amdgcn_make_buffer_rsrc(base, 0, kSlotBytes, 0x00020000);
+    };
+    constexpr int kSysCoherent = 1 | 16;   // sc0 | sc1
+    {
+        const __amdgpu_buffer_rsrc_t r = slot_rsrc(c);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const f32x4_t xv = {dva[db][4 * qd], dva[db][4 * qd + 1], dva[db][4 * qd + 2], dva[db][4 * qd + 3]};
+                const f32x4_t xk = {dka[db][4 * qd], dka[db][4 * qd + 1], dka[db][4 * qd + 2], dka[db][4 * qd + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(xv, r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+                __builtin_amdgcn_raw_buffer_store_b128(xk, r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+            }
+        }
+    }
+    // Every partial store of this wave completes before its arrival is counted.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(p.cnt + ((int64_t)kblk * p.bg_count + bg) * kWavesB + wave, 1,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    asm volatile("" ::: "memory");
+    if (old != nch - 1) return;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            dva[db][e] = 0.f;
+            dka[db][e] = 0.f;
+        }
+    }
+    for (int cc = 0; cc < nch; ++cc) {
+        const __amdgpu_buffer_rsrc_t r = slot_rsrc(cc);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const f32x4_t xv = __builtin_amdgcn_raw_buffer_load_b128(r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+                const f32x4_t xk = __builtin_amdgcn_raw_buffer_load_b128(r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dva[db][4 * qd + i] += xv[i];
+                    dka[db][4 * qd + i] += xk[i];
+                }
+            }
+        }
+    }
+    store_final(dva, dka);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -673,23 +791,68 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
 
 int pad32(int n) { return (n + kT - 1) / kT * kT; }
 
+size_t r256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Chunk size of the dK/dV walks (position tiles): about half the mean number of tiles a
+// resident workgroup gets, at least kChunkMinTiles; and the largest chunk count over the
+// key blocks (sizes the partial buffer).
+void walk_plan(int P, int L, int B, int N, int bg, int d, int* tc, int* nch_max) {
+    int64_t total = 0;
+    int maxnpt = 0;
+    for (int kb0 = 0; kb0 < N; kb0 += kKeysPerWG) {
+        int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
+        const int n = kblock_tile_ranges(kb0, kb0 + kKeysPerWG < N ? kb0 + kKeysPerWG : N, P, L, B, N, rs, re);
+        int npt = 0;
+        for (int i = 0; i < n; ++i) npt += re[i] - rs[i];
+        total += npt;
+        maxnpt = npt > maxnpt ? npt : maxnpt;
+    }
+    const int64_t slots = d == 64 ? kNominalSlots64 : kNominalSlots128;
+    const int64_t t = (total * bg + 2 * slots - 1) / (2 * slots);
+    *tc = (int)(t < kChunkMinTiles ? kChunkMinTiles : t);
+    *nch_max = walk_chunks(maxnpt, *tc);
+}
+
+// Workspace: Qc [batch][Npad][hq][D] bf16 | -LSE2 [batch][hq][Npad] | -D [batch][hq][Npad] |
+// counters [kblocks][batch*hkv][4] int | partials [nch][kblocks][batch*hkv][4 waves][32 x 2D] fp32
+// (partials only when some key block's walk is split).
+struct BwdLayout {
+    size_t qc, nlse, ndelta, cnt, part, total;
+    int Npad, kblocks, nch, tc;
+};
+BwdLayout bwd_layout(int batch, int hq, int hkv, int d, int P, int L, int B, int N) {
+    BwdLayout w;
+    w.Npad = pad32(N);
+    w.kblocks = (N + kKeysPerWG - 1) / kKeysPerWG;
+    const size_t bg = (size_t)batch * hkv;
+    walk_plan(P, L, B, N, (int)bg, d, &w.tc, &w.nch);
+    w.qc = 0;
+    w.nlse = r256((size_t)batch * w.Npad * hq * d * 2);
+    w.ndelta = w.nlse + r256((size_t)batch * hq * w.Npad * 4);
+    w.cnt = w.ndelta + r256((size_t)batch * hq * w.Npad * 4);
+    w.part = w.cnt + r256((size_t)w.kblocks * bg * kWavesB * 4);
+    w.total = w.part + (w.nch > 1 ? r256((size_t)w.nch * w.kblocks * bg * kKeysPerWG * 2 * d * 4) : 0);
+    return w;
+}
+
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int batch, int hq, int N, int d) {
-    const size_t Np = (size_t)pad32(N);
-    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    return r256((size_t)batch * Np * hq * d * 2) + 2 * r256((size_t)batch * hq * Np * 4);
+size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int d, int P, int L, int B) {
+    return bwd_layout(batch, hq, hkv, d, P, L, B, P + 2 * L).total;
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
-    const int Npad = pad32(a.N);
-    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const BwdLayout w = bwd_layout(a.batch, a.hq, a.hkv, a.d, a.P, a.L, a.B, a.N);
+    const int Npad = w.Npad;
     char* ws = static_cast<char*>(a.ws);
-    uint16_t* qc = reinterpret_cast<uint16_t*>(ws);
-    float* nlse = reinterpret_cast<float*>(ws + r256((size_t)a.batch * Npad * a.hq * a.d * 2));
-    float* ndelta = reinterpret_cast<float*>(reinterpret_cast<char*>(nlse) + r256((size_t)a.batch * a.hq * Npad * 4));
+    uint16_t* qc = reinterpret_cast<uint16_t*>(ws + w.qc);
+    float* nlse = reinterpret_cast<float*>(ws + w.nlse);
+    float* ndelta = reinterpret_cast<float*>(ws + w.ndelta);
+    int* cnt = reinterpret_cast<int*>(ws + w.cnt);
+    float* part = reinterpret_cast<float*>(ws + w.part);
     const int G = a.hq / a.hkv;
     const float c = a.scale * kLog2e;
+    const int bg_count = a.batch * a.hkv;
 
     PrepParams pp;
     pp.q = static_cast<const uint16_t*>(a.q);
@@ -699,6 +862,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     pp.qc = qc;
     pp.nlse = nlse;
     pp.ndelta = ndelta;
+    pp.cnt = cnt;
     pp.qs0 = a.qs[0]; pp.qs1 = a.qs[1]; pp.qs2 = a.qs[2];
     pp.os0 = a.os[0]; pp.os1 = a.os[1]; pp.os2 = a.os[2];
     pp.ds0 = a.dos[0]; pp.ds1 = a.dos[1]; pp.ds2 = a.dos[2];
@@ -706,8 +870,10 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     pp.hq = a.hq;
     pp.N = a.N;
     pp.Npad = Npad;
+    pp.ncnt = w.kblocks * bg_count * kWavesB;
     pp.c = c;
-    const int64_t prep_threads = (int64_t)a.batch * Npad * a.hq * (a.d / 8);
+    int64_t prep_threads = (int64_t)a.batch * Npad * a.hq * (a.d / 8);
+    if (prep_threads < pp.ncnt) prep_threads = pp.ncnt;
     const dim3 pg((unsigned)((prep_threads + 255) / 256));
     if (a.d == 128) hipLaunchKernelGGL((attn_bwd_prep_kernel<128>), pg, dim3(256), 0, s, pp);
     else hipLaunchKernelGGL((attn_bwd_prep_kernel<64>), pg, dim3(256), 0, s, pp);
@@ -721,6 +887,8 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.ndelta = ndelta;
     kp.dk = static_cast<uint16_t*>(a.dk);
     kp.dv = static_cast<uint16_t*>(a.dv);
+    kp.part = part;
+    kp.cnt = cnt;
     kp.ds0 = a.dos[0]; kp.ds1 = a.dos[1]; kp.ds2 = a.dos[2];
     kp.ks0 = a.ks[0]; kp.ks1 = a.ks[1]; kp.ks2 = a.ks[2];
     kp.vs0 = a.vs[0]; kp.vs1 = a.vs[1]; kp.vs2 = a.vs[2];
@@ -734,9 +902,11 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.B = a.B;
     kp.N = a.N;
     kp.Npad = Npad;
-    kp.bg_count = a.batch * a.hkv;
-    const int kblocks = (a.N + kKeysPerWG - 1) / kKeysPerWG;
-    const dim3 kg((unsigned)((int64_t)kblocks * kp.bg_count));
+    kp.bg_count = bg_count;
+    kp.kblocks = w.kblocks;
+    kp.nch_max = w.nch;
+    kp.tc = w.tc;
+    const dim3 kg((unsigned)((int64_t)w.nch * w.kblocks * bg_count));
     if (a.d == 128) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128>), kg, dim3(kThreadsB), 0, s, kp);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), kg, dim3(kThreadsB), 0, s, kp);
 
@@ -766,7 +936,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     int tN0 = (int)((noisy_row0 + kRowsPerWGB - 1) / kRowsPerWGB);
     if (tN0 > qp.tiles_per_pair) tN0 = qp.tiles_per_pair;
     qp.tN0 = tN0;
-    qp.bg_count = a.batch * a.hkv;
+    qp.bg_count = bg_count;
     qp.scale = a.scale;
     const dim3 qg((unsigned)((int64_t)qp.tiles_per_pair * qp.bg_count));
     if (a.d == 128) hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), qg, dim3(kThreadsB), 0, s, qp);

@@ -121,7 +121,8 @@ int mars_attn_bwd_workspace_bytes(const mars_attn_desc* desc, size_t* bytes) {
     if (st) return st;
     if (!bytes) return MARS_EINVAL;
     if (desc->dtype != MARS_DTYPE_BF16) return MARS_EUNSUPPORTED;
-    *bytes = mars::attn_bwd_workspace_bytes(desc->batch, desc->n_q_heads, (int)attn_N(desc), desc->head_dim);
+    *bytes = mars::attn_bwd_workspace_bytes(desc->batch, desc->n_q_heads, desc->n_kv_heads, desc->head_dim,
+                                            desc->prompt_len, desc->resp_len, desc->block);
     return MARS_OK;
 }
 
@@ -141,7 +142,8 @@ int mars_attn_bwd(const mars_attn_desc* desc, const mars_attn_bwd_strides* gs, c
         !strides_ok(gs->dv_strides, 2))
         return MARS_EINVAL;
     if (gs->do_strides[1] > kMaxKeyPosStride) return MARS_EUNSUPPORTED;
-    const size_t need = mars::attn_bwd_workspace_bytes(desc->batch, desc->n_q_heads, (int)attn_N(desc), desc->head_dim);
+    const size_t need = mars::attn_bwd_workspace_bytes(desc->batch, desc->n_q_heads, desc->n_kv_heads,
+                                                       desc->head_dim, desc->prompt_len, desc->resp_len, desc->block);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MARS_EWORKSPACE;
     mars::AttnBwdArgs a;
     a.q = q;

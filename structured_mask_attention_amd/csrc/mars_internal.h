@@ -43,7 +43,7 @@ struct AttnBwdArgs {
     int batch, hq, hkv, d, P, L, B, N;
     float scale;         // > 0
 };
-size_t attn_bwd_workspace_bytes(int batch, int hq, int N, int d);
+size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int d, int P, int L, int B);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
 
 // Debug mask kernels (mask_kernels.hip).
