@@ -13,7 +13,9 @@ per-kernel durations come from groups of K back-to-back launches of one kernel (
 around each group, three groups, mean).  Three independent
 copies of every input rotate across steps, so a step reads data last touched about 700 MB
 earlier and the 256 MB Infinity Cache holds none of it (no dirty flush traffic either).
-The 7B-shaped and long training layouts are timed as well (own events) and reported.
+The 7B-shaped and long training layouts are timed as well (own events) and reported, and so
+is the training backward (mars_attn_bwd: dQ, dK, dV) on all three layouts (counted as five
+products over the forward's visible tiles).
 The CPU baseline is the fp64 oracle on a bounded sample of the same workloads.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -43,6 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-layouts", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training backward figures")
     ap.add_argument("--copies", type=int, default=3, help="rotated input copies (1 = warm caches)")
     return ap.parse_args()
 
@@ -207,6 +210,44 @@ def main():
     acc_bytes = logits.numel() * 2
     td, tc = float(np.mean(t_dec)), float(np.mean(t_acc))
 
+    def time_backward(s2, sets2, reps=10):
+        """mars_attn_bwd on a training layout: forward outputs (O, LSE) made once per input
+        copy outside the timed region, then `reps` backwards with the same rotation."""
+        ws = torch.empty(M.mars_attn_bwd_workspace_bytes(s2.batch, s2.hq, s2.hkv, s2.d, s2.P, s2.L, s2.B),
+                         dtype=torch.uint8, device=dev)
+        do = I.grad_output(s2).to(dev)
+        fw = []
+        for tq, tk, tv in sets2:
+            lse = torch.empty((s2.batch, s2.hq, s2.N), dtype=torch.float32, device=dev)
+            fw.append((M.mars_attn_fwd(tq, tk, tv, s2.P, s2.L, s2.B, lse=lse), lse))
+        g = [torch.empty_like(sets2[0][0]), torch.empty_like(sets2[0][1]), torch.empty_like(sets2[0][2])]
+
+        def bwd(r):
+            tq, tk, tv = sets2[r % len(sets2)]
+            ob, lb = fw[r % len(sets2)]
+            M.mars_attn_bwd(tq, tk, tv, ob, lb, do, s2.P, s2.L, s2.B, dq=g[0], dk=g[1], dv=g[2], ws=ws)
+        for r in range(3):
+            bwd(r)
+        a3, z3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a3.record(stream)
+        for r in range(reps):
+            bwd(r)
+        z3.record(stream)
+        torch.cuda.synchronize()
+        t3 = a3.elapsed_time(z3) * 1e-3 / reps
+        fvt, falg = train_flops(M, s2)
+        # dQ, dK, dV: five products of the forward's two (S, dP, dV, dK, dQ), same visible tiles
+        out = {"workload": s2.name, "us": t3 * 1e6, "tflops_visible_tile": 2.5 * fvt / t3 / 1e12,
+               "tflops_alg": 2.5 * falg / t3 / 1e12, "frac_of_peak": 2.5 * fvt / t3 / 1e12 / PEAK_BF16_TFLOPS,
+               "workspace_bytes": int(ws.numel())}
+        del ws, do, fw, g
+        return out
+
+    backward = {}
+    if not args.no_backward:
+        backward[st.name] = time_backward(st, train_sets)
+
     # ---- other training layouts (own events, same rotation of input copies) ----
     layouts = {}
     if not args.no_extra_layouts:
@@ -231,6 +272,8 @@ def main():
             fvt, falg = train_flops(M, s2)
             layouts[s2.name] = {"us": t2 * 1e6, "tflops_visible_tile": fvt / t2 / 1e12,
                                 "tflops_alg": falg / t2 / 1e12, "frac_of_peak": fvt / t2 / 1e12 / PEAK_BF16_TFLOPS}
+            if not args.no_backward:
+                backward[s2.name] = time_backward(s2, sets2, reps=4)
             del sets2, q2, o2
         torch.cuda.empty_cache()
 
@@ -275,6 +318,7 @@ def main():
         "train_attn_us": ta * 1e6,
         "train_attn_us_groups": [float(t) * 1e6 for t in t_attn],
         "train_layouts": layouts,
+        "train_backward": backward,
         "wall_s_timed_region": t_wall,
         "input_copies_rotated": ncopy,
     }
