@@ -17,6 +17,8 @@ title and section):
   no mask slots).
 * [TRENDS] aitrends.kr summary of MARS, inference paragraph (at least one token
   is always accepted).
+* [BLOG] section "Inference: a knob, not a mode switch", second finding: a margin
+  gate (how far the top token is ahead, rather than how confident it is).
 
 Readings taken where the pages are silent (each is listed in the design notes):
 
@@ -27,6 +29,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
 * GQA: query head h reads KV head h // (Hq / Hkv).
 * Acceptance uses the temperature-1 softmax over the full vocabulary; the argmax
   tie rule is "lowest index"; tau >= 1 accepts exactly one token.
+* The margin gate's margin is the top-1 minus the top-2 probability of that softmax,
+  where top-2 is the second largest entry of the row counted with multiplicity (a
+  tied maximum gives margin 0); it commits the same way as the probability gate.
 
 Parity status: every public function here is pinned by a ``-m "not gpu"`` test
 (brute-force rule enumeration, the Fig. 2 matrix, closed forms, invariants and
@@ -56,6 +61,8 @@ __all__ = [
     "accept_rows",
     "accept",
     "accept_scalar",
+    "accept_margin",
+    "accept_margin_scalar",
 ]
 
 
@@ -484,3 +491,60 @@ def accept_scalar(logits, tau):
                     break
         n[bi] = max(1, cnt)
     return tokens, pmax, n
+
+
+def accept_margin(logits, tau):
+    """Margin-gate acceptance: logits [b, W, V] -> (tokens, pmax, margin, n).
+
+    Per row, with l1 >= l2 the two largest entries (with multiplicity), m = l1 and
+    S = sum exp(l - m): pmax = 1 / S and margin = (exp(l1 - m) - exp(l2 - m)) / S, the
+    top-1 minus the top-2 probability.  Commit window positions left to right while
+    margin >= tau, stop at the first below, at least one; tau >= 1 commits exactly one.
+    """
+    x = np.asarray(logits, dtype=np.float64)
+    tokens, pmax = accept_rows(x)
+    top2 = np.sort(x, axis=-1)[..., -2:]          # [..., (l2, l1)]
+    l2, l1 = top2[..., 0], top2[..., 1]
+    S = 1.0 / pmax
+    margin = (1.0 - np.exp(l2 - l1)) / S
+    b, W = margin.shape
+    n = np.zeros(b, dtype=np.int32)
+    for bi in range(b):
+        run = 0
+        if tau < 1.0:
+            while run < W and margin[bi, run] >= tau:
+                run += 1
+        n[bi] = max(1, run)
+    return tokens, pmax, margin, n
+
+
+def accept_margin_scalar(logits, tau):
+    """Loop form of :func:`accept_margin` (tiny vocabularies): one pass keeping the two
+    largest entries, compensated summation for S."""
+    x = np.asarray(logits, dtype=np.float64)
+    b, W, V = x.shape
+    tokens = np.zeros((b, W), dtype=np.int32)
+    margin = np.zeros((b, W))
+    n = np.zeros(b, dtype=np.int32)
+    for bi in range(b):
+        for i in range(W):
+            row = [float(t) for t in x[bi, i]]
+            best, arg, second = row[0], 0, -math.inf
+            for vi in range(1, V):
+                t = row[vi]
+                if t > best:
+                    best, second, arg = t, best, vi
+                elif t > second:
+                    second = t
+            tokens[bi, i] = arg
+            S = math.fsum(math.exp(t - best) for t in row)
+            margin[bi, i] = (1.0 - (math.exp(second - best) if V > 1 else 0.0)) / S
+        cnt = 0
+        if tau < 1.0:
+            for i in range(W):
+                if margin[bi, i] >= tau:
+                    cnt += 1
+                else:
+                    break
+        n[bi] = max(1, cnt)
+    return tokens, margin, n

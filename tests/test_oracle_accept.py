@@ -82,3 +82,51 @@ def test_matches_scalar_and_torch_softmax():
     sm = torch.softmax(torch.from_numpy(x), -1)
     assert np.max(np.abs(sm.max(-1).values.numpy() - pmax)) <= 1e-15
     assert np.array_equal(sm.argmax(-1).numpy(), tok)
+
+
+# ---------------------------------------------------------------------------
+# Margin gate (top-1 minus top-2 probability)
+# ---------------------------------------------------------------------------
+
+def test_margin_matches_scalar_brute_force():
+    rng = np.random.default_rng(71)
+    for V in (2, 3, 7, 33):
+        x = np.round(rng.standard_normal((3, 4, V)) * 2, 1)   # coarse values: ties happen
+        t, pm, mg, n = O.accept_margin(x, 0.3)
+        t2, mg2, n2 = O.accept_margin_scalar(x, 0.3)
+        assert np.array_equal(t, t2) and np.array_equal(n, n2)
+        assert np.max(np.abs(mg - mg2)) < 1e-12
+        # brute force: sort the probabilities
+        p = np.exp(x - x.max(axis=-1, keepdims=True))
+        p /= p.sum(axis=-1, keepdims=True)
+        ps = np.sort(p, axis=-1)
+        assert np.max(np.abs(mg - (ps[..., -1] - ps[..., -2]))) < 1e-12
+
+
+def test_margin_closed_forms():
+    V = 1000
+    # one spike of height h over zeros: p1 = e^h / (e^h + V - 1), p2 = 1 / (e^h + V - 1)
+    for h in (0.5, 3.0, 12.0):
+        x = np.zeros((1, 1, V))
+        x[0, 0, 17] = h
+        t, pm, mg, n = O.accept_margin(x, 0.5)
+        den = math.exp(h) + V - 1
+        assert t[0, 0] == 17 and abs(mg[0, 0] - (math.exp(h) - 1) / den) < 1e-12
+    # a tied maximum (two equal top entries) has margin exactly 0; a constant row too
+    x = np.zeros((1, 2, V))
+    x[0, 0, [5, 9]] = 4.0
+    t, pm, mg, n = O.accept_margin(x, 1e-9)
+    assert mg[0, 0] == 0.0 and mg[0, 1] == 0.0 and t[0, 0] == 5 and n[0] == 1
+
+
+def test_margin_gate_prefix_and_tau_one():
+    V = 50
+    x = np.zeros((2, 4, V))
+    for i, h in enumerate((30.0, 30.0, 0.1, 30.0)):   # margins ~1, ~1, small, ~1
+        x[:, i, 3] = h
+    _, _, mg, n = O.accept_margin(x, 0.9)
+    assert list(n) == [2, 2]                           # stops at the first small margin
+    _, _, _, n1 = O.accept_margin(x, 1.0)
+    assert list(n1) == [1, 1]                          # exact AR fallback
+    _, _, _, n0 = O.accept_margin(x, 1e-12)
+    assert list(n0) == [4, 4]                          # every margin is > 0 here
