@@ -503,8 +503,9 @@ def accept_margin(logits, tau):
     """
     x = np.asarray(logits, dtype=np.float64)
     tokens, pmax = accept_rows(x)
-    top2 = np.sort(x, axis=-1)[..., -2:]          # [..., (l2, l1)]
-    l2, l1 = top2[..., 0], top2[..., 1]
+    srt = np.sort(x, axis=-1)
+    l1 = srt[..., -1]
+    l2 = srt[..., -2] if x.shape[-1] > 1 else np.full_like(l1, -np.inf)   # one entry: no top-2
     S = 1.0 / pmax
     margin = (1.0 - np.exp(l2 - l1)) / S
     b, W = margin.shape

@@ -117,6 +117,11 @@ def test_margin_closed_forms():
     x[0, 0, [5, 9]] = 4.0
     t, pm, mg, n = O.accept_margin(x, 1e-9)
     assert mg[0, 0] == 0.0 and mg[0, 1] == 0.0 and t[0, 0] == 5 and n[0] == 1
+    # a one-entry vocabulary has no second entry: margin = top-1 probability = 1
+    t, pm, mg, n = O.accept_margin(np.full((1, 3, 1), 2.0), 0.999)
+    assert np.all(mg == 1.0) and np.all(t == 0) and n[0] == 3
+    t2, mg2, n2 = O.accept_margin_scalar(np.full((1, 3, 1), 2.0), 0.999)
+    assert np.all(mg2 == 1.0) and n2[0] == 3
 
 
 def test_margin_gate_prefix_and_tau_one():
