@@ -6,7 +6,8 @@ One step = one pass of the whole path on synthetic, seeded inputs resident in HB
      head_dim 64, P=256, L=512, B=4)                          -> visible-tile TFLOP/s;
   2. mars_decode_step on the Qwen2.5-7B-shaped decode workload (32 sequences, 28/4 heads,
      head_dim 128, cache lengths U[512, 4096], 4 window rows)  -> GB/s;
-  3. mars_accept on its logits [32, 4, 152064] at tau = 0.95   -> GB/s;
+  3. mars_accept on its logits [32, 4, 152064] at tau = 0.95   -> GB/s (the margin gate,
+     mars_accept_margin, is timed beside it and reported in the decode section);
   decode tokens/s = sum(n_accept) / (t_decode + t_accept)  (one attention layer + accept).
 The timed region is exactly K whole steps (HIP events at its ends, on the launch stream);
 per-kernel durations come from groups of K back-to-back launches of one kernel (events
@@ -36,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "visible-tile TFLOP/s (train layout) + decode-step tokens/s at τ=0.95, 1 GPU"
+MARGIN_TAU = 0.3              # margin-gate threshold for its timing line (the pages give no value)
 
 
 def parse():
@@ -196,7 +198,15 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(z) * 1e-3 / args.steps
 
+    mgn = torch.empty((sd.batch, sd.W), dtype=torch.float32, device=dev)
+
+    def accept_margin(i):
+        M.mars_accept_margin(dec_sets[i % ncopy][6], MARGIN_TAU, ws=aws, tokens=tok, pmax=pmx, margin=mgn,
+                             n_accept=nacc)
+
     reps = [(group(attn), group(decode), group(accept)) for _ in range(3)]
+    t_mgn = float(np.mean([group(accept_margin) for _ in range(3)]))
+    accept(0)   # leave the probability gate's n_accept in place for the tokens/s figure
     t_attn = np.array([r[0] for r in reps])
     t_dec = np.array([r[1] for r in reps])
     t_acc = np.array([r[2] for r in reps])
@@ -313,6 +323,8 @@ def main():
             "decode_us": td * 1e6, "accept_us": tc * 1e6,
             "decode_GBps": dec_bytes / td / 1e9, "decode_frac_hbm": dec_bytes / td / 1e9 / PEAK_HBM_GBS,
             "accept_GBps": acc_bytes / tc / 1e9, "accept_frac_hbm": acc_bytes / tc / 1e9 / PEAK_HBM_GBS,
+            "accept_margin_us": t_mgn * 1e6, "accept_margin_GBps": acc_bytes / t_mgn / 1e9,
+            "accept_margin_tau": MARGIN_TAU,
             "cpu_baseline": cpu_dec,
         },
         "train_attn_us": ta * 1e6,

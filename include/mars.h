@@ -12,7 +12,9 @@
  *                       the window itself;
  *   - mars_accept:      the confidence-threshold rule of the MARS author blog, section
  *                       "Inference: a knob, not a mode switch": commit window positions
- *                       left to right while the top-1 probability is >= tau, at least one.
+ *                       left to right while the top-1 probability is >= tau, at least one;
+ *   - mars_accept_margin: the same rule gated on the top-1 minus top-2 probability margin
+ *                       (the blog's margin gate).
  *
  * Conventions (all entry points):
  *   - Every call returns an int status: MARS_OK (0) or a negative MARS_E* code.
@@ -259,6 +261,20 @@ int mars_accept_workspace_bytes(const mars_accept_desc* desc, size_t* bytes);
  */
 int mars_accept(const mars_accept_desc* desc, const void* logits, int32_t* tokens, float* pmax,
                 int32_t* n_accept, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Margin gate (MARS author blog, "Inference: a knob, not a mode switch", second finding:
+ * gate on how far the top token is ahead rather than on how confident it is).  Per row,
+ * with l1 >= l2 the two largest logits counted with multiplicity (a tied maximum gives
+ * l2 = l1) and S = sum_v exp(l_v - l1):
+ *   margin = top-1 minus top-2 probability = (1 - exp(l2 - l1)) / S   (in [0, 1)),
+ * and n_accept[b] = the leading run of rows with margin >= desc->tau, at least one
+ * (tau >= 1: exactly one, exact AR decoding).  tokens as mars_accept; pmax (optional,
+ * may be NULL) = 1 / S; margin fp32 [batch][window].  Same descriptor, workspace size and
+ * errors as mars_accept.
+ */
+int mars_accept_margin(const mars_accept_desc* desc, const void* logits, int32_t* tokens, float* pmax,
+                       float* margin, int32_t* n_accept, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ __all__ = [
     "mars_decode_step",
     "mars_accept_workspace_bytes",
     "mars_accept",
+    "mars_accept_margin",
 ]
 
 
@@ -281,3 +282,25 @@ def mars_accept(logits, tau, ws=None, tokens=None, pmax=None, n_accept=None):
     _check(L.load().mars_accept(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(pmax), _ptr(n_accept),
                                 _ptr(ws), ws.numel(), _stream(logits)), "mars_accept")
     return tokens, pmax, n_accept
+
+
+def mars_accept_margin(logits, tau, ws=None, tokens=None, pmax=None, margin=None, n_accept=None):
+    """Margin gate: logits bf16 [b, W, V] -> (tokens, pmax, margin fp32 [b,W], n_accept [b]).
+
+    margin = top-1 minus top-2 probability; n_accept = leading run with margin >= tau, at
+    least one.  ``ws``: optional device workspace (uint8, at least mars_accept_workspace_bytes).
+    """
+    b, W, V = logits.shape
+    if logits.stride(-1) != 1:
+        raise ValueError("vocab dimension must be contiguous")
+    desc = accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1))
+    dev = logits.device
+    tokens = torch.empty((b, W), dtype=torch.int32, device=dev) if tokens is None else tokens
+    pmax = torch.empty((b, W), dtype=torch.float32, device=dev) if pmax is None else pmax
+    margin = torch.empty((b, W), dtype=torch.float32, device=dev) if margin is None else margin
+    n_accept = torch.empty((b,), dtype=torch.int32, device=dev) if n_accept is None else n_accept
+    if ws is None:
+        ws = torch.empty(max(mars_accept_workspace_bytes(b, W, V, tau), 16), dtype=torch.uint8, device=dev)
+    _check(L.load().mars_accept_margin(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(pmax), _ptr(margin),
+                                       _ptr(n_accept), _ptr(ws), ws.numel(), _stream(logits)), "mars_accept_margin")
+    return tokens, pmax, margin, n_accept

@@ -69,6 +69,7 @@ _SIGNATURES = {
     "mars_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "mars_accept_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_accept": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), P, P, P, P, P, ctypes.c_size_t, P]),
+    "mars_accept_margin": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), P, P, P, P, P, P, ctypes.c_size_t, P]),
 }
 
 _lib = None

@@ -2,6 +2,10 @@
 // switch"; greedy decoding): per window row the argmax (lowest index on ties) and the
 // top-1 probability pmax = 1 / sum_v exp(l_v - max); per sequence the length of the
 // leading run of rows with pmax >= tau, at least one (tau >= 1: exactly one).
+// The margin gate (same blog section: how far the top token is ahead) gates on
+// margin = top-1 minus top-2 probability = (1 - exp(l2 - l1)) / sum_v exp(l_v - l1), with
+// l2 the second largest entry counted with multiplicity; the slice kernel then also keeps
+// each thread's two largest entries (v_med3 / v_max per entry).
 //
 // Two launches on the caller's stream; the kernel boundary orders them, so no device-scope
 // fences or counters are needed and the workspace needs no initialisation.
@@ -36,7 +40,8 @@ struct AcceptKParams {
     int32_t* tokens;
     float* pmax;
     int32_t* n_accept;
-    float4* partial;     // [batch*W][split]: (max, sum, index bits, unused)
+    float4* partial;     // [batch*W][split]: (max, sum, index bits, second largest)
+    float* margin;       // margin gate only (may be null otherwise)
     int64_t bstride, rstride;
     int W, V, split;
     float tau;
@@ -46,14 +51,17 @@ struct Part {
     float m;
     float s;
     int idx;
+    float m2;            // second largest entry with multiplicity (margin gate; else -inf)
 };
 
-// Merge two (max, lowest argmax, sum of exp relative to max) triples (branch-free).
+// Merge two (max, lowest argmax, sum of exp relative to max, second largest) tuples
+// (branch-free).  The union's second largest is the smaller maximum or the larger second.
 __device__ inline Part merge(Part a, Part b) {
     const bool bw = b.m > a.m || (b.m == a.m && b.idx < a.idx);
     Part r;
     r.m = bw ? b.m : a.m;
     r.idx = bw ? b.idx : a.idx;
+    r.m2 = fmaxf(fminf(a.m, b.m), fmaxf(a.m2, b.m2));
     const float lo_m = bw ? a.m : b.m;
     const float lo_s = bw ? a.s : b.s;
     const float hi_s = bw ? b.s : a.s;
@@ -64,7 +72,8 @@ __device__ inline Part merge(Part a, Part b) {
 
 template <int CTRL>
 __device__ inline Part dpp_part(Part x) {
-    return Part{dpp_f32<CTRL>(x.m), dpp_f32<CTRL>(x.s), __float_as_int(dpp_f32<CTRL>(__int_as_float(x.idx)))};
+    return Part{dpp_f32<CTRL>(x.m), dpp_f32<CTRL>(x.s), __float_as_int(dpp_f32<CTRL>(__int_as_float(x.idx))),
+                dpp_f32<CTRL>(x.m2)};
 }
 
 // merge() is symmetric in its arguments, so each step may pair lanes by any involution:
@@ -79,15 +88,17 @@ __device__ inline Part wave_reduce(Part x) {
         auto m = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.m), __float_as_uint(x.m), false, false);
         auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.s), __float_as_uint(x.s), false, false);
         auto i = __builtin_amdgcn_permlane16_swap((uint32_t)x.idx, (uint32_t)x.idx, false, false);
-        x = merge(Part{__uint_as_float(m[0]), __uint_as_float(s[0]), (int)i[0]},
-                  Part{__uint_as_float(m[1]), __uint_as_float(s[1]), (int)i[1]});
+        auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.m2), __float_as_uint(x.m2), false, false);
+        x = merge(Part{__uint_as_float(m[0]), __uint_as_float(s[0]), (int)i[0], __uint_as_float(t[0])},
+                  Part{__uint_as_float(m[1]), __uint_as_float(s[1]), (int)i[1], __uint_as_float(t[1])});
     }
     {
         auto m = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.m), __float_as_uint(x.m), false, false);
         auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.s), __float_as_uint(x.s), false, false);
         auto i = __builtin_amdgcn_permlane32_swap((uint32_t)x.idx, (uint32_t)x.idx, false, false);
-        x = merge(Part{__uint_as_float(m[0]), __uint_as_float(s[0]), (int)i[0]},
-                  Part{__uint_as_float(m[1]), __uint_as_float(s[1]), (int)i[1]});
+        auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.m2), __float_as_uint(x.m2), false, false);
+        x = merge(Part{__uint_as_float(m[0]), __uint_as_float(s[0]), (int)i[0], __uint_as_float(t[0])},
+                  Part{__uint_as_float(m[1]), __uint_as_float(s[1]), (int)i[1], __uint_as_float(t[1])});
     }
     return x;
 }
@@ -146,7 +157,8 @@ __device__ inline void finish_chunk(int v0, int v1, int c, int tid, uint32_t (&w
 }
 
 // RAGGED: V is not a multiple of 8, so the last vector of a row is read entry by entry.
-template <bool RAGGED>
+// TOP2: also keep the second largest entry (margin gate).
+template <bool RAGGED, bool TOP2>
 __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p) {
     __shared__ Part red[kThreads / 64];
 
@@ -161,7 +173,9 @@ __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p)
     // are then reduced in order as their data arrives, into this thread's running (max,
     // lowest argmax, sum).  sched_barrier keeps the compiler from hoisting any use of the
     // loaded words above the later loads (which would wait for the data and serialise them).
-    Part x{-INFINITY, 0.f, 0x7fffffff};
+    Part x{-INFINITY, 0.f, 0x7fffffff, -INFINITY};
+    // Two independent (largest, second largest) chains over even / odd entries (TOP2).
+    float ta1 = -INFINITY, ta2 = -INFINITY, tb1 = -INFINITY, tb2 = -INFINITY;
     uint32_t w[kChunks][kVecPerChunk][4];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) load_chunk<RAGGED>(rowp, v0, v1, c, tid, w[c]);
@@ -197,6 +211,19 @@ __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p)
             x.s *= __builtin_amdgcn_exp2f((x.m - cm) * kLog2e);
             x.m = cm;
         }
+        if constexpr (TOP2) {
+#pragma unroll
+            for (int k = 0; k < kVecPerChunk; ++k) {
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float va = entry(w[k], e), vb = entry(w[k], e + 1);
+                    ta2 = __builtin_amdgcn_fmed3f(ta1, va, ta2);
+                    ta1 = fmaxf(ta1, va);
+                    tb2 = __builtin_amdgcn_fmed3f(tb1, vb, tb2);
+                    tb1 = fmaxf(tb1, vb);
+                }
+            }
+        }
         if (x.m != -INFINITY) {
             const float mb = x.m * kLog2e;
             float s0 = 0.f, s1 = 0.f;
@@ -213,6 +240,7 @@ __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p)
     };
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) reduce_chunk(c, w[c]);
+    if constexpr (TOP2) x.m2 = fmaxf(fminf(ta1, tb1), fmaxf(ta2, tb2));
 
     x = wave_reduce(x);
     if (lane == 0) red[wave] = x;
@@ -221,35 +249,44 @@ __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p)
         Part y = red[0];
 #pragma unroll
         for (int k = 1; k < kThreads / 64; ++k) y = merge(y, red[k]);
-        p.partial[(int64_t)row * p.split + sl] = float4{y.m, y.s, __int_as_float(y.idx), 0.f};
+        p.partial[(int64_t)row * p.split + sl] = float4{y.m, y.s, __int_as_float(y.idx), y.m2};
     }
 }
 
 // One workgroup per sequence: one wave per row, lanes over slices (fixed merge order).
+// MARGIN: gate on the top-1 minus top-2 probability instead of the top-1 probability.
+template <bool MARGIN>
 __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptKParams p) {
-    __shared__ float row_pmax[kMaxWindow];
+    __shared__ float row_gate[kMaxWindow];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int r = wave; r < p.W; r += kThreads / 64) {
-        Part y{-INFINITY, 0.f, 0x7fffffff};
+        Part y{-INFINITY, 0.f, 0x7fffffff, -INFINITY};
         const float4* pr = p.partial + ((int64_t)b * p.W + r) * p.split;
         for (int s2 = lane; s2 < p.split; s2 += 64) {
             const float4 q = pr[s2];
-            y = merge(y, Part{q.x, q.y, __float_as_int(q.z)});
+            y = merge(y, Part{q.x, q.y, __float_as_int(q.z), q.w});
         }
         y = wave_reduce(y);
         if (lane == 0) {
             const float pm = 1.f / y.s;
-            row_pmax[r] = pm;
             p.tokens[(int64_t)b * p.W + r] = y.idx;
-            p.pmax[(int64_t)b * p.W + r] = pm;
+            if (p.pmax) p.pmax[(int64_t)b * p.W + r] = pm;
+            if constexpr (MARGIN) {
+                // p1 - p2 = (1 - e^(l2 - l1)) / S (0 for a tied maximum)
+                const float mg = (1.f - expf(y.m2 - y.m)) * pm;
+                row_gate[r] = mg;
+                p.margin[(int64_t)b * p.W + r] = mg;
+            } else {
+                row_gate[r] = pm;
+            }
         }
     }
     __syncthreads();
     if (tid == 0) {
         int n = 0;
         if (p.tau < 1.f) {
-            while (n < p.W && row_pmax[n] >= p.tau) ++n;
+            while (n < p.W && row_gate[n] >= p.tau) ++n;
         }
         p.n_accept[b] = n > 1 ? n : 1;
     }
@@ -277,12 +314,20 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t s) {
     p.V = a.V;
     p.split = accept_split(a.V);
     p.tau = a.tau;
+    p.margin = a.margin;
     const dim3 grid((unsigned)(a.batch * a.W), (unsigned)p.split);
-    if (a.V % 8 == 0) hipLaunchKernelGGL(accept_slice_kernel<false>, grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL(accept_slice_kernel<true>, grid, dim3(kThreads), 0, s, p);
+    const bool ragged = a.V % 8 != 0;
+    if (a.margin) {
+        if (!ragged) hipLaunchKernelGGL((accept_slice_kernel<false, true>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((accept_slice_kernel<true, true>), grid, dim3(kThreads), 0, s, p);
+    } else {
+        if (!ragged) hipLaunchKernelGGL((accept_slice_kernel<false, false>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((accept_slice_kernel<true, false>), grid, dim3(kThreads), 0, s, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(accept_finish_kernel, dim3((unsigned)a.batch), dim3(kThreads), 0, s, p);
+    if (a.margin) hipLaunchKernelGGL(accept_finish_kernel<true>, dim3((unsigned)a.batch), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL(accept_finish_kernel<false>, dim3((unsigned)a.batch), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -365,6 +365,37 @@ int mars_accept(const mars_accept_desc* desc, const void* logits, int32_t* token
     a.logits = logits;
     a.tokens = tokens;
     a.pmax = pmax;
+    a.margin = nullptr;
+    a.n_accept = n_accept;
+    a.ws = ws;
+    a.batch_stride = desc->batch_stride;
+    a.row_stride = desc->row_stride;
+    a.batch = desc->batch;
+    a.W = desc->window;
+    a.V = desc->vocab;
+    a.tau = desc->tau;
+    return map_hip(mars::launch_accept(a, stream));
+}
+
+int mars_accept_margin(const mars_accept_desc* desc, const void* logits, int32_t* tokens, float* pmax,
+                       float* margin, int32_t* n_accept, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_accept_desc(desc);
+    if (st) return st;
+    if (desc->batch == 0) return MARS_OK;
+    if (!logits || !tokens || !margin || !n_accept) return MARS_EINVAL;
+    if (desc->batch_stride < 0 || desc->row_stride < 0 || desc->batch_stride % 8 || desc->row_stride % 8)
+        return MARS_EINVAL;
+    if (!aligned16(logits) || (reinterpret_cast<uintptr_t>(tokens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(pmax) & 3u) || (reinterpret_cast<uintptr_t>(margin) & 3u) ||
+        (reinterpret_cast<uintptr_t>(n_accept) & 3u))
+        return MARS_EINVAL;
+    const size_t need = mars::accept_workspace_bytes(desc->batch, desc->window, desc->vocab);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MARS_EWORKSPACE;
+    mars::AcceptArgs a;
+    a.logits = logits;
+    a.tokens = tokens;
+    a.pmax = pmax;
+    a.margin = margin;
     a.n_accept = n_accept;
     a.ws = ws;
     a.batch_stride = desc->batch_stride;

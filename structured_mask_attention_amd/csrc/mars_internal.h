@@ -75,7 +75,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 struct AcceptArgs {
     const void* logits;
     int32_t* tokens;
-    float* pmax;
+    float* pmax;         // may be null for the margin gate
+    float* margin;       // non-null: margin gate (gate on top-1 minus top-2 probability)
     int32_t* n_accept;
     void* ws;
     int64_t batch_stride, row_stride;

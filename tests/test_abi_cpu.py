@@ -198,6 +198,28 @@ def test_accept_validation_errors():
     assert call(d, ptr=None, ws=None) == L.MARS_OK
 
 
+def test_accept_margin_validation_errors():
+    lib = L.load()
+    good = lambda: M.accept_desc(32, 4, 152064, 0.3)
+
+    def call(d, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE, pmax=FAKE, margin=FAKE):
+        return lib.mars_accept_margin(ctypes.byref(d), ptr, ptr, pmax, margin, ptr, ws, ws_bytes, None)
+
+    for field, val, code in [("tau", 0.0, L.MARS_EINVAL), ("min_accept", 2, L.MARS_EINVAL),
+                             ("window", 65, L.MARS_EUNSUPPORTED), ("dtype", L.MARS_DTYPE_FP32, L.MARS_EUNSUPPORTED)]:
+        d = good()
+        setattr(d, field, val)
+        assert call(d) == code, field
+    assert call(good(), margin=None) == L.MARS_EINVAL          # margin output is required
+    assert call(good(), margin=FAKE + 2) == L.MARS_EINVAL
+    assert call(good(), pmax=FAKE + 2) == L.MARS_EINVAL
+    assert call(good(), ptr=None) == L.MARS_EINVAL
+    need = M.mars_accept_workspace_bytes(32, 4, 152064)
+    assert call(good(), ws_bytes=need - 1) == L.MARS_EWORKSPACE
+    d = good(); d.batch = 0
+    assert call(d, ptr=None, ws=None, pmax=None, margin=None) == L.MARS_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
