@@ -18,7 +18,10 @@ title and section):
 * [TRENDS] aitrends.kr summary of MARS, inference paragraph (at least one token
   is always accepted).
 * [BLOG] section "Inference: a knob, not a mode switch", second finding: a margin
-  gate (how far the top token is ahead, rather than how confident it is).
+  gate (how far the top token is ahead, rather than how confident it is); and
+  "Batching is where methods like this usually die": the block-level KV cache that
+  advances at the batch-minimum acceptance, and the deferred-KV sampler with
+  per-sample cursors and a cache-validity bitmask.
 
 Readings taken where the pages are silent (each is listed in the design notes):
 
@@ -29,6 +32,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
 * GQA: query head h reads KV head h // (Hq / Hkv).
 * Acceptance uses the temperature-1 softmax over the full vocabulary; the argmax
   tie rule is "lowest index"; tau >= 1 accepts exactly one token.
+* KV commit: the accepted window rows 0..n-1 of a sequence are appended to its cache
+  at its cursor, and the cursor advances by n; the per-sample policy uses each
+  sequence's own n, the batch-minimum policy min over the batch for every sequence;
+  a sequence whose cache cannot hold n more rows commits none and reports it; the
+  validity bitmask of a sequence has bit i set iff window row i was committed.
 * The margin gate's margin is the top-1 minus the top-2 probability of that softmax,
   where top-2 is the second largest entry of the row counted with multiplicity (a
   tied maximum gives margin 0); it commits the same way as the probability gate.
@@ -63,6 +71,7 @@ __all__ = [
     "accept_scalar",
     "accept_margin",
     "accept_margin_scalar",
+    "kv_commit",
 ]
 
 
@@ -549,3 +558,41 @@ def accept_margin_scalar(logits, tau):
                     break
         n[bi] = max(1, cnt)
     return tokens, margin, n
+
+
+# ---------------------------------------------------------------------------
+# KV commit and cursor advance ([BLOG] "Batching is where methods like this usually die")
+# ---------------------------------------------------------------------------
+
+def kv_commit(k_cache, v_cache, cache_len, k_win, v_win, n_accept, batch_min=False):
+    """Append accepted window K/V to per-sequence caches and advance the cursors.
+
+    k_cache, v_cache [b, Hkv, cap, D]; cache_len [b]; k_win, v_win [b, W, Hkv, D];
+    n_accept [b] in [1, W].  n_b = n_accept[b] (per-sample cursors), or min_b n_accept
+    for every sequence (the block-level cache advancing at the batch minimum).  If
+    cache_len[b] + n_b > cap nothing is committed for b.  Returns (k_cache', v_cache',
+    cache_len', valid [b] bitmask of committed window rows, overflow [b] bool).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    ln = np.array(cache_len, dtype=np.int64, copy=True)
+    b, Hkv, cap, D = kc.shape
+    W = k_win.shape[1]
+    n_acc = np.asarray(n_accept, dtype=np.int64)
+    nmin = int(n_acc.min()) if b else 0
+    valid = np.zeros(b, dtype=np.uint64)
+    over = np.zeros(b, dtype=bool)
+    for bi in range(b):
+        n = nmin if batch_min else int(n_acc[bi])
+        n = max(0, min(n, W))
+        start = int(ln[bi])
+        if start + n > cap:
+            over[bi] = True
+            continue
+        for i in range(n):
+            for g in range(Hkv):
+                kc[bi, g, start + i, :] = k_win[bi, i, g, :]
+                vc[bi, g, start + i, :] = v_win[bi, i, g, :]
+            valid[bi] |= np.uint64(1) << np.uint64(i)
+        ln[bi] = start + n
+    return kc, vc, ln.astype(np.int32), valid, over

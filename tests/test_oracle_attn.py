@@ -293,3 +293,50 @@ def test_attn_bwd_row_and_key_subsets():
     sq, sk, sv = O.attn_bwd(q, k, v, do, P, L, B, rows=rows, keys=keys)
     assert np.max(np.abs(sq - dq[:, rows])) < 1e-13
     assert np.max(np.abs(sk - dk[:, keys])) < 1e-13 and np.max(np.abs(sv - dv[:, keys])) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# KV commit and cursor advance
+# ---------------------------------------------------------------------------
+
+def test_kv_commit_per_sample_and_batch_min():
+    b, Hkv, cap, D, W = 3, 2, 10, 4, 4
+    kc, vc = rand((b, Hkv, cap, D), 51), rand((b, Hkv, cap, D), 52)
+    kw, vw = rand((b, W, Hkv, D), 53), rand((b, W, Hkv, D), 54)
+    ln = np.array([0, 5, 8], dtype=np.int32)
+    nacc = np.array([3, 1, 4], dtype=np.int32)
+    k2, v2, l2, valid, over = O.kv_commit(kc, vc, ln, kw, vw, nacc)
+    # sequence 0: rows 0..2 at 0..2; sequence 1: row 0 at 5; sequence 2: 8 + 4 > 10 -> nothing
+    assert l2.tolist() == [3, 6, 8] and over.tolist() == [False, False, True]
+    assert valid.tolist() == [0b111, 0b1, 0]
+    assert np.array_equal(k2[0, :, 0:3], kw[0, 0:3].transpose(1, 0, 2))
+    assert np.array_equal(v2[1, :, 5], vw[1, 0])
+    untouched = np.ones((b, Hkv, cap), dtype=bool)
+    untouched[0, :, 0:3] = False
+    untouched[1, :, 5] = False
+    assert np.array_equal(k2[untouched], kc[untouched]) and np.array_equal(v2[untouched], vc[untouched])
+    # batch minimum: every sequence advances by min n = 1
+    k3, v3, l3, valid3, over3 = O.kv_commit(kc, vc, ln, kw, vw, nacc, batch_min=True)
+    assert l3.tolist() == [1, 6, 9] and valid3.tolist() == [1, 1, 1] and not over3.any()
+    assert np.array_equal(k3[2, :, 8], kw[2, 0])
+
+
+def test_kv_commit_then_decode_equals_decode_over_longer_cache():
+    """Committing window rows 0..n-1 and decoding a new window equals one decode whose
+    cache already held them (the cursor semantics the decode step relies on)."""
+    b, Hq, Hkv, cap, D, W = 2, 4, 2, 16, 8, 3
+    kc, vc = rand((b, Hkv, cap, D), 61), rand((b, Hkv, cap, D), 62)
+    ln = np.array([4, 7], dtype=np.int32)
+    kw, vw = rand((b, W, Hkv, D), 63), rand((b, W, Hkv, D), 64)
+    k2, v2, l2, _, _ = O.kv_commit(kc, vc, ln, kw, vw, np.array([2, 3]))
+    qn, kn, vn = rand((b, W, Hq, D), 65), rand((b, W, Hkv, D), 66), rand((b, W, Hkv, D), 67)
+    got = O.decode(qn, kn, vn, k2, v2, l2)
+    for bi in range(b):
+        n = int(l2[bi])
+        # reference: the same cache built by hand
+        kref, vref = kc.copy(), vc.copy()
+        m = n - int(ln[bi])
+        kref[bi, :, ln[bi]:n] = kw[bi, :m].transpose(1, 0, 2)
+        vref[bi, :, ln[bi]:n] = vw[bi, :m].transpose(1, 0, 2)
+        ref = O.decode(qn[bi:bi + 1], kn[bi:bi + 1], vn[bi:bi + 1], kref[bi:bi + 1], vref[bi:bi + 1], l2[bi:bi + 1])
+        assert np.array_equal(got[bi:bi + 1], ref)
