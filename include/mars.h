@@ -14,7 +14,9 @@
  *                       "Inference: a knob, not a mode switch": commit window positions
  *                       left to right while the top-1 probability is >= tau, at least one;
  *   - mars_accept_margin: the same rule gated on the top-1 minus top-2 probability margin
- *                       (the blog's margin gate).
+ *                       (the blog's margin gate);
+ *   - mars_kv_commit:   append the accepted window K/V to the caches and advance the
+ *                       per-sequence cursors (or all at the batch minimum).
  *
  * Conventions (all entry points):
  *   - Every call returns an int status: MARS_OK (0) or a negative MARS_E* code.
@@ -229,6 +231,30 @@ int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void
                      const void* v_win, const void* k_cache, const void* v_cache,
                      const int32_t* cache_len, void* o, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * KV commit and cursor advance (MARS author blog, "Batching is where methods like this
+ * usually die": the block-level KV cache advancing at the batch-minimum acceptance, and
+ * the deferred-KV sampler with per-sample cursors and a cache-validity bitmask).
+ *
+ * After acceptance, sequence b appends window rows 0..n_b-1 of k_win / v_win (the K and
+ * V of its proposal forward) to k_cache / v_cache at positions cache_len[b] .. +n_b - 1
+ * and advances cache_len[b] by n_b, where
+ *   n_b = n_accept[b]                      (MARS_COMMIT_PER_SAMPLE: per-sample cursors)
+ *   n_b = min over the batch of n_accept   (MARS_COMMIT_BATCH_MIN: the block cache)
+ * clamped to [0, window].  If cache_len[b] + n_b > cache_capacity nothing is committed
+ * for b (overflow[b] = 1).  valid (optional, uint64 [batch]): bit i set iff window row
+ * i of b was committed.  overflow (optional, int32 [batch]).
+ * desc: the decode step's descriptor (window, cache and window strides, head_dim); the q
+ * and o strides and the scale are not used.  n_accept and cache_len are device int32
+ * [batch] (cache_len is read, clamped to [0, cache_capacity], and rewritten).  The window
+ * tensors must not overlap the caches.  One launch, no workspace.
+ * ------------------------------------------------------------------------------------ */
+#define MARS_COMMIT_PER_SAMPLE 0
+#define MARS_COMMIT_BATCH_MIN 1
+int mars_kv_commit(const mars_decode_desc* desc, const void* k_win, const void* v_win, const int32_t* n_accept,
+                   void* k_cache, void* v_cache, int32_t* cache_len, uint64_t* valid, int32_t* overflow,
+                   int32_t policy, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * Confidence-threshold acceptance (MARS author blog, "Inference: a knob, not a mode

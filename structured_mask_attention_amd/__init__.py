@@ -29,6 +29,7 @@ __all__ = [
     "mars_accept_workspace_bytes",
     "mars_accept",
     "mars_accept_margin",
+    "mars_kv_commit",
 ]
 
 
@@ -304,3 +305,20 @@ def mars_accept_margin(logits, tau, ws=None, tokens=None, pmax=None, margin=None
     _check(L.load().mars_accept_margin(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(pmax), _ptr(margin),
                                        _ptr(n_accept), _ptr(ws), ws.numel(), _stream(logits)), "mars_accept_margin")
     return tokens, pmax, margin, n_accept
+
+
+def mars_kv_commit(k_win, v_win, n_accept, k_cache, v_cache, cache_len, batch_min=False, valid=None, overflow=None):
+    """Append accepted window K/V ([b, W, Hkv, D]) to the caches ([b, Hkv, cap, D]) at the
+    cursors ``cache_len`` (int32 [b], updated in place) and advance them by n_accept[b]
+    (or the batch minimum).  Returns (valid uint64-as-int64 [b], overflow int32 [b])."""
+    b, W, hkv, d = k_win.shape
+    cap = k_cache.shape[2]
+    desc = decode_desc(b, hkv, hkv, d, W, cap, 0.0, None, k_win, v_win, k_cache, v_cache, None)
+    dev = k_win.device
+    valid = torch.empty((b,), dtype=torch.int64, device=dev) if valid is None else valid
+    overflow = torch.empty((b,), dtype=torch.int32, device=dev) if overflow is None else overflow
+    policy = L.MARS_COMMIT_BATCH_MIN if batch_min else L.MARS_COMMIT_PER_SAMPLE
+    _check(L.load().mars_kv_commit(ctypes.byref(desc), _ptr(k_win), _ptr(v_win), _ptr(n_accept), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(cache_len), _ptr(valid), _ptr(overflow), policy,
+                                   _stream(k_win)), "mars_kv_commit")
+    return valid, overflow

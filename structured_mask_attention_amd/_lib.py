@@ -14,6 +14,8 @@ MARS_EWORKSPACE = -3
 MARS_EHIP = -4
 MARS_DTYPE_BF16 = 0
 MARS_DTYPE_FP32 = 1
+MARS_COMMIT_PER_SAMPLE = 0
+MARS_COMMIT_BATCH_MIN = 1
 
 I64x3 = ctypes.c_int64 * 3
 
@@ -67,6 +69,7 @@ _SIGNATURES = {
                                      P, P, P, P, ctypes.c_size_t, P]),
     "mars_decode_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    "mars_kv_commit": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_int32, P]),
     "mars_accept_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_accept": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), P, P, P, P, P, ctypes.c_size_t, P]),
     "mars_accept_margin": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), P, P, P, P, P, P, ctypes.c_size_t, P]),

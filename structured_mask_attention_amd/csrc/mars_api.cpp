@@ -407,4 +407,44 @@ int mars_accept_margin(const mars_accept_desc* desc, const void* logits, int32_t
     return map_hip(mars::launch_accept(a, stream));
 }
 
+int mars_kv_commit(const mars_decode_desc* desc, const void* k_win, const void* v_win, const int32_t* n_accept,
+                   void* k_cache, void* v_cache, int32_t* cache_len, uint64_t* valid, int32_t* overflow,
+                   int32_t policy, hipStream_t stream) {
+    int st = check_decode_desc(desc);
+    if (st) return st;
+    if (policy != MARS_COMMIT_PER_SAMPLE && policy != MARS_COMMIT_BATCH_MIN) return MARS_EINVAL;
+    if (desc->batch == 0) return MARS_OK;
+    if (!k_win || !v_win || !n_accept || !cache_len) return MARS_EINVAL;
+    if (desc->cache_capacity > 0 && (!k_cache || !v_cache)) return MARS_EINVAL;
+    if (!aligned16(k_win) || !aligned16(v_win) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(n_accept) & 3u) || (reinterpret_cast<uintptr_t>(cache_len) & 3u) ||
+        (reinterpret_cast<uintptr_t>(valid) & 7u) || (reinterpret_cast<uintptr_t>(overflow) & 3u))
+        return MARS_EINVAL;
+    if (!strides_ok(desc->kw_strides, 2) || !strides_ok(desc->vw_strides, 2) || !strides_ok(desc->kc_strides, 2) ||
+        !strides_ok(desc->vc_strides, 2))
+        return MARS_EINVAL;
+    mars::CommitArgs a;
+    a.kw = k_win;
+    a.vw = v_win;
+    a.n_accept = n_accept;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.cache_len = cache_len;
+    a.valid = valid;
+    a.overflow = overflow;
+    for (int i = 0; i < 3; ++i) {
+        a.kws[i] = desc->kw_strides[i];
+        a.vws[i] = desc->vw_strides[i];
+        a.kcs[i] = desc->kc_strides[i];
+        a.vcs[i] = desc->vc_strides[i];
+    }
+    a.batch = desc->batch;
+    a.hkv = desc->n_kv_heads;
+    a.d = desc->head_dim;
+    a.W = desc->window;
+    a.cap = desc->cache_capacity;
+    a.batch_min = policy == MARS_COMMIT_BATCH_MIN ? 1 : 0;
+    return map_hip(mars::launch_kv_commit(a, stream));
+}
+
 }  // extern "C"

@@ -71,6 +71,21 @@ constexpr int64_t kDecodeMaxCapacity = int64_t(65535) * kDecodeChunk;
 size_t decode_workspace_bytes(int batch, int hkv, int G, int W, int d, int cap);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// KV commit and cursor advance (kv_commit.hip).
+struct CommitArgs {
+    const void* kw;
+    const void* vw;
+    const int32_t* n_accept;
+    void* kc;
+    void* vc;
+    int32_t* cache_len;
+    uint64_t* valid;     // may be null
+    int32_t* overflow;   // may be null
+    int64_t kws[3], vws[3], kcs[3], vcs[3];
+    int batch, hkv, d, W, cap, batch_min;
+};
+hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t s);
+
 // Acceptance (accept.hip).
 struct AcceptArgs {
     const void* logits;

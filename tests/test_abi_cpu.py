@@ -220,6 +220,27 @@ def test_accept_margin_validation_errors():
     assert call(d, ptr=None, ws=None, pmax=None, margin=None) == L.MARS_OK
 
 
+def test_kv_commit_validation_errors():
+    lib = L.load()
+    good = lambda: M.decode_desc(4, 28, 4, 128, 4, 4096)
+
+    def call(d, ptr=FAKE, valid=None, overflow=None, policy=0):
+        return lib.mars_kv_commit(ctypes.byref(d), ptr, ptr, ptr, ptr, ptr, ptr, valid, overflow, policy, None)
+
+    assert call(good(), policy=2) == L.MARS_EINVAL
+    assert call(good(), policy=-1) == L.MARS_EINVAL
+    assert call(good(), ptr=None) == L.MARS_EINVAL
+    assert call(good(), ptr=MISALIGNED) == L.MARS_EINVAL
+    assert call(good(), valid=FAKE + 4) == L.MARS_EINVAL          # uint64 alignment
+    assert call(good(), overflow=FAKE + 2) == L.MARS_EINVAL
+    d = good(); d.head_dim = 96
+    assert call(d) == L.MARS_EUNSUPPORTED
+    d = good(); d.kc_strides[2] = 100                              # cache rows lose 16-byte alignment
+    assert call(d) == L.MARS_EINVAL
+    d = good(); d.batch = 0
+    assert call(d, ptr=None) == L.MARS_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
