@@ -37,6 +37,13 @@ Readings taken where the pages are silent (each is listed in the design notes):
   sequence's own n, the batch-minimum policy min over the batch for every sequence;
   a sequence whose cache cannot hold n more rows commits none and reports it; the
   validity bitmask of a sequence has bit i set iff window row i was committed.
+* Training loss (MARS §3.2 Eq. 3, §3.3 Eq. 5, logits right-shifted as in AR: the logit
+  row of position p predicts the token at p + 1): L_AR takes response token x_t from
+  the clean row before it (the last prompt row for t = 0; none if there is no prompt);
+  L_mask takes x_t from the noisy row before it inside its block, and the first token
+  of a block, whose only fully clean context is the clean prefix (§3.3: position 1 of a
+  block is exactly an AR prediction; Eq. 4's 1/B), from the same clean row as L_AR.
+  Losses are sums of -log softmax(row)[target] (natural log).
 * The margin gate's margin is the top-1 minus the top-2 probability of that softmax,
   where top-2 is the second largest entry of the row counted with multiplicity (a
   tied maximum gives margin 0); it commits the same way as the probability gate.
@@ -72,6 +79,8 @@ __all__ = [
     "accept_margin",
     "accept_margin_scalar",
     "kv_commit",
+    "shifted_ce_targets",
+    "shifted_ce",
 ]
 
 
@@ -596,3 +605,64 @@ def kv_commit(k_cache, v_cache, cache_len, k_win, v_win, n_accept, batch_min=Fal
             valid[bi] |= np.uint64(1) << np.uint64(i)
         ln[bi] = start + n
     return kc, vc, ln.astype(np.int32), valid, over
+
+
+# ---------------------------------------------------------------------------
+# Right-shifted cross-entropy L = L_mask + L_AR ([MARS] §3.2 Eq. 3, §3.3 Eq. 4-5)
+# ---------------------------------------------------------------------------
+
+def shifted_ce_targets(P, L, B):
+    """Per logits row of [prompt; x; x~] (N = P + 2L rows): (target response offset or -1,
+    AR weight, mask weight).  Right-shifted logits: row p predicts the token at p + 1.
+
+    * clean row P - 1 + t (t = 0..L-1, row >= 0) predicts x_t: AR weight 1; mask weight 1
+      when t is the first offset of a block (t % B == 0), whose context is fully clean;
+    * noisy row P + L + j (j = 0..L-2) predicts x_{j+1} when j+1 is not a block start:
+      mask weight 1 (context: the clean prefix of earlier blocks plus the masks up to j);
+    * every other row predicts nothing.
+    """
+    N = P + 2 * L
+    tgt = np.full(N, -1, dtype=np.int64)
+    war = np.zeros(N)
+    wmask = np.zeros(N)
+    for t in range(L):
+        r = P - 1 + t
+        if r >= 0:
+            tgt[r] = t
+            war[r] = 1.0
+            if t % B == 0:
+                wmask[r] = 1.0
+    for j in range(L - 1):
+        if (j + 1) % B != 0:
+            r = P + L + j
+            tgt[r] = j + 1
+            wmask[r] = 1.0
+    return tgt, war, wmask
+
+
+def shifted_ce(logits, x, P, L, B):
+    """L_mask and L_AR of one batch of logits [b, N, V] for response tokens x [b, L].
+
+    Returns (loss_mask [b], loss_ar [b], dlogits [b, N, V]) in float64, where dlogits is
+    the gradient of L_mask + L_AR: (w_ar + w_mask) * (softmax(row) - onehot(target)) on rows
+    with a target, zero elsewhere.
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    b, N, V = z.shape
+    assert N == P + 2 * L and x.shape == (b, L)
+    tgt, war, wmask = shifted_ce_targets(P, L, B)
+    rows = np.nonzero(tgt >= 0)[0]
+    m = z[:, rows].max(axis=-1, keepdims=True)
+    lse = m[..., 0] + np.log(np.exp(z[:, rows] - m).sum(axis=-1))           # [b, R]
+    tok = np.asarray(x)[:, tgt[rows]]                                          # [b, R]
+    picked = np.take_along_axis(z[:, rows], tok[..., None], axis=-1)[..., 0]
+    ce = lse - picked
+    loss_ar = (ce * war[rows]).sum(axis=1)
+    loss_mask = (ce * wmask[rows]).sum(axis=1)
+    d = np.zeros_like(z)
+    sm = np.exp(z[:, rows] - lse[..., None])
+    for k, r in enumerate(rows):
+        g = sm[:, k].copy()
+        g[np.arange(b), tok[:, k]] -= 1.0
+        d[:, r] = (war[r] + wmask[r]) * g
+    return loss_mask, loss_ar, d

@@ -340,3 +340,62 @@ def test_kv_commit_then_decode_equals_decode_over_longer_cache():
         vref[bi, :, ln[bi]:n] = vw[bi, :m].transpose(1, 0, 2)
         ref = O.decode(qn[bi:bi + 1], kn[bi:bi + 1], vn[bi:bi + 1], kref[bi:bi + 1], vref[bi:bi + 1], l2[bi:bi + 1])
         assert np.array_equal(got[bi:bi + 1], ref)
+
+
+# ---------------------------------------------------------------------------
+# Right-shifted cross-entropy (Eq. 3 and Eq. 5)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P,L,B", [(3, 8, 4), (0, 9, 4), (5, 6, 1), (2, 5, 8)])
+def test_shifted_ce_term_counts_and_eq4(P, L, B):
+    """Every response token has exactly one AR and one mask term (the first one none when
+    there is no prompt), and the mask terms taken from clean rows are the block starts:
+    their share is ceil(L/B)/L, Eq. 4's 1/B when B divides L."""
+    tgt, war, wmask = O.shifted_ce_targets(P, L, B)
+    n_tok = L - (1 if P == 0 else 0)
+    assert war.sum() == n_tok and wmask.sum() == n_tok
+    PL = P + L
+    clean_mask = wmask[:PL].sum()
+    assert clean_mask == -(-L // B) - (1 if P == 0 else 0)
+    if P > 0 and L % B == 0:
+        assert clean_mask / wmask.sum() == 1.0 / B
+    # targets: clean row P-1+t -> t; noisy row PL+j -> j+1, never a block start
+    for r in np.nonzero(tgt >= 0)[0]:
+        if r < PL:
+            assert tgt[r] == r - P + 1
+        else:
+            assert tgt[r] == r - PL + 1 and (r - PL + 1) % B != 0
+
+
+def test_shifted_ce_uniform_logits_closed_form():
+    P, L, B, V = 4, 8, 4, 37
+    z = np.zeros((2, P + 2 * L, V))
+    x = np.random.default_rng(3).integers(0, V, size=(2, L))
+    lm, la, d = O.shifted_ce(z, x, P, L, B)
+    assert np.allclose(la, L * math.log(V), rtol=0, atol=1e-12)
+    assert np.allclose(lm, L * math.log(V), rtol=0, atol=1e-12)
+
+
+def test_shifted_ce_matches_torch_cross_entropy_and_gradient():
+    """torch float64 cross_entropy on the selected rows (library cross-check) and central
+    differences of L_mask + L_AR for the gradient."""
+    P, L, B, V = 2, 7, 3, 11
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((2, P + 2 * L, V))
+    x = rng.integers(0, V, size=(2, L))
+    lm, la, d = O.shifted_ce(z, x, P, L, B)
+    tgt, war, wmask = O.shifted_ce_targets(P, L, B)
+    zt = torch.from_numpy(z)
+    for bi in range(2):
+        for w, ref in ((war, la[bi]), (wmask, lm[bi])):
+            rows = np.nonzero(w)[0]
+            ce = F.cross_entropy(zt[bi, rows], torch.from_numpy(x[bi, tgt[rows]]), reduction="sum").item()
+            assert abs(ce - ref) < 1e-12
+    eps = 1e-6
+    for (bi, r, v) in [(0, 1, 3), (1, P + L + 2, 7), (0, P + 3, 0), (1, P + 2 * L - 1, 5), (0, P + L + 1, 10)]:
+        zp, zm = z.copy(), z.copy()
+        zp[bi, r, v] += eps
+        zm[bi, r, v] -= eps
+        fp = sum(a.sum() for a in O.shifted_ce(zp, x, P, L, B)[:2])
+        fm = sum(a.sum() for a in O.shifted_ce(zm, x, P, L, B)[:2])
+        assert abs((fp - fm) / (2 * eps) - d[bi, r, v]) < 1e-7
