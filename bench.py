@@ -7,7 +7,8 @@ One step = one pass of the whole path on synthetic, seeded inputs resident in HB
   2. mars_decode_step on the Qwen2.5-7B-shaped decode workload (32 sequences, 28/4 heads,
      head_dim 128, cache lengths U[512, 4096], 4 window rows)  -> GB/s;
   3. mars_accept on its logits [32, 4, 152064] at tau = 0.95   -> GB/s (the margin gate,
-     mars_accept_margin, is timed beside it and reported in the decode section);
+     mars_accept_margin, is timed beside it and reported in the decode section, and so is
+     mars_kv_commit, the loop's cache append and cursor advance);
   decode tokens/s = sum(n_accept) / (t_decode + t_accept)  (one attention layer + accept).
 The timed region is exactly K whole steps (HIP events at its ends, on the launch stream);
 per-kernel durations come from groups of K back-to-back launches of one kernel (events
@@ -16,7 +17,9 @@ copies of every input rotate across steps, so a step reads data last touched abo
 earlier and the 256 MB Infinity Cache holds none of it (no dirty flush traffic either).
 The 7B-shaped and long training layouts are timed as well (own events) and reported, and so
 is the training backward (mars_attn_bwd: dQ, dK, dV) on all three layouts (counted as five
-products over the forward's visible tiles).
+products over the forward's visible tiles), and the training loss (mars_shifted_ce: L_mask +
+L_AR with the logits gradient on [8, 1280, 151936] bf16 logits -> GB/s of one read of the
+logits and one write of the gradient).
 The CPU baseline is the fp64 oracle on a bounded sample of the same workloads.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -24,6 +27,7 @@ Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -38,6 +42,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "visible-tile TFLOP/s (train layout) + decode-step tokens/s at τ=0.95, 1 GPU"
 MARGIN_TAU = 0.3              # margin-gate threshold for its timing line (the pages give no value)
+QWEN05B_VOCAB = 151936        # Qwen2.5-0.5B output vocabulary (training-loss timing)
 
 
 def parse():
@@ -48,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-layouts", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the training backward figures")
+    ap.add_argument("--no-loss", action="store_true", help="skip the training loss (L_mask + L_AR) figures")
     ap.add_argument("--copies", type=int, default=3, help="rotated input copies (1 = warm caches)")
     return ap.parse_args()
 
@@ -173,6 +179,10 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # No collector passes inside timed groups: a full pass over torch's objects takes tens
+    # of milliseconds and would stall the launching thread.
+    gc.collect()
+    gc.disable()
 
     # (1) The timed region: exactly `steps` whole steps, events at its two ends.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -188,13 +198,17 @@ def main():
 
     # (2) Per-kernel durations: each kernel launched `steps` times back to back (same input
     # rotation), events around each group, so launch gaps are amortised as in the trace.
+    host_issue = {}
+
     def group(fn):
         a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        h0 = time.perf_counter()
         a.record(stream)
         for i in range(args.steps):
             fn(i)
         z.record(stream)
+        host_issue.setdefault(fn.__name__, []).append((time.perf_counter() - h0) / args.steps * 1e6)
         torch.cuda.synchronize()
         return a.elapsed_time(z) * 1e-3 / args.steps
 
@@ -210,6 +224,20 @@ def main():
     t_attn = np.array([r[0] for r in reps])
     t_dec = np.array([r[1] for r in reps])
     t_acc = np.array([r[2] for r in reps])
+
+    # KV commit (decode loop bookkeeping): timed last, on a scratch cursor array that starts at
+    # 0 each group, so it writes cache rows the timed steps above have already read.
+    lens_s = torch.zeros_like(dec_sets[0][5])
+
+    def commit(i):
+        dq_, dk_, dv_, dkc_, dvc_, _, _ = dec_sets[i % ncopy]
+        M.mars_kv_commit(dk_, dv_, nacc, dkc_, dvc_, lens_s)
+
+    t_cmt = []
+    for _ in range(3):
+        lens_s.zero_()
+        t_cmt.append(group(commit))
+    t_cmt = float(np.mean(t_cmt))
 
     flop_vt, flop_alg = train_flops(M, st)
     ta = float(np.mean(t_attn))
@@ -300,6 +328,31 @@ def main():
         cpu = cpu_baseline_train(st)
         cpu_dec = cpu_baseline_decode(sd)
 
+    # ---- training loss L_mask + L_AR with its logits gradient (one copy: 6 GB of traffic per
+    # call, far beyond the caches) ----
+    loss = {}
+    if not args.no_loss:
+        torch.cuda.empty_cache()
+        V = QWEN05B_VOCAB
+        lg, tk = I.ce_inputs(st.batch, st.P, st.L, V, 2002, device=dev)
+        dlg = torch.empty_like(lg)
+        cws = torch.empty(max(16, st.batch * st.N * 4), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            M.mars_shifted_ce(lg, tk, st.P, st.L, st.B, grad=True, dlogits=dlg, ws=cws)
+        reps = 10
+        a4, z4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a4.record(stream)
+        for _ in range(reps):
+            M.mars_shifted_ce(lg, tk, st.P, st.L, st.B, grad=True, dlogits=dlg, ws=cws)
+        z4.record(stream)
+        torch.cuda.synchronize()
+        t4 = a4.elapsed_time(z4) * 1e-3 / reps
+        ce_bytes = 2 * 2 * st.batch * st.N * V   # bf16 logits read once, bf16 gradient written once
+        loss = {"workload": f"{st.name}_V{V}", "us": t4 * 1e6, "GBps": ce_bytes / t4 / 1e9,
+                "frac_hbm": ce_bytes / t4 / 1e9 / PEAK_HBM_GBS, "bytes": ce_bytes}
+        del lg, tk, dlg, cws
+
     rec = {
         "metric": METRIC,
         "value": tflops,
@@ -321,17 +374,22 @@ def main():
             "tokens_per_s": n_sum / (td + tc),
             "tokens_accepted": n_sum,
             "decode_us": td * 1e6, "accept_us": tc * 1e6,
+            "decode_us_groups": [float(t) * 1e6 for t in t_dec],
             "decode_GBps": dec_bytes / td / 1e9, "decode_frac_hbm": dec_bytes / td / 1e9 / PEAK_HBM_GBS,
             "accept_GBps": acc_bytes / tc / 1e9, "accept_frac_hbm": acc_bytes / tc / 1e9 / PEAK_HBM_GBS,
             "accept_margin_us": t_mgn * 1e6, "accept_margin_GBps": acc_bytes / t_mgn / 1e9,
             "accept_margin_tau": MARGIN_TAU,
+            "kv_commit_us": t_cmt * 1e6,
+            "tokens_per_s_with_commit": n_sum / (td + tc + t_cmt),
             "cpu_baseline": cpu_dec,
         },
         "train_attn_us": ta * 1e6,
         "train_attn_us_groups": [float(t) * 1e6 for t in t_attn],
         "train_layouts": layouts,
         "train_backward": backward,
+        "train_loss": loss,
         "wall_s_timed_region": t_wall,
+        "host_issue_us_per_call": {k: [round(x, 1) for x in v] for k, v in host_issue.items()},
         "input_copies_rotated": ncopy,
     }
     print(json.dumps(rec))

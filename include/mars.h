@@ -16,7 +16,9 @@
  *   - mars_accept_margin: the same rule gated on the top-1 minus top-2 probability margin
  *                       (the blog's margin gate);
  *   - mars_kv_commit:   append the accepted window K/V to the caches and advance the
- *                       per-sequence cursors (or all at the batch minimum).
+ *                       per-sequence cursors (or all at the batch minimum);
+ *   - mars_shifted_ce:  the training loss L_mask + L_AR (§3.2 Eq. 3, §3.3 Eq. 5) over the
+ *                       vocabulary, right-shifted logits, optional gradient.
  *
  * Conventions (all entry points):
  *   - Every call returns an int status: MARS_OK (0) or a negative MARS_E* code.
@@ -231,6 +233,43 @@ int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void
                      const void* v_win, const void* k_cache, const void* v_cache,
                      const int32_t* cache_len, void* o, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * Training loss over the vocabulary (MARS §3.2 Eq. 3 and §3.3 Eq. 5): L = L_mask + L_AR
+ * on the logits of one forward over [prompt ; x ; x~] (N = P + 2L rows), right-shifted
+ * as in AR training (the row of position p predicts the token at p + 1):
+ *   L_AR   = sum over response tokens x_t of CE(row P - 1 + t, x_t)   (no term for t = 0
+ *            when P = 0);
+ *   L_mask = sum over x_t of CE(noisy row P + L + t - 1, x_t) inside a block, and, for the
+ *            first token of each block (t % B == 0: its only fully clean context is the
+ *            clean prefix, §3.3 and Eq. 4), CE(clean row P - 1 + t, x_t);
+ *   CE(row, y) = logsumexp(row) - row[y]  (natural log).
+ * Optionally also dL/dlogits = (w_AR + w_mask) * (softmax(row) - onehot(y)) per row, zero
+ * rows where nothing is predicted.
+ * ------------------------------------------------------------------------------------ */
+typedef struct mars_ce_desc {
+    int32_t batch;              /* >= 0, <= 65535 */
+    int32_t prompt_len;         /* P >= 0 */
+    int32_t resp_len;           /* L >= 0 */
+    int32_t block;              /* B >= 1 */
+    int32_t vocab;              /* >= 8, a multiple of 8 (16-byte rows), else MARS_EUNSUPPORTED */
+    int32_t dtype;              /* MARS_DTYPE_BF16 */
+    int64_t logits_strides[2];  /* logits [batch][N][vocab]: batch, position (vocab contiguous) */
+    int64_t dlogits_strides[2]; /* dlogits, same shape (used only when dlogits is given) */
+    int64_t tokens_stride;      /* tokens int32 [batch][resp_len]: batch stride (elements) */
+} mars_ce_desc;
+
+/* Workspace mars_shifted_ce needs, in bytes (one fp32 per (sequence, row)). */
+int mars_shifted_ce_workspace_bytes(const mars_ce_desc* desc, size_t* bytes);
+
+/*
+ * logits: bf16, finite.  tokens: int32 response tokens x, each in [0, vocab).  Outputs on
+ * the device: loss_mask, loss_ar fp32 [batch] (sums, summed in a fixed order); dlogits
+ * (optional, may be NULL): bf16 gradient of loss_mask + loss_ar.  ws: device workspace of
+ * at least mars_shifted_ce_workspace_bytes, no initialisation needed.
+ */
+int mars_shifted_ce(const mars_ce_desc* desc, const void* logits, const int32_t* tokens, float* loss_mask,
+                    float* loss_ar, void* dlogits, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
  * KV commit and cursor advance (MARS author blog, "Batching is where methods like this

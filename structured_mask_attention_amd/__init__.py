@@ -30,6 +30,7 @@ __all__ = [
     "mars_accept",
     "mars_accept_margin",
     "mars_kv_commit",
+    "mars_shifted_ce",
 ]
 
 
@@ -322,3 +323,38 @@ def mars_kv_commit(k_win, v_win, n_accept, k_cache, v_cache, cache_len, batch_mi
                                    _ptr(v_cache), _ptr(cache_len), _ptr(valid), _ptr(overflow), policy,
                                    _stream(k_win)), "mars_kv_commit")
     return valid, overflow
+
+
+def ce_desc(batch, P, Lr, B, V, logits=None, dlogits=None, tokens=None):
+    desc = L.CeDesc()
+    desc.batch, desc.prompt_len, desc.resp_len, desc.block, desc.vocab = batch, P, Lr, B, V
+    desc.dtype = L.MARS_DTYPE_BF16
+    N = P + 2 * Lr
+    ls = (logits.stride(0), logits.stride(1)) if logits is not None else (N * V, V)
+    ds = (dlogits.stride(0), dlogits.stride(1)) if dlogits is not None else (N * V, V)
+    desc.logits_strides = (ctypes.c_int64 * 2)(*ls)
+    desc.dlogits_strides = (ctypes.c_int64 * 2)(*ds)
+    desc.tokens_stride = tokens.stride(0) if tokens is not None else Lr
+    return desc
+
+
+def mars_shifted_ce(logits, tokens, prompt_len, resp_len, block, grad=False, dlogits=None, ws=None):
+    """L_mask, L_AR (fp32 [b] each) of logits bf16 [b, N, V] for response tokens int32
+    [b, L]; with ``grad`` also dlogits bf16 [b, N, V].  Returns (loss_mask, loss_ar, dlogits)."""
+    b, N, V = logits.shape
+    if logits.stride(-1) != 1 or tokens.stride(-1) != 1:
+        raise ValueError("vocab and token dimensions must be contiguous")
+    dev = logits.device
+    if grad and dlogits is None:
+        dlogits = torch.empty_like(logits)
+    desc = ce_desc(b, prompt_len, resp_len, block, V, logits, dlogits, tokens)
+    n = ctypes.c_size_t()
+    _check(L.load().mars_shifted_ce_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "mars_shifted_ce_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+    lm = torch.empty((b,), dtype=torch.float32, device=dev)
+    la = torch.empty((b,), dtype=torch.float32, device=dev)
+    _check(L.load().mars_shifted_ce(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(lm), _ptr(la),
+                                    _ptr(dlogits), _ptr(ws), ws.numel(), _stream(logits)), "mars_shifted_ce")
+    return lm, la, dlogits

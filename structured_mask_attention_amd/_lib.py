@@ -34,6 +34,15 @@ class AttnBwdStrides(ctypes.Structure):
     _fields_ = [("do_strides", I64x3), ("dq_strides", I64x3), ("dk_strides", I64x3), ("dv_strides", I64x3)]
 
 
+class CeDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("prompt_len", ctypes.c_int32), ("resp_len", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("logits_strides", ctypes.c_int64 * 2), ("dlogits_strides", ctypes.c_int64 * 2),
+        ("tokens_stride", ctypes.c_int64),
+    ]
+
+
 class DecodeDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
@@ -70,6 +79,8 @@ _SIGNATURES = {
     "mars_decode_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "mars_kv_commit": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_int32, P]),
+    "mars_shifted_ce_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(CeDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "mars_shifted_ce": (ctypes.c_int, [ctypes.POINTER(CeDesc), P, P, P, P, P, P, ctypes.c_size_t, P]),
     "mars_accept_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_accept": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), P, P, P, P, P, ctypes.c_size_t, P]),
     "mars_accept_margin": (ctypes.c_int, [ctypes.POINTER(AcceptDesc), P, P, P, P, P, P, ctypes.c_size_t, P]),

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmars.so")
-SOURCES = ["mars_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "accept.hip", "mask_kernels.hip", "kv_commit.hip"]
+SOURCES = ["mars_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "accept.hip", "mask_kernels.hip", "kv_commit.hip", "shifted_ce.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

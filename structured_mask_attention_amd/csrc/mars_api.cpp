@@ -447,4 +447,60 @@ int mars_kv_commit(const mars_decode_desc* desc, const void* k_win, const void* 
     return map_hip(mars::launch_kv_commit(a, stream));
 }
 
+static int check_ce_desc(const mars_ce_desc* d) {
+    if (!d) return MARS_EINVAL;
+    if (d->batch < 0 || d->prompt_len < 0 || d->resp_len < 0 || d->block < 1 || d->vocab < 1) return MARS_EINVAL;
+    if (d->dtype != MARS_DTYPE_BF16) return d->dtype == MARS_DTYPE_FP32 ? MARS_EUNSUPPORTED : MARS_EINVAL;
+    if (d->vocab % 8 != 0) return MARS_EUNSUPPORTED;
+    if (d->batch > 65535) return MARS_EUNSUPPORTED;
+    if ((int64_t)d->prompt_len + 2 * (int64_t)d->resp_len > (1 << 24)) return MARS_EUNSUPPORTED;
+    return MARS_OK;
+}
+
+int mars_shifted_ce_workspace_bytes(const mars_ce_desc* desc, size_t* bytes) {
+    const int st = check_ce_desc(desc);
+    if (st) return st;
+    if (!bytes) return MARS_EINVAL;
+    *bytes = mars::shifted_ce_workspace_bytes(desc->batch, desc->prompt_len, desc->resp_len);
+    return MARS_OK;
+}
+
+int mars_shifted_ce(const mars_ce_desc* desc, const void* logits, const int32_t* tokens, float* loss_mask,
+                    float* loss_ar, void* dlogits, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const int st = check_ce_desc(desc);
+    if (st) return st;
+    if (desc->batch == 0) return MARS_OK;
+    if (!loss_mask || !loss_ar) return MARS_EINVAL;
+    const int64_t N = (int64_t)desc->prompt_len + 2 * (int64_t)desc->resp_len;
+    if (N > 0 && (!logits || (desc->resp_len > 0 && !tokens))) return MARS_EINVAL;
+    if (!aligned16(logits) || !aligned16(dlogits) || (reinterpret_cast<uintptr_t>(tokens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(loss_mask) & 3u) || (reinterpret_cast<uintptr_t>(loss_ar) & 3u))
+        return MARS_EINVAL;
+    for (int i = 0; i < 2; ++i) {
+        if (desc->logits_strides[i] < 0 || desc->logits_strides[i] % 8) return MARS_EINVAL;
+        if (dlogits && (desc->dlogits_strides[i] < 0 || desc->dlogits_strides[i] % 8)) return MARS_EINVAL;
+    }
+    if (desc->tokens_stride < 0) return MARS_EINVAL;
+    const size_t need = mars::shifted_ce_workspace_bytes(desc->batch, desc->prompt_len, desc->resp_len);
+    if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 3u))) return MARS_EWORKSPACE;
+    mars::CeArgs a;
+    a.logits = logits;
+    a.tokens = tokens;
+    a.loss_mask = loss_mask;
+    a.loss_ar = loss_ar;
+    a.dlogits = dlogits;
+    a.ws = ws;
+    a.ls[0] = desc->logits_strides[0];
+    a.ls[1] = desc->logits_strides[1];
+    a.ds[0] = desc->dlogits_strides[0];
+    a.ds[1] = desc->dlogits_strides[1];
+    a.ts0 = desc->tokens_stride;
+    a.batch = desc->batch;
+    a.P = desc->prompt_len;
+    a.L = desc->resp_len;
+    a.B = desc->block;
+    a.V = desc->vocab;
+    return map_hip(mars::launch_shifted_ce(a, stream));
+}
+
 }  // extern "C"

@@ -86,6 +86,20 @@ struct CommitArgs {
 };
 hipError_t launch_kv_commit(const CommitArgs& a, hipStream_t s);
 
+// Right-shifted cross-entropy L_mask + L_AR (shifted_ce.hip).
+struct CeArgs {
+    const void* logits;
+    const int32_t* tokens;
+    float* loss_mask;
+    float* loss_ar;
+    void* dlogits;       // may be null
+    void* ws;
+    int64_t ls[2], ds[2], ts0;
+    int batch, P, L, B, V;
+};
+size_t shifted_ce_workspace_bytes(int batch, int P, int L);
+hipError_t launch_shifted_ce(const CeArgs& a, hipStream_t s);
+
 // Acceptance (accept.hip).
 struct AcceptArgs {
     const void* logits;

@@ -157,3 +157,23 @@ def logits_inputs(batch, W, vocab, seed, spike_hi=20.0):
     bi, wi = np.meshgrid(np.arange(batch), np.arange(W), indexing="ij")
     x[bi, wi, ids] += h
     return to_bf16(x)
+
+
+def ce_inputs(batch, P, L, vocab, seed, device="cpu", spike_hi=20.0):
+    """Logits bf16 [batch, P + 2L, vocab] and response tokens int32 [batch, L] for the
+    training loss.  Drawn with one torch generator on ``device`` (so the full-size
+    workload is made on the GPU without a host copy), in this order: logits (float32
+    standard normal), one spike per row (height uniform on [0, spike_hi) at a uniform
+    token id, added in float32 before the bf16 rounding), then the tokens (uniform on
+    [0, vocab))."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    N = P + 2 * L
+    x = torch.randn((batch, N, vocab), generator=g, dtype=torch.float32, device=device)
+    h = torch.rand((batch, N), generator=g, dtype=torch.float32, device=device) * spike_hi
+    ids = torch.randint(0, vocab, (batch, N), generator=g, device=device)
+    x.scatter_add_(2, ids[..., None], h[..., None])
+    logits = x.to(torch.bfloat16)
+    del x
+    tokens = torch.randint(0, vocab, (batch, L), generator=g, device=device).to(torch.int32)
+    return logits, tokens

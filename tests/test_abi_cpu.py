@@ -241,6 +241,37 @@ def test_kv_commit_validation_errors():
     assert call(d, ptr=None) == L.MARS_OK
 
 
+def test_shifted_ce_validation_errors():
+    lib = L.load()
+    good = lambda: M.ce_desc(8, 256, 512, 4, 151936)
+
+    def call(d, ptr=FAKE, lm=FAKE, la=FAKE, dl=None, ws=FAKE, ws_bytes=1 << 40):
+        return lib.mars_shifted_ce(ctypes.byref(d), ptr, ptr, lm, la, dl, ws, ws_bytes, None)
+
+    for field, val, code in [("vocab", 151937, L.MARS_EUNSUPPORTED), ("vocab", 0, L.MARS_EINVAL),
+                             ("block", 0, L.MARS_EINVAL), ("resp_len", -1, L.MARS_EINVAL),
+                             ("batch", 70000, L.MARS_EUNSUPPORTED), ("dtype", L.MARS_DTYPE_FP32, L.MARS_EUNSUPPORTED)]:
+        d = good()
+        setattr(d, field, val)
+        assert call(d) == code, field
+    assert call(good(), lm=None) == L.MARS_EINVAL
+    assert call(good(), ptr=None) == L.MARS_EINVAL
+    assert call(good(), ptr=MISALIGNED) == L.MARS_EINVAL
+    assert call(good(), dl=MISALIGNED) == L.MARS_EINVAL
+    assert call(good(), la=FAKE + 2) == L.MARS_EINVAL
+    d = good(); d.logits_strides[1] = 151937                       # rows lose 16-byte alignment
+    assert call(d) == L.MARS_EINVAL
+    d = good(); d.dlogits_strides[0] = -8
+    assert call(d, dl=FAKE) == L.MARS_EINVAL
+    n = ctypes.c_size_t()
+    assert lib.mars_shifted_ce_workspace_bytes(ctypes.byref(good()), ctypes.byref(n)) == L.MARS_OK
+    assert n.value == 8 * (256 + 2 * 512) * 4
+    assert call(good(), ws_bytes=n.value - 1) == L.MARS_EWORKSPACE
+    assert call(good(), ws=None) == L.MARS_EWORKSPACE
+    d = good(); d.batch = 0
+    assert call(d, ptr=None, lm=None, la=None, ws=None) == L.MARS_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))

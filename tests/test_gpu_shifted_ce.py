@@ -1,0 +1,164 @@
+"""GPU parity of mars_shifted_ce (L_mask, L_AR and their logits gradient) against the
+fp64 oracle.
+
+Bounds, from the kernel's arithmetic (bf16 logits are exact inputs; everything after is
+fp32 with one bf16 rounding of the gradient):
+  * per-row CE: the log-sum-exp adds at most V exp terms in fp32 per thread and merges
+    the partial sums in a tree (relative error of the sum <= ~200 * 2^-24 for the
+    vocabularies here), exp2 of an fp32 argument of magnitude <= 64 (argument rounding
+    <= 64 * 2^-24), and one log: 5e-5 + 1e-6 |lse| nats per row covers it with margin;
+  * losses: n rows of CE each within the row bound, summed in fp32 (n * 2^-24 of the sum
+    of |CE| for the order of the sum);
+  * gradient entries: w (softmax - onehot) with the softmax in fp32 from the same lse
+    (relative 1e-4), rounded once to bf16 (2^-8 of the value), and 1e-4 w absolute at the
+    target entry where p - 1 loses the relative form.
+"""
+import numpy as np
+import pytest
+import torch
+
+import structured_mask_attention_amd as M
+from oracle import mars_oracle as O
+from structured_mask_attention_amd import inputs as I
+from tests.gpu_helpers import dev, to_np64
+
+pytestmark = pytest.mark.gpu
+
+ROW_ABS = 5e-5
+ROW_REL = 1e-6
+
+
+def loss_bound(ce_rows, weights):
+    n = np.count_nonzero(weights)
+    return n * ROW_ABS + ROW_REL * np.abs(ce_rows * weights).sum() + n * 2.0 ** -24 * np.abs(ce_rows * weights).sum()
+
+
+def oracle_row_ce(z, x, P, L, B):
+    """Per-row CE of the oracle for the bounds (the oracle's own per-row terms: loss of a
+    one-row weight vector)."""
+    tgt, war, wmask = O.shifted_ce_targets(P, L, B)
+    zz = np.asarray(z, dtype=np.float64)
+    m = zz.max(axis=-1, keepdims=True)
+    lse = m[..., 0] + np.log(np.exp(zz - m).sum(axis=-1))
+    return lse, tgt, war, wmask
+
+
+def check_losses(lm, la, ref_lm, ref_la, z, x, P, L, B, what):
+    lse, tgt, war, wmask = oracle_row_ce(z, x, P, L, B)
+    b = z.shape[0]
+    for bi in range(b):
+        ce = np.zeros(len(tgt))
+        has = tgt >= 0
+        ce[has] = lse[bi, has] - z[bi, has, x[bi, tgt[has]]]
+        for name, got, ref, w in (("L_mask", lm, ref_lm, wmask), ("L_AR", la, ref_la, war)):
+            err = abs(float(got[bi]) - ref[bi])
+            bound = loss_bound(ce, w) + 1e-6
+            print(f"[{what} b{bi} {name}] got={float(got[bi]):.6f} ref={ref[bi]:.6f} err={err:.2e} bound={bound:.2e}", flush=True)
+            assert np.isfinite(got[bi]) and err <= bound, f"{what}: {name} of sequence {bi} off by {err}"
+
+
+def check_grad(got, ref, x, P, L, B, what, rows=None):
+    tgt, war, wmask = O.shifted_ce_targets(P, L, B)
+    w = war + wmask
+    if rows is not None:
+        tgt, w = tgt[rows], w[rows]
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite gradient"
+    bound = (2.0 ** -8 + 1e-4) * np.abs(ref) + 1e-36
+    b = ref.shape[0]
+    for bi in range(b):
+        for k, t in enumerate(tgt):
+            if t >= 0:
+                bound[bi, k, x[bi, t]] += 1e-4 * w[k]
+    err = np.abs(got - ref)
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    print(f"[{what} dlogits] max_abs={float(err.max()) if err.size else 0:.3e} max err/bound={ratio:.3f}", flush=True)
+    assert ratio <= 1.0, f"{what}: gradient error exceeds its bound (ratio {ratio:.3f})"
+    # rows that predict nothing are exactly zero
+    for k, t in enumerate(tgt):
+        if t < 0:
+            assert np.all(got[:, k] == 0.0), f"{what}: row {k} without a target has a nonzero gradient"
+
+
+def run_case(b, P, L, B, V, seed, what):
+    print(f"case shifted_ce {what} b={b} P={P} L={L} B={B} V={V} seed={seed}", flush=True)
+    logits, tokens = I.ce_inputs(b, P, L, V, seed)
+    z, x = to_np64(logits), tokens.numpy().astype(np.int64)
+    lm, la, dl = M.mars_shifted_ce(logits.to(dev()), tokens.to(dev()), P, L, B, grad=True)
+    torch.cuda.synchronize()
+    ref_lm, ref_la, ref_d = O.shifted_ce(z, x, P, L, B)
+    check_losses(to_np64(lm), to_np64(la), ref_lm, ref_la, z, x, P, L, B, what)
+    check_grad(to_np64(dl), ref_d, x, P, L, B, what)
+    return lm, la, dl
+
+
+@pytest.mark.parametrize("b,P,L,B,V", [
+    (2, 5, 12, 4, 1000),            # ragged last vector slice (1000 / 8 = 125 vectors)
+    (1, 0, 9, 4, 64),               # no prompt: x_0 has no AR term
+    (2, 3, 6, 1, 256),              # B = 1: every token is a block start
+    (1, 4, 3, 8, 512),              # B > L
+    (1, 7, 1, 4, 72),               # L = 1: no noisy row predicts anything
+    (1, 6, 0, 4, 128),              # prompt only: both losses 0, gradient all zero
+    (1, 2, 5, 2, 8),                # smallest vocabulary (one vector)
+    (2, 64, 128, 4, 4096),          # several blocks, V of 4 vectors per thread
+    (1, 3, 10, 4, 8 * 1024 + 8),    # two vectors per thread, second one mostly padding
+    (1, 2, 6, 4, 8 * 1024 * 20),    # largest register-resident vocabulary
+    (1, 2, 6, 4, 8 * 1024 * 20 + 8),   # streaming kernel (vocabulary beyond registers)
+    (1, 1, 5, 2, 262144),           # streaming kernel, larger vocabulary
+])
+def test_ce_small_all_elements(b, P, L, B, V):
+    run_case(b, P, L, B, V, 31 + V + 7 * L, f"P{P} L{L} B{B} V{V}")
+
+
+def test_ce_loss_only_matches_gradient_run_bitwise():
+    b, P, L, B, V = 2, 16, 40, 4, 151936
+    logits, tokens = I.ce_inputs(b, P, L, V, 5, device=dev())
+    a = M.mars_shifted_ce(logits, tokens, P, L, B, grad=True)
+    c = M.mars_shifted_ce(logits, tokens, P, L, B, grad=False)
+    d = M.mars_shifted_ce(logits, tokens, P, L, B, grad=True)
+    torch.cuda.synchronize()
+    assert c[2] is None
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+    assert torch.equal(a[0], d[0]) and torch.equal(a[1], d[1]) and torch.equal(a[2], d[2])
+
+
+def test_ce_strided_views():
+    """Logits and the gradient as row-strided views of wider buffers; padding untouched."""
+    b, P, L, B, V = 2, 4, 10, 4, 512
+    N = P + 2 * L
+    logits, tokens = I.ce_inputs(b, P, L, V, 11)
+    big = torch.zeros((b, N, V + 64), dtype=torch.bfloat16)
+    big[..., :V] = logits
+    lv = big.to(dev())[..., :V]
+    tok_big = torch.zeros((b, L + 3), dtype=torch.int32)
+    tok_big[:, :L] = tokens
+    tv = tok_big.to(dev())[:, :L]
+    dbuf = torch.full((b, N, V + 32), 3.0, dtype=torch.bfloat16, device=dev())
+    dv = dbuf[..., :V]
+    lm, la, _ = M.mars_shifted_ce(lv, tv, P, L, B, grad=True, dlogits=dv)
+    ref = M.mars_shifted_ce(logits.to(dev()), tokens.to(dev()), P, L, B, grad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lm, ref[0]) and torch.equal(la, ref[1]) and torch.equal(dv, ref[2])
+    assert torch.all(dbuf[..., V:] == 3.0)
+
+
+def test_ce_full_size_qwen05b():
+    """The training workload's loss: Qwen2.5-0.5B layout [8, 1280] rows over its 151936-entry
+    vocabulary, in the launch the bench times.  Sequence 0 is checked whole against the
+    oracle (both losses, the gradient on sampled rows); every sequence's losses are finite
+    and non-negative."""
+    s = I.QWEN05B
+    V = 151936
+    print(f"case shifted_ce full size {s.name} V={V}", flush=True)
+    logits, tokens = I.ce_inputs(s.batch, s.P, s.L, V, 2002, device=dev())
+    lm, la, dl = M.mars_shifted_ce(logits, tokens, s.P, s.L, s.B, grad=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lm).all() and torch.isfinite(la).all()
+    assert (lm >= 0).all() and (la >= 0).all()
+    z = to_np64(logits[:1])
+    x = tokens[:1].cpu().numpy().astype(np.int64)
+    ref_lm, ref_la, ref_d = O.shifted_ce(z, x, s.P, s.L, s.B)
+    check_losses(to_np64(lm[:1]), to_np64(la[:1]), ref_lm, ref_la, z, x, s.P, s.L, s.B, "qwen0.5b")
+    rows = np.unique(np.concatenate([[0, s.P - 2, s.P - 1, s.P, s.P + s.L - 1, s.P + s.L, s.N - 2, s.N - 1],
+                                     np.random.default_rng(3).integers(0, s.N, 24)]))
+    check_grad(to_np64(dl[:1, rows]), ref_d[:, rows], x, s.P, s.L, s.B, "qwen0.5b", rows=rows)
