@@ -16,8 +16,8 @@
 //      least this loss can move.  Larger vocabularies take a streaming kernel that keeps
 //      an online (max, sum) and reads the row a second time for the gradient.  Rows
 //      without a target write CE 0 and a zero gradient row.
-//   2. sums: one wave per sequence adds the per-row CE with its weights in row order
-//      (deterministic) into loss_mask[b] and loss_ar[b].
+//   2. sums: one workgroup per sequence adds the per-row CE with its weights in a fixed
+//      order (deterministic) into loss_mask[b] and loss_ar[b].
 #include <cmath>
 #include <utility>
 
@@ -142,39 +142,46 @@ __global__ __launch_bounds__(kThreadsR) void ce_row_reg_kernel(CeParams p) {
     }
     const int target = p.tokens[b * p.ts0 + t];
 
-    // Padding of the last vector: the most negative finite bf16 pair, whose exp is 0.
-    constexpr uint32_t kPad = 0xff7fff7fu;
     uint4 q[NV];
 #pragma unroll
     for (int u = 0; u < NV - 1; ++u) q[u] = *reinterpret_cast<const uint4*>(row + 8 * (tid + u * kThreadsR));
-    q[NV - 1] = last_in ? *reinterpret_cast<const uint4*>(row + 8 * (tid + (NV - 1) * kThreadsR))
-                        : uint4{kPad, kPad, kPad, kPad};
+    q[NV - 1] = last_in ? *reinterpret_cast<const uint4*>(row + 8 * (tid + (NV - 1) * kThreadsR)) : uint4{0u, 0u, 0u, 0u};
     if (tid == 0) s_tv = (target >= 0 && target < p.V) ? __uint_as_float((uint32_t)row[target] << 16) : -INFINITY;
 
-    // Exp offset: any value at or near the row max serves (lse = m + log sum exp(x - m) for
-    // every m), so the high entry of each pair is read as the whole 32-bit word, the bf16
-    // value plus at most one bf16 ulp of low bits, which saves its unpacking.
-    float m = -INFINITY;
+    // One pass over the vectors as they arrive: a running (max, sum of exp relative to it)
+    // per thread, rescaled once per vector.  Any offset at or near the max serves (lse = m +
+    // log sum exp(x - m) for every m), so the high entry of each pair enters the max as the
+    // whole 32-bit word, the bf16 value plus at most one bf16 ulp of low bits, which saves
+    // its unpacking there.
+    float m = -INFINITY, s = 0.f;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-        const uint32_t wv[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+        if (u < NV - 1 || last_in) {   // past the row: nothing to add (with NV = 1, m stays -inf, s 0)
+            const uint32_t wv[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+            float mn = m;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m = max3_raw(m, lo_bf(wv[k]), __uint_as_float(wv[k]));
-    }
-    m = block_max(m, red_m);
-    const float mb = m * kLog2e;
-    pin_regs<NV>(q);
-    float s = 0.f;
+            for (int k = 0; k < 4; ++k) mn = max3_raw(mn, lo_bf(wv[k]), __uint_as_float(wv[k]));
+            s *= __builtin_amdgcn_exp2f((m - mn) * kLog2e);   // 0 on the first vector (m = -inf, s = 0)
+            m = mn;
+            const float mb = m * kLog2e;
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-        const uint32_t wv[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            s += __builtin_amdgcn_exp2f(fmaf(lo_bf(wv[k]), kLog2e, -mb));
-            s += __builtin_amdgcn_exp2f(fmaf(hi_bf(wv[k]), kLog2e, -mb));
+            for (int k = 0; k < 4; ++k) {
+                s += __builtin_amdgcn_exp2f(fmaf(lo_bf(wv[k]), kLog2e, -mb));
+                s += __builtin_amdgcn_exp2f(fmaf(hi_bf(wv[k]), kLog2e, -mb));
+            }
+            // Order the pass vector by vector: this vector's sum is complete before the next
+            // vector is unpacked (left to itself the compiler computes every vector's max
+            // first and keeps their unpacked entries in registers until the exps).
+            if (u + 1 < NV)
+                asm volatile("" : "+v"(s), "+v"(m), "+v"(q[u + 1].x), "+v"(q[u + 1].y), "+v"(q[u + 1].z),
+                             "+v"(q[u + 1].w));
         }
     }
-    s = block_sum(s, red_s);
+    // Workgroup max, each thread's sum moved to it (a thread without entries has s = 0 and
+    // m = -inf: factor 0), workgroup sum.
+    const float M = block_max(m, red_m);
+    s = block_sum(s * __builtin_amdgcn_exp2f((m - M) * kLog2e), red_s);
+    m = M;
     const float lse = m + logf(s);
     if (tid == 0) p.ce[(int64_t)b * p.N + r] = lse - s_tv;
 
@@ -325,26 +332,49 @@ __global__ __launch_bounds__(kThreads) void ce_row_kernel(CeParams p) {
     }
 }
 
-// One wave per sequence: weighted sums of the row CE in row order.
-__global__ __launch_bounds__(64) void ce_sum_kernel(CeParams p) {
-    const int b = blockIdx.x, lane = threadIdx.x;
-    // Fixed order: lane k adds rows k, k + 64, ...; then a fixed butterfly.
+// One 256-thread workgroup per sequence: weighted sums of the row CE.  Thread k adds
+// rows k, k + 256, ... (loads issued together), then a fixed butterfly and the four wave
+// sums in wave order: the same order on every call (deterministic).
+constexpr int kSumThreads = 256;
+
+__global__ __launch_bounds__(kSumThreads) void ce_sum_kernel(CeParams p) {
+    __shared__ float red_a[kSumThreads / 64], red_m[kSumThreads / 64];
+    const int b = blockIdx.x, tid = threadIdx.x;
     float sa = 0.f, sm = 0.f;
-    for (int r = lane; r < p.N; r += 64) {
-        float w_ar, w_mask;
-        if (ce_target(r, p.P, p.L, p.B, &w_ar, &w_mask) < 0) continue;
-        const float c = p.ce[(int64_t)b * p.N + r];
-        sa += w_ar * c;
-        sm += w_mask * c;
+    for (int r0 = 0; r0 < p.N; r0 += 4 * kSumThreads) {
+        float c[4], wa[4], wm[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = r0 + k * kSumThreads + tid;
+            const bool has = r < p.N && ce_target(r, p.P, p.L, p.B, &wa[k], &wm[k]) >= 0;
+            if (!has) wa[k] = wm[k] = 0.f;
+            c[k] = has ? p.ce[(int64_t)b * p.N + r] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            sa += wa[k] * c[k];
+            sm += wm[k] * c[k];
+        }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         sa += __shfl_xor(sa, off);
         sm += __shfl_xor(sm, off);
     }
-    if (lane == 0) {
-        p.loss_ar[b] = sa;
-        p.loss_mask[b] = sm;
+    if ((tid & 63) == 0) {
+        red_a[tid >> 6] = sa;
+        red_m[tid >> 6] = sm;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float ta = red_a[0], tm = red_m[0];
+#pragma unroll
+        for (int w = 1; w < kSumThreads / 64; ++w) {
+            ta += red_a[w];
+            tm += red_m[w];
+        }
+        p.loss_ar[b] = ta;
+        p.loss_mask[b] = tm;
     }
 }
 
@@ -370,7 +400,7 @@ hipError_t launch_shifted_ce(const CeArgs& a, hipStream_t s) {
     p.N = a.P + 2 * a.L;
     p.V = a.V;
     if (p.N == 0) {
-        hipLaunchKernelGGL(ce_sum_kernel, dim3((unsigned)a.batch), dim3(64), 0, s, p);
+        hipLaunchKernelGGL(ce_sum_kernel, dim3((unsigned)a.batch), dim3(kSumThreads), 0, s, p);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)p.N, (unsigned)a.batch);
@@ -383,7 +413,7 @@ hipError_t launch_shifted_ce(const CeArgs& a, hipStream_t s) {
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ce_sum_kernel, dim3((unsigned)a.batch), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(ce_sum_kernel, dim3((unsigned)a.batch), dim3(kSumThreads), 0, s, p);
     return hipGetLastError();
 }
 
