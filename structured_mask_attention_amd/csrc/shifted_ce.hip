@@ -84,8 +84,8 @@ __device__ inline void pin_regs(uint4 (&q)[NV]) {
     for (int u = 0; u < NV; ++u) asm volatile("" : "+v"(q[u].x), "+v"(q[u].y), "+v"(q[u].z), "+v"(q[u].w));
 }
 
-// max(a, b, c) in one instruction.  The operands are finite floats made by bit moves,
-// which fmaxf would first canonicalise one by one.
+// max(a, b, c) in one instruction.  The operands are finite floats unpacked from bf16 by
+// bit moves, which fmaxf would first canonicalise one by one.
 __device__ inline float max3_raw(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
@@ -149,10 +149,7 @@ __global__ __launch_bounds__(kThreadsR) void ce_row_reg_kernel(CeParams p) {
     if (tid == 0) s_tv = (target >= 0 && target < p.V) ? __uint_as_float((uint32_t)row[target] << 16) : -INFINITY;
 
     // One pass over the vectors as they arrive: a running (max, sum of exp relative to it)
-    // per thread, rescaled once per vector.  Any offset at or near the max serves (lse = m +
-    // log sum exp(x - m) for every m), so the high entry of each pair enters the max as the
-    // whole 32-bit word, the bf16 value plus at most one bf16 ulp of low bits, which saves
-    // its unpacking there.
+    // per thread, rescaled once per vector.
     float m = -INFINITY, s = 0.f;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -160,7 +157,7 @@ __global__ __launch_bounds__(kThreadsR) void ce_row_reg_kernel(CeParams p) {
             const uint32_t wv[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
             float mn = m;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) mn = max3_raw(mn, lo_bf(wv[k]), __uint_as_float(wv[k]));
+            for (int k = 0; k < 4; ++k) mn = max3_raw(mn, lo_bf(wv[k]), hi_bf(wv[k]));
             s *= __builtin_amdgcn_exp2f((m - mn) * kLog2e);   // 0 on the first vector (m = -inf, s = 0)
             m = mn;
             const float mb = m * kLog2e;
