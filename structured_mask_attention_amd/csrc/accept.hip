@@ -47,6 +47,18 @@ struct AcceptKParams {
     float tau;
 };
 
+// Every sum of exps is taken relative to c = fl(m log2 e), the max's log2-domain image
+// rounded once to fp32: terms are exp2(fma(l, log2 e, -c)) (the product is exact inside
+// the fma, so a term near the max carries no rounding at the magnitude of the logits),
+// sums with different maxima are rescaled by exp2(c_a - c_b), and pmax = exp2(fma(m,
+// log2 e, -c)) / S undoes the rounding of c itself.
+// The product is rounded on its own (no fusing into a later subtraction), so every
+// use sees the same fp32 value of c.
+__device__ inline float exp_offset(float m) {
+#pragma clang fp contract(off)
+    return m * kLog2e;
+}
+
 struct Part {
     float m;
     float s;
@@ -65,7 +77,7 @@ __device__ inline Part merge(Part a, Part b) {
     const float lo_m = bw ? a.m : b.m;
     const float lo_s = bw ? a.s : b.s;
     const float hi_s = bw ? b.s : a.s;
-    const float scale = (lo_m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((lo_m - r.m) * kLog2e);
+    const float scale = (lo_m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(exp_offset(lo_m) - exp_offset(r.m));
     r.s = fmaf(lo_s, scale, hi_s);
     return r;
 }
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p)
 #pragma unroll
             for (int e = 6; e >= 0; --e) ee = (entry(sel, e) == cm) ? e : ee;
             x.idx = v0 + c * kChunk + 8 * (tid + kThreads * kk) + ee;
-            x.s *= __builtin_amdgcn_exp2f((x.m - cm) * kLog2e);
+            x.s *= __builtin_amdgcn_exp2f(exp_offset(x.m) - exp_offset(cm));   // 0 while x.m = -inf (s = 0)
             x.m = cm;
         }
         if constexpr (TOP2) {
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void accept_slice_kernel(AcceptKParams p)
             }
         }
         if (x.m != -INFINITY) {
-            const float mb = x.m * kLog2e;
+            const float mb = exp_offset(x.m);
             float s0 = 0.f, s1 = 0.f;
 #pragma unroll
             for (int k = 0; k < kVecPerChunk; ++k) {
@@ -269,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void accept_finish_kernel(AcceptKParams p
         }
         y = wave_reduce(y);
         if (lane == 0) {
-            const float pm = 1.f / y.s;
+            const float pm = __builtin_amdgcn_exp2f(fmaf(y.m, kLog2e, -exp_offset(y.m))) / y.s;
             p.tokens[(int64_t)b * p.W + r] = y.idx;
             if (p.pmax) p.pmax[(int64_t)b * p.W + r] = pm;
             if constexpr (MARGIN) {

@@ -66,11 +66,23 @@ __device__ inline float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff000
 constexpr int kThreadsR = 1024;   // register-resident kernel
 constexpr int kMaxVecR = 20;      // 16-byte vectors per thread: V <= 20 * 8 * 1024
 
+// Sums of exps are taken relative to c = fl(m log2 e), the max's log2-domain image rounded
+// once: terms exp2(fma(x, log2 e, -c)) (the product is exact inside the fma, so a term near
+// the max carries no rounding at the magnitude of the logits), sums over different maxima
+// rescaled by exp2(c_a - c_b), and lse2 = c + log2 S keeps c's rounding out of
+// CE = (fma(x_t, -log2 e, c) + log2 S) ln 2.
+// The product is rounded on its own (no fusing into a later subtraction), so every
+// use sees the same fp32 value of c.
+__device__ inline float exp_offset(float m) {
+#pragma clang fp contract(off)
+    return m * kLog2e;
+}
+
 // Merge two (max, sum of exp relative to that max) pairs.
 __device__ inline void merge_ms(float& ma, float& sa, float mb, float sb) {
     const float mn = fmaxf(ma, mb);
-    const float a = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ma - mn) * kLog2e);
-    const float c = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - mn) * kLog2e);
+    const float a = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(exp_offset(ma) - exp_offset(mn));
+    const float c = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(exp_offset(mb) - exp_offset(mn));
     sa = sa * a + sb * c;
     ma = mn;
 }
@@ -158,9 +170,9 @@ __global__ __launch_bounds__(kThreadsR) void ce_row_reg_kernel(CeParams p) {
             float mn = m;
 #pragma unroll
             for (int k = 0; k < 4; ++k) mn = max3_raw(mn, lo_bf(wv[k]), hi_bf(wv[k]));
-            s *= __builtin_amdgcn_exp2f((m - mn) * kLog2e);   // 0 on the first vector (m = -inf, s = 0)
+            s *= __builtin_amdgcn_exp2f(exp_offset(m) - exp_offset(mn));   // 0 on the first vector (m = -inf, s = 0)
             m = mn;
-            const float mb = m * kLog2e;
+            const float mb = exp_offset(m);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 s += __builtin_amdgcn_exp2f(fmaf(lo_bf(wv[k]), kLog2e, -mb));
@@ -177,17 +189,16 @@ __global__ __launch_bounds__(kThreadsR) void ce_row_reg_kernel(CeParams p) {
     // Workgroup max, each thread's sum moved to it (a thread without entries has s = 0 and
     // m = -inf: factor 0), workgroup sum.
     const float M = block_max(m, red_m);
-    s = block_sum(s * __builtin_amdgcn_exp2f((m - M) * kLog2e), red_s);
-    m = M;
-    const float lse = m + logf(s);
-    if (tid == 0) p.ce[(int64_t)b * p.N + r] = lse - s_tv;
+    s = block_sum(s * __builtin_amdgcn_exp2f(exp_offset(m) - exp_offset(M)), red_s);
+    const float C = exp_offset(M), ls2 = log2f(s);
+    if (tid == 0) p.ce[(int64_t)b * p.N + r] = (fmaf(s_tv, -kLog2e, C) + ls2) * kLn2;
 
     if (drow) {
-        // w * softmax = exp2(x log2e - (lse log2e - log2 w)), w in {1, 2}; the target entry
+        // w * softmax = exp2(x log2e - (lse2 - log2 w)), w in {1, 2}; the target entry
         // then gets -w, added only by the thread that holds it.
         pin_regs<NV>(q);
         const float w = w_ar + w_mask;
-        const float lb = lse * kLog2e - (w > 1.5f ? 1.f : 0.f);
+        const float lb = C + (ls2 - (w > 1.5f ? 1.f : 0.f));
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int v = tid + u * kThreadsR;
@@ -266,11 +277,11 @@ __global__ __launch_bounds__(kThreads) void ce_row_kernel(CeParams p) {
 #pragma unroll
             for (int k = 1; k < 8; ++k) vm = fmaxf(vm, x[k]);
             if (vm > m) {
-                s *= __builtin_amdgcn_exp2f((m - vm) * kLog2e);
+                s *= __builtin_amdgcn_exp2f(exp_offset(m) - exp_offset(vm));
                 m = vm;
             }
             if (m != -INFINITY) {
-                const float mb = m * kLog2e;
+                const float mb = exp_offset(m);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) s += __builtin_amdgcn_exp2f(fmaf(x[k], kLog2e, -mb));
             }
@@ -303,13 +314,13 @@ __global__ __launch_bounds__(kThreads) void ce_row_kernel(CeParams p) {
         merge_ms(m, s, red_m[k], red_s[k]);
         tv = fmaxf(tv, red_t[k]);
     }
-    const float lse = m + logf(s);
-    if (tid == 0) p.ce[(int64_t)b * p.N + r] = lse - tv;
+    const float C = exp_offset(m), ls2 = log2f(s);
+    if (tid == 0) p.ce[(int64_t)b * p.N + r] = (fmaf(tv, -kLog2e, C) + ls2) * kLn2;
 
     // Pass 2 (gradient): w * (exp(l - lse) - onehot(target)).
     if (p.dlogits) {
         const float w = w_ar + w_mask;
-        const float lb = lse * kLog2e;
+        const float lb = C + ls2;
         uint16_t* drow = p.dlogits + b * p.ds0 + (int64_t)r * p.ds1;
         for (int v = tid; v < nvec; v += kThreads) {
             const uint4 q = *reinterpret_cast<const uint4*>(row + 8 * v);

@@ -103,3 +103,18 @@ def test_accept_workspace_reuse_and_strided_rows():
     rtok, rpmax, _ = O.accept(to_np64(view), 0.95)
     assert np.array_equal(r1[0].cpu().numpy(), rtok)
     assert np.abs(r1[1].cpu().numpy() - rpmax).max() <= PMAX_ABS
+
+
+def test_accept_extreme_logits():
+    """Logits of large magnitude: a row shifted by -30000 (bf16 spacing 128 there, so the top
+    entries tie often), a row scaled by 60 (pmax at 1 to fp32 precision or split between
+    tied maxima), and a row whose maximum sits in the last vocabulary slice far above the
+    rest (the running maximum moves by thousands)."""
+    x = I.logits_inputs(2, 4, 152064, 321).float()
+    x[0, 0] -= 30000.0
+    x[0, 1] *= 60.0
+    x[0, 2, -5] = 5000.0
+    x[1, 3] = -2.0
+    x[1, 3, 17] = 1.0
+    for tau in (0.95, 0.5):
+        check_accept(x.to(torch.bfloat16), tau, f"extreme logits tau {tau}")

@@ -89,3 +89,13 @@ def test_margin_top_two_across_slices_and_ties():
     tok, mg, _ = check_margin(x, 0.1, "top-2 across slices")
     assert mg[0, 0] == 0.0 and mg[0, 2] == 0.0 and np.all(mg[1] == 0.0)
     assert tok[0].tolist() == [3, 20000, 16383, 7]
+
+
+def test_margin_extreme_logits():
+    x = I.logits_inputs(2, 4, 152064, 321).float()
+    x[0, 0] -= 30000.0
+    x[0, 1] *= 60.0
+    x[0, 2, -5] = 5000.0
+    x[1, 3] = -2.0
+    x[1, 3, 17] = 1.0
+    check_margin(x.to(torch.bfloat16), 0.3, "margin extreme logits")

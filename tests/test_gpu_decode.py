@@ -74,3 +74,25 @@ def test_decode_deterministic():
     o2 = M.mars_decode_step(*args)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("q_gain", [24.0, -24.0])
+def test_decode_large_scores_and_late_maxima(q_gain):
+    """Scores in the hundreds (Q scaled up), and the largest scores in the last chunk of a
+    long cache and in the window: the chunk and window merges must rescale by large
+    amounts, and peaked softmax rows make the output follow one or two values."""
+    batch, hq, hkv, d, W, cap = 2, 28, 4, 128, 4, 1500
+    s = I.DecodeShape("adhoc", batch, hq, hkv, d, W, cap, 0, cap, 8, 0.95, 0.5, 91)
+    x = I.decode_inputs(s, with_logits=False)
+    q = (x.q_win.float() * q_gain).to(torch.bfloat16)
+    kc = x.k_cache.float()
+    kc[:, :, 1400:1450] *= 3.0                 # late keys with larger norms (last chunk of sequence 0)
+    kc = kc.to(torch.bfloat16)
+    kw = (x.k_win.float() * 2.0).to(torch.bfloat16)
+    lens = torch.tensor([1500, 700], dtype=torch.int32)
+    print(f"case decode large scores gain={q_gain}", flush=True)
+    out = M.mars_decode_step(q.to(dev()), kw.to(dev()), x.v_win.to(dev()), kc.to(dev()), x.v_cache.to(dev()),
+                             lens.to(dev()))
+    torch.cuda.synchronize()
+    ref = O.decode(to_np64(q), to_np64(kw), to_np64(x.v_win), to_np64(kc), to_np64(x.v_cache), lens.numpy())
+    check_close(to_np64(out), ref, f"decode large scores gain {q_gain}")
