@@ -57,7 +57,7 @@ extern "C" {
 /* Status codes. */
 #define MARS_OK 0
 #define MARS_EINVAL (-1)       /* bad shape, enum, tau, null pointer, alignment or stride */
-#define MARS_EUNSUPPORTED (-2) /* valid request this build does not implement (head_dim, dtype, window) */
+#define MARS_EUNSUPPORTED (-2) /* valid request the library does not implement (head_dim, dtype, window) */
 #define MARS_EWORKSPACE (-3)   /* workspace null or smaller than the *_workspace_bytes figure */
 #define MARS_EHIP (-4)         /* the HIP runtime reported an error at launch */
 
