@@ -54,6 +54,20 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+_DESCS = {}
+
+
+def _memo(key, build):
+    """Descriptors depend only on shapes, strides and scalars: build each one once (the
+    C side copies nothing from them after the call returns, so sharing is safe)."""
+    d = _DESCS.get(key)
+    if d is None:
+        if len(_DESCS) > 512:
+            _DESCS.clear()
+        d = _DESCS[key] = build()
+    return d
+
+
 def _dtype_code(dt):
     if dt == torch.bfloat16:
         return L.MARS_DTYPE_BF16
@@ -238,10 +252,12 @@ def mars_decode_step(q_win, k_win, v_win, k_cache, v_cache, cache_len, scale=0.0
     if cache_len.dtype != torch.int32 or cache_len.shape != (b,):
         raise ValueError("cache_len must be int32 [batch]")
     out = torch.empty_like(q_win) if out is None else out
-    desc = decode_desc(b, hq, hkv, d, W, cap, scale, q_win, k_win, v_win, k_cache, v_cache, out)
-    need = mars_decode_workspace_bytes(b, hq, hkv, d, W, cap)
+    key = ("dec", b, hq, hkv, d, W, cap, float(scale), q_win.stride(), k_win.stride(), v_win.stride(),
+           k_cache.stride(), v_cache.stride(), out.stride())
+    desc = _memo(key, lambda: decode_desc(b, hq, hkv, d, W, cap, scale, q_win, k_win, v_win, k_cache, v_cache, out))
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q_win.device)
+        ws = torch.empty(max(mars_decode_workspace_bytes(b, hq, hkv, d, W, cap), 16), dtype=torch.uint8,
+                         device=q_win.device)
     _check(L.load().mars_decode_step(ctypes.byref(desc), _ptr(q_win), _ptr(k_win), _ptr(v_win), _ptr(k_cache),
                                      _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(ws), ws.numel(),
                                      _stream(q_win)), "mars_decode_step")
@@ -274,7 +290,8 @@ def mars_accept(logits, tau, ws=None, tokens=None, pmax=None, n_accept=None):
     b, W, V = logits.shape
     if logits.stride(-1) != 1:
         raise ValueError("vocab dimension must be contiguous")
-    desc = accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1))
+    desc = _memo(("acc", b, W, V, float(tau), logits.stride(0), logits.stride(1)),
+                 lambda: accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1)))
     dev = logits.device
     tokens = torch.empty((b, W), dtype=torch.int32, device=dev) if tokens is None else tokens
     pmax = torch.empty((b, W), dtype=torch.float32, device=dev) if pmax is None else pmax
@@ -295,7 +312,8 @@ def mars_accept_margin(logits, tau, ws=None, tokens=None, pmax=None, margin=None
     b, W, V = logits.shape
     if logits.stride(-1) != 1:
         raise ValueError("vocab dimension must be contiguous")
-    desc = accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1))
+    desc = _memo(("acc", b, W, V, float(tau), logits.stride(0), logits.stride(1)),
+                 lambda: accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1)))
     dev = logits.device
     tokens = torch.empty((b, W), dtype=torch.int32, device=dev) if tokens is None else tokens
     pmax = torch.empty((b, W), dtype=torch.float32, device=dev) if pmax is None else pmax
