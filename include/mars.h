@@ -263,7 +263,9 @@ typedef struct mars_ce_desc {
 int mars_shifted_ce_workspace_bytes(const mars_ce_desc* desc, size_t* bytes);
 
 /*
- * logits: bf16, finite.  tokens: int32 response tokens x, each in [0, vocab).  Outputs on
+ * logits: bf16, finite.  tokens: int32 response tokens x, each in [0, vocab) (a token
+ * outside that range is never used as an index: its terms' CE is +inf and its rows'
+ * gradient lacks the -w of the target entry).  Outputs on
  * the device: loss_mask, loss_ar fp32 [batch] (sums, summed in a fixed order); dlogits
  * (optional, may be NULL): bf16 gradient of loss_mask + loss_ar.  ws: device workspace of
  * at least mars_shifted_ce_workspace_bytes, no initialisation needed.

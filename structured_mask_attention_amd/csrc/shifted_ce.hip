@@ -359,9 +359,9 @@ __global__ __launch_bounds__(kSumThreads) void ce_sum_kernel(CeParams p) {
             c[k] = has ? p.ce[(int64_t)b * p.N + r] : 0.f;
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sa += wa[k] * c[k];
-            sm += wm[k] * c[k];
+        for (int k = 0; k < 4; ++k) {   // a zero weight adds nothing (not 0 * inf)
+            sa += wa[k] != 0.f ? wa[k] * c[k] : 0.f;
+            sm += wm[k] != 0.f ? wm[k] * c[k] : 0.f;
         }
     }
 #pragma unroll

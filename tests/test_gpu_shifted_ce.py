@@ -187,3 +187,19 @@ def test_ce_extreme_and_constant_rows():
         ref_lm, ref_la, ref_d = O.shifted_ce(zz, x, P, L, B)
         check_losses(to_np64(run[0]), to_np64(run[1]), ref_lm, ref_la, zz, x, P, L, B, f"extreme V{V}")
         check_grad(to_np64(run[2]), ref_d, zz, x, P, L, B, f"extreme V{V}")
+
+
+def test_ce_out_of_range_tokens_give_infinite_loss():
+    """Tokens outside [0, V) are compared, never used as an index: the terms they enter
+    are +inf, the other sequence's losses and every gradient stay finite."""
+    for V in (4096, 200000):
+        b, P, L, B = 2, 3, 5, 4
+        logits, tokens = I.ce_inputs(b, P, L, V, 13)
+        tokens[0, 1] = V
+        tokens[0, 2] = -1
+        lm, la, dl = M.mars_shifted_ce(logits.to(dev()), tokens.to(dev()), P, L, B, grad=True)
+        torch.cuda.synchronize()
+        assert torch.isinf(la[0]) and la[0] > 0 and torch.isinf(lm[0]) and lm[0] > 0
+        ref_lm, ref_la, _ = O.shifted_ce(to_np64(logits[1:]), tokens[1:].numpy().astype(np.int64), P, L, B)
+        assert abs(float(la[1]) - ref_la[0]) < 1e-3 and abs(float(lm[1]) - ref_lm[0]) < 1e-3
+        assert torch.isfinite(dl).all()
