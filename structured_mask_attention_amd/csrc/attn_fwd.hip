@@ -33,6 +33,7 @@
 //
 // fp32 path: one thread per query row on the vector ALUs, fp32 throughout (for fp32
 // inputs; a correctness path, not a tuned one).
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 
@@ -681,12 +682,14 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
     // fit would start only when a first-round workgroup ends (late: the oldest waves have
     // issue priority).  Those lightest items are dispatched first instead; they finish
     // early and their slots take the rest.
-    static int slot_cache[2][64];
+    // Resident-slot count per (head_dim, device), computed once; atomics because callers
+    // on several host threads may race to fill it (they all store the same value).
+    static std::atomic<int> slot_cache[2][64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     const int di = a.d == 128 ? 1 : 0;
-    int slots = (dev >= 0 && dev < 64) ? slot_cache[di][dev] : 0;
+    int slots = (dev >= 0 && dev < 64) ? slot_cache[di][dev].load(std::memory_order_relaxed) : 0;
     if (slots <= 0) {
         int cus = 0, per_cu = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -695,7 +698,7 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<64, false>, kThreads, 0);
         if (e != hipSuccess) return e;
         slots = cus * (per_cu > 0 ? per_cu : 1);
-        if (dev >= 0 && dev < 64) slot_cache[di][dev] = slots;
+        if (dev >= 0 && dev < 64) slot_cache[di][dev].store(slots, std::memory_order_relaxed);
     }
     p.lead = (grid > slots && grid < 2 * (int64_t)slots) ? (int)(grid - slots) : 0;
     const dim3 g((unsigned)grid), blk(kThreads);
