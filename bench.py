@@ -79,15 +79,20 @@ def traffic_from_profile(kernel_tag, src_file):
     return float(m_b.group(1)) if sha == m_sha.group(1) else None
 
 
+def blas_threads():
+    """Threads the oracle's NumPy BLAS actually runs with (the CPU baseline's core count)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline_train(s, budget_s=20.0):
     """fp64 oracle on whole (batch, head) slices of the training layout, FLOP_vt-scaled."""
     from oracle import mars_oracle as O
     from structured_mask_attention_amd import inputs as I
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = blas_threads()
     q, k, v = I.train_inputs(s)
     G = s.hq // s.hkv
     qn = q.float().numpy().astype(np.float64)
@@ -121,7 +126,7 @@ def cpu_baseline_decode(s, budget_s=8.0):
         toks += int(n.sum())
         seqs += 1
     dt = time.perf_counter() - t0
-    return {"value": toks / dt, "unit": "tokens/s", "kind": "oracle",
+    return {"value": toks / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{seqs} of {s.batch} sequences of the decode step + accept, fp64 NumPy, {dt:.1f} s"}
 
 
