@@ -233,10 +233,12 @@ def main():
     # KV commit (decode loop bookkeeping): timed last, on a scratch cursor array that starts at
     # 0 each group, so it writes cache rows the timed steps above have already read.
     lens_s = torch.zeros_like(dec_sets[0][5])
+    valid_s = torch.empty((sd.batch,), dtype=torch.int64, device=dev)
+    ovf_s = torch.empty((sd.batch,), dtype=torch.int32, device=dev)
 
     def commit(i):
         dq_, dk_, dv_, dkc_, dvc_, _, _ = dec_sets[i % ncopy]
-        M.mars_kv_commit(dk_, dv_, nacc, dkc_, dvc_, lens_s)
+        M.mars_kv_commit(dk_, dv_, nacc, dkc_, dvc_, lens_s, valid=valid_s, overflow=ovf_s)
 
     t_cmt = []
     for _ in range(3):

@@ -47,11 +47,19 @@ def _check(status: int, where: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # ctypes turns a Python int into the void* argument itself.
+    return None if t is None else t.data_ptr()
+
+
+# The raw handle of a device's current stream, without building a torch Stream object per
+# call (the binding's host time per call bounds back-to-back launches of short kernels).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(t):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 _DESCS = {}
@@ -332,7 +340,8 @@ def mars_kv_commit(k_win, v_win, n_accept, k_cache, v_cache, cache_len, batch_mi
     (or the batch minimum).  Returns (valid uint64-as-int64 [b], overflow int32 [b])."""
     b, W, hkv, d = k_win.shape
     cap = k_cache.shape[2]
-    desc = decode_desc(b, hkv, hkv, d, W, cap, 0.0, None, k_win, v_win, k_cache, v_cache, None)
+    key = ("commit", b, hkv, d, W, cap, k_win.stride(), v_win.stride(), k_cache.stride(), v_cache.stride())
+    desc = _memo(key, lambda: decode_desc(b, hkv, hkv, d, W, cap, 0.0, None, k_win, v_win, k_cache, v_cache, None))
     dev = k_win.device
     valid = torch.empty((b,), dtype=torch.int64, device=dev) if valid is None else valid
     overflow = torch.empty((b,), dtype=torch.int32, device=dev) if overflow is None else overflow
