@@ -65,6 +65,18 @@ def train_flops(M, s):
     return per * vis, per * nnz
 
 
+def executed_flops(M, s, tensors):
+    """FLOPs the kernel itself executes in one forward: every (packed-row block, key block)
+    tile its tile log records as visited, counted whole (QK^T and PV on the MFMA tiles, masked
+    elements included), 4 * D * rows * keys each.  One untimed run of the logging variant."""
+    q, k, v = tensors
+    rb, kb, _ = M.mars_attn_tilelog_geometry(s.batch, s.hq, s.hkv, s.d, s.P, s.L, s.B)
+    _, log = M.mars_attn_fwd_tilelog(q, k, v, s.P, s.L, s.B)
+    n = int((log > 0).sum().item())
+    del log
+    return 4.0 * s.d * rb * kb * n
+
+
 def traffic_from_profile(kernel_tag, src_file):
     """HBM bytes per launch from a committed counter summary, if the kernel source still matches."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.md")
@@ -247,6 +259,7 @@ def main():
     t_cmt = float(np.mean(t_cmt))
 
     flop_vt, flop_alg = train_flops(M, st)
+    flop_exe = executed_flops(M, st, train_sets[0])
     ta = float(np.mean(t_attn))
     tflops = flop_vt / ta / 1e12
     n_sum = int(nacc.sum().item())
@@ -315,8 +328,10 @@ def main():
             torch.cuda.synchronize()
             t2 = a2.elapsed_time(z2) * 1e-3 / reps
             fvt, falg = train_flops(M, s2)
+            fexe = executed_flops(M, s2, sets2[0])
             layouts[s2.name] = {"us": t2 * 1e6, "tflops_visible_tile": fvt / t2 / 1e12,
-                                "tflops_alg": falg / t2 / 1e12, "frac_of_peak": fvt / t2 / 1e12 / PEAK_BF16_TFLOPS}
+                                "tflops_alg": falg / t2 / 1e12, "tflops_executed": fexe / t2 / 1e12,
+                                "frac_of_peak": fvt / t2 / 1e12 / PEAK_BF16_TFLOPS}
             if not args.no_backward:
                 backward[s2.name] = time_backward(s2, sets2, reps=4)
             del sets2, q2, o2
@@ -327,7 +342,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": "attn_fwd_bf16_kernel<64>", "work_per_launch_flop_vt": flop_vt,
-                "achieved_alg": flop_alg / ta / 1e12}
+                "achieved_alg": flop_alg / ta / 1e12,
+                "work_per_launch_flop_executed": flop_exe, "achieved_executed": flop_exe / ta / 1e12}
 
     cpu = None
     cpu_dec = None
