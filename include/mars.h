@@ -29,8 +29,11 @@
  *     nothing is written.
  *   - Work is enqueued on the caller's stream and the call returns without a host sync.
  *     A device fault surfaces at the caller's next synchronisation.
- *   - The library keeps no state between calls; calls are thread-safe. Two calls that
- *     share a workspace must not run concurrently.
+ *   - Calls are thread-safe. Two calls that share a workspace must not run concurrently.
+ *     The library keeps one piece of state between calls: per device, the number of
+ *     training-forward workgroups the GPU holds at once, queried from the runtime on the
+ *     device's first mars_attn_fwd call and used only to order that kernel's work items
+ *     (which items start first); every output is the same whatever the count.
  *   - Strides are in elements. The innermost dimension (head_dim or vocab) is contiguous.
  *     Tensor base pointers must be 16-byte aligned and every stride a multiple of
  *     16 bytes worth of elements (8 for bf16, 4 for fp32); MARS_EINVAL otherwise.
@@ -304,7 +307,8 @@ int mars_kv_commit(const mars_decode_desc* desc, const void* k_win, const void* 
  * Per window row (b, i): m = max_v logit, token = lowest v with logit == m,
  * pmax = 1 / sum_v exp(logit_v - m) (temperature-1 softmax over the full vocabulary).
  * Per sequence: n_accept[b] = length of the leading run of rows with pmax >= tau,
- * at least min_accept (= 1); tau >= 1 gives exactly 1 (exact AR decoding).
+ * at least min_accept (= 1); tau = 1 gives exactly 1 (exact AR decoding, also where
+ * finite precision rounds some pmax to 1).
  * ------------------------------------------------------------------------------------ */
 typedef struct mars_accept_desc {
     int32_t batch;         /* >= 0 */
@@ -313,7 +317,7 @@ typedef struct mars_accept_desc {
     int32_t dtype;         /* MARS_DTYPE_BF16 */
     int64_t batch_stride;  /* elements between sequences */
     int64_t row_stride;    /* elements between window rows */
-    float tau;             /* 0 < tau (tau >= 1 means exact AR: one token) */
+    float tau;             /* 0 < tau <= 1, else MARS_EINVAL (tau == 1 means exact AR: one token) */
     int32_t min_accept;    /* must be 1 */
 } mars_accept_desc;
 
@@ -336,7 +340,7 @@ int mars_accept(const mars_accept_desc* desc, const void* logits, int32_t* token
  * l2 = l1) and S = sum_v exp(l_v - l1):
  *   margin = top-1 minus top-2 probability = (1 - exp(l2 - l1)) / S   (in [0, 1)),
  * and n_accept[b] = the leading run of rows with margin >= desc->tau, at least one
- * (tau >= 1: exactly one, exact AR decoding).  tokens as mars_accept; pmax (optional,
+ * (tau = 1: exactly one, exact AR decoding).  tokens as mars_accept; pmax (optional,
  * may be NULL) = 1 / S; margin fp32 [batch][window].  Same descriptor, workspace size and
  * errors as mars_accept.
  */

@@ -51,6 +51,43 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _spec_check(t, name, dtype, shape=None, contiguous=False):
+    """dtype (TypeError), shape and contiguity (ValueError) of one tensor argument."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _validate(specs):
+    """Check every tensor argument before anything reaches the C ABI: first each one's dtype,
+    shape and contiguity, then that all of them live on one device (ROCm) - the device of the
+    first.  The library reads every buffer with the element type and layout its descriptor
+    states, so a wrong dtype or a host pointer must never get that far.
+    specs: (tensor or None, name, dtype(s), shape or None, contiguous) tuples; None skipped."""
+    specs = [sp for sp in specs if sp[0] is not None]
+    for t, name, dtype, shape, contiguous in specs:
+        _spec_check(t, name, dtype, shape, contiguous)
+    dev = None
+    for t, name, *_ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device (ROCm) tensor, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+
+
+def _out(t, shape, dtype, dev):
+    """An output the kernels write densely: the caller's (validated) tensor, or a new one."""
+    return torch.empty(shape, dtype=dtype, device=dev) if t is None else t
+
+
 # The raw handle of a device's current stream, without building a torch Stream object per
 # call (the binding's host time per call bounds back-to-back launches of short kernels).
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
@@ -120,16 +157,26 @@ def attn_desc(batch, hq, hkv, d, P, Lr, B, dtype=torch.bfloat16, scale=0.0, q=No
     return desc
 
 
-def _attn_desc_from(q, k, v, o, P, Lr, B, scale):
+def _attn_specs(q, k, v, o, P, Lr, dtypes=(torch.bfloat16, torch.float32), lse=None, lse_required=False):
+    """Argument specs of the training-layout calls (shapes from q and k)."""
+    _spec_check(q, "q", dtypes)
+    _spec_check(k, "k", q.dtype)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [batch, N, n_q_heads, head_dim] and k [batch, N, n_kv_heads, head_dim]")
     b, N, hq, d = q.shape
     hkv = k.shape[2]
     if N != P + 2 * Lr:
         raise ValueError(f"sequence length {N} != P + 2L = {P + 2 * Lr}")
-    if k.shape != (b, N, hkv, d) or v.shape != k.shape or o.shape != q.shape:
-        raise ValueError("q/k/v/o shapes disagree")
-    if not (q.dtype == k.dtype == v.dtype == o.dtype):
-        raise TypeError("q/k/v/o dtypes disagree")
-    return attn_desc(b, hq, hkv, d, P, Lr, B, q.dtype, scale, q, k, v, o)
+    if lse_required and lse is None:
+        raise ValueError("lse (the forward's fp32 [b, Hq, N] log-sum-exp) is required")
+    return [(q, "q", q.dtype, None, False), (k, "k", q.dtype, (b, N, hkv, d), False),
+            (v, "v", q.dtype, (b, N, hkv, d), False), (o, "out", q.dtype, q.shape, False),
+            (lse, "lse", torch.float32, (b, hq, N), True)]
+
+
+def _attn_desc_from(q, k, v, o, P, Lr, B, scale):
+    b, N, hq, d = q.shape
+    return attn_desc(b, hq, k.shape[2], d, P, Lr, B, q.dtype, scale, q, k, v, o)
 
 
 def mars_attn_fwd(q, k, v, prompt_len, resp_len, block, scale=0.0, out=None, lse=None):
@@ -137,6 +184,7 @@ def mars_attn_fwd(q, k, v, prompt_len, resp_len, block, scale=0.0, out=None, lse
 
     ``lse``: optional fp32 [b, Hq, N] tensor to receive the log-sum-exp.  Returns ``out``.
     """
+    _validate(_attn_specs(q, k, v, out, prompt_len, resp_len, lse=lse))
     out = torch.empty_like(q) if out is None else out
     desc = _attn_desc_from(q, k, v, out, prompt_len, resp_len, block, scale)
     _check(L.load().mars_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
@@ -160,22 +208,21 @@ def mars_attn_bwd(q, k, v, o, lse, dout, prompt_len, resp_len, block, scale=0.0,
     q/k/v: the forward's inputs; o, lse: its outputs (lse fp32 [b, Hq, N]); dout like o.
     ``ws``: optional uint8 device tensor of at least mars_attn_bwd_workspace_bytes.
     """
+    specs = _attn_specs(q, k, v, o, prompt_len, resp_len, torch.bfloat16, lse=lse, lse_required=True)
+    specs[3] = (o, "o", torch.bfloat16, q.shape, False)
+    specs += [(dout, "dout", torch.bfloat16, q.shape, False), (dq, "dq", torch.bfloat16, q.shape, False),
+              (dk, "dk", torch.bfloat16, k.shape, False), (dv, "dv", torch.bfloat16, k.shape, False),
+              (ws, "ws", torch.uint8, None, False)]
+    _validate(specs)
+    desc = _attn_desc_from(q, k, v, o, prompt_len, resp_len, block, scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    desc = _attn_desc_from(q, k, v, o, prompt_len, resp_len, block, scale)
-    for name, t, ref in (("dout", dout, o), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype:
-            raise ValueError(f"{name} must match the shape and dtype of its forward tensor")
-    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() or \
-            lse.shape != (q.shape[0], q.shape[2], q.shape[1]):
-        raise ValueError("lse must be a contiguous fp32 [b, Hq, N] tensor")
     gs = L.AttnBwdStrides()
     gs.do_strides, gs.dq_strides, gs.dk_strides, gs.dv_strides = _s3(dout), _s3(dq), _s3(dk), _s3(dv)
     n = ctypes.c_size_t()
     _check(L.load().mars_attn_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "mars_attn_bwd_workspace_bytes")
-    if ws is None:
-        ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device) if ws is None else ws
     _check(L.load().mars_attn_bwd(ctypes.byref(desc), ctypes.byref(gs), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                   _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ctypes.c_size_t(ws.numel()),
                                   _stream(q)), "mars_attn_bwd")
@@ -217,6 +264,7 @@ def mars_attn_tilelog_geometry(batch, hq, hkv, d, P, Lr, B):
 
 def mars_attn_fwd_tilelog(q, k, v, prompt_len, resp_len, block, scale=0.0, out=None, lse=None):
     """bf16 forward that also returns the kernel's tile log int8 [b, Hkv, row groups, key groups]."""
+    _validate(_attn_specs(q, k, v, out, prompt_len, resp_len, torch.bfloat16, lse=lse))
     out = torch.empty_like(q) if out is None else out
     desc = _attn_desc_from(q, k, v, out, prompt_len, resp_len, block, scale)
     rb, kb, rows = mars_attn_tilelog_geometry(q.shape[0], q.shape[2], k.shape[2], q.shape[3],
@@ -253,12 +301,20 @@ def mars_decode_workspace_bytes(batch, hq, hkv, d, W, cap):
 
 def mars_decode_step(q_win, k_win, v_win, k_cache, v_cache, cache_len, scale=0.0, out=None, ws=None):
     """Window rows [b,W,Hq,D] attend to cache [b,Hkv,cap,D] prefix of cache_len[b] plus the causal window."""
+    _spec_check(q_win, "q_win", torch.bfloat16)
+    _spec_check(k_cache, "k_cache", torch.bfloat16)
+    if q_win.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q_win must be [batch, W, n_q_heads, D] and k_cache [batch, n_kv_heads, cap, D]")
     b, W, hq, d = q_win.shape
     hkv, cap = k_cache.shape[1], k_cache.shape[2]
-    if k_win.shape != (b, W, hkv, d) or v_win.shape != k_win.shape or v_cache.shape != k_cache.shape:
-        raise ValueError("decode shapes disagree")
-    if cache_len.dtype != torch.int32 or cache_len.shape != (b,):
-        raise ValueError("cache_len must be int32 [batch]")
+    _validate([(q_win, "q_win", torch.bfloat16, None, False),
+               (k_win, "k_win", torch.bfloat16, (b, W, hkv, d), False),
+               (v_win, "v_win", torch.bfloat16, (b, W, hkv, d), False),
+               (k_cache, "k_cache", torch.bfloat16, (b, hkv, cap, d), False),
+               (v_cache, "v_cache", torch.bfloat16, (b, hkv, cap, d), False),
+               (cache_len, "cache_len", torch.int32, (b,), True),
+               (out, "out", torch.bfloat16, q_win.shape, False),
+               (ws, "ws", torch.uint8, None, False)])
     out = torch.empty_like(q_win) if out is None else out
     key = ("dec", b, hq, hkv, d, W, cap, float(scale), q_win.stride(), k_win.stride(), v_win.stride(),
            k_cache.stride(), v_cache.stride(), out.stride())
@@ -295,15 +351,21 @@ def mars_accept(logits, tau, ws=None, tokens=None, pmax=None, n_accept=None):
 
     ``ws``: optional device workspace (uint8, at least mars_accept_workspace_bytes).
     """
+    _spec_check(logits, "logits", torch.bfloat16)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, W, vocab]")
     b, W, V = logits.shape
+    _validate([(logits, "logits", torch.bfloat16, None, False), (tokens, "tokens", torch.int32, (b, W), True),
+               (pmax, "pmax", torch.float32, (b, W), True), (n_accept, "n_accept", torch.int32, (b,), True),
+               (ws, "ws", torch.uint8, None, False)])
     if logits.stride(-1) != 1:
         raise ValueError("vocab dimension must be contiguous")
     desc = _memo(("acc", b, W, V, float(tau), logits.stride(0), logits.stride(1)),
                  lambda: accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1)))
     dev = logits.device
-    tokens = torch.empty((b, W), dtype=torch.int32, device=dev) if tokens is None else tokens
-    pmax = torch.empty((b, W), dtype=torch.float32, device=dev) if pmax is None else pmax
-    n_accept = torch.empty((b,), dtype=torch.int32, device=dev) if n_accept is None else n_accept
+    tokens = _out(tokens, (b, W), torch.int32, dev)
+    pmax = _out(pmax, (b, W), torch.float32, dev)
+    n_accept = _out(n_accept, (b,), torch.int32, dev)
     if ws is None:
         ws = torch.empty(max(mars_accept_workspace_bytes(b, W, V, tau), 16), dtype=torch.uint8, device=dev)
     _check(L.load().mars_accept(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(pmax), _ptr(n_accept),
@@ -317,16 +379,22 @@ def mars_accept_margin(logits, tau, ws=None, tokens=None, pmax=None, margin=None
     margin = top-1 minus top-2 probability; n_accept = leading run with margin >= tau, at
     least one.  ``ws``: optional device workspace (uint8, at least mars_accept_workspace_bytes).
     """
+    _spec_check(logits, "logits", torch.bfloat16)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, W, vocab]")
     b, W, V = logits.shape
+    _validate([(logits, "logits", torch.bfloat16, None, False), (tokens, "tokens", torch.int32, (b, W), True),
+               (pmax, "pmax", torch.float32, (b, W), True), (margin, "margin", torch.float32, (b, W), True),
+               (n_accept, "n_accept", torch.int32, (b,), True), (ws, "ws", torch.uint8, None, False)])
     if logits.stride(-1) != 1:
         raise ValueError("vocab dimension must be contiguous")
     desc = _memo(("acc", b, W, V, float(tau), logits.stride(0), logits.stride(1)),
                  lambda: accept_desc(b, W, V, tau, logits.stride(0), logits.stride(1)))
     dev = logits.device
-    tokens = torch.empty((b, W), dtype=torch.int32, device=dev) if tokens is None else tokens
-    pmax = torch.empty((b, W), dtype=torch.float32, device=dev) if pmax is None else pmax
-    margin = torch.empty((b, W), dtype=torch.float32, device=dev) if margin is None else margin
-    n_accept = torch.empty((b,), dtype=torch.int32, device=dev) if n_accept is None else n_accept
+    tokens = _out(tokens, (b, W), torch.int32, dev)
+    pmax = _out(pmax, (b, W), torch.float32, dev)
+    margin = _out(margin, (b, W), torch.float32, dev)
+    n_accept = _out(n_accept, (b,), torch.int32, dev)
     if ws is None:
         ws = torch.empty(max(mars_accept_workspace_bytes(b, W, V, tau), 16), dtype=torch.uint8, device=dev)
     _check(L.load().mars_accept_margin(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(pmax), _ptr(margin),
@@ -338,13 +406,24 @@ def mars_kv_commit(k_win, v_win, n_accept, k_cache, v_cache, cache_len, batch_mi
     """Append accepted window K/V ([b, W, Hkv, D]) to the caches ([b, Hkv, cap, D]) at the
     cursors ``cache_len`` (int32 [b], updated in place) and advance them by n_accept[b]
     (or the batch minimum).  Returns (valid uint64-as-int64 [b], overflow int32 [b])."""
+    _spec_check(k_win, "k_win", torch.bfloat16)
+    _spec_check(k_cache, "k_cache", torch.bfloat16)
+    if k_win.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("k_win must be [batch, W, n_kv_heads, D] and k_cache [batch, n_kv_heads, cap, D]")
     b, W, hkv, d = k_win.shape
     cap = k_cache.shape[2]
+    _validate([(k_win, "k_win", torch.bfloat16, None, False),
+               (v_win, "v_win", torch.bfloat16, (b, W, hkv, d), False),
+               (n_accept, "n_accept", torch.int32, (b,), True),
+               (k_cache, "k_cache", torch.bfloat16, (b, hkv, cap, d), False),
+               (v_cache, "v_cache", torch.bfloat16, (b, hkv, cap, d), False),
+               (cache_len, "cache_len", torch.int32, (b,), True),
+               (valid, "valid", torch.int64, (b,), True), (overflow, "overflow", torch.int32, (b,), True)])
     key = ("commit", b, hkv, d, W, cap, k_win.stride(), v_win.stride(), k_cache.stride(), v_cache.stride())
     desc = _memo(key, lambda: decode_desc(b, hkv, hkv, d, W, cap, 0.0, None, k_win, v_win, k_cache, v_cache, None))
     dev = k_win.device
-    valid = torch.empty((b,), dtype=torch.int64, device=dev) if valid is None else valid
-    overflow = torch.empty((b,), dtype=torch.int32, device=dev) if overflow is None else overflow
+    valid = _out(valid, (b,), torch.int64, dev)
+    overflow = _out(overflow, (b,), torch.int32, dev)
     policy = L.MARS_COMMIT_BATCH_MIN if batch_min else L.MARS_COMMIT_PER_SAMPLE
     _check(L.load().mars_kv_commit(ctypes.byref(desc), _ptr(k_win), _ptr(v_win), _ptr(n_accept), _ptr(k_cache),
                                    _ptr(v_cache), _ptr(cache_len), _ptr(valid), _ptr(overflow), policy,
@@ -368,18 +447,24 @@ def ce_desc(batch, P, Lr, B, V, logits=None, dlogits=None, tokens=None):
 def mars_shifted_ce(logits, tokens, prompt_len, resp_len, block, grad=False, dlogits=None, ws=None):
     """L_mask, L_AR (fp32 [b] each) of logits bf16 [b, N, V] for response tokens int32
     [b, L]; with ``grad`` also dlogits bf16 [b, N, V].  Returns (loss_mask, loss_ar, dlogits)."""
+    _spec_check(logits, "logits", torch.bfloat16)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, N, vocab]")
     b, N, V = logits.shape
-    if logits.stride(-1) != 1 or tokens.stride(-1) != 1:
-        raise ValueError("vocab and token dimensions must be contiguous")
+    if N != prompt_len + 2 * resp_len:
+        raise ValueError(f"logits rows {N} != P + 2L = {prompt_len + 2 * resp_len}")
+    _validate([(logits, "logits", torch.bfloat16, None, False), (tokens, "tokens", torch.int32, (b, resp_len), False),
+               (dlogits, "dlogits", torch.bfloat16, logits.shape, False), (ws, "ws", torch.uint8, None, False)])
     dev = logits.device
+    if logits.stride(-1) != 1 or tokens.stride(-1) != 1 or (dlogits is not None and dlogits.stride(-1) != 1):
+        raise ValueError("vocab and token dimensions must be contiguous")
     if grad and dlogits is None:
         dlogits = torch.empty_like(logits)
     desc = ce_desc(b, prompt_len, resp_len, block, V, logits, dlogits, tokens)
     n = ctypes.c_size_t()
     _check(L.load().mars_shifted_ce_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
            "mars_shifted_ce_workspace_bytes")
-    if ws is None:
-        ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev) if ws is None else ws
     lm = torch.empty((b,), dtype=torch.float32, device=dev)
     la = torch.empty((b,), dtype=torch.float32, device=dev)
     _check(L.load().mars_shifted_ce(ctypes.byref(desc), _ptr(logits), _ptr(tokens), _ptr(lm), _ptr(la),

@@ -1,6 +1,7 @@
 // C ABI of libmars (include/mars.h): argument validation, then kernel launches on the
 // caller's stream.  Validation is complete before anything is launched, so an error
-// leaves every buffer untouched.  Nothing here allocates device memory or keeps state.
+// leaves every buffer untouched.  Nothing here allocates device memory; the only state the
+// library keeps is the forward launcher's per-device count of resident workgroups.
 #include <math.h>
 #include <stdint.h>
 
@@ -334,7 +335,7 @@ static int check_accept_desc(const mars_accept_desc* d) {
     if (d->window > 64) return MARS_EUNSUPPORTED;
     if (d->vocab > 65535 * 8192) return MARS_EUNSUPPORTED;
     if (d->dtype != MARS_DTYPE_BF16) return d->dtype == MARS_DTYPE_FP32 ? MARS_EUNSUPPORTED : MARS_EINVAL;
-    if (!(d->tau > 0.f) || !isfinite(d->tau)) return MARS_EINVAL;
+    if (!(d->tau > 0.f && d->tau <= 1.f)) return MARS_EINVAL;   // (0, 1]; NaN fails too
     if (d->min_accept != 1) return MARS_EINVAL;
     if (d->batch > 65535) return MARS_EUNSUPPORTED;
     return MARS_OK;

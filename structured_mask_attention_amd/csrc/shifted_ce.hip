@@ -231,9 +231,10 @@ hipError_t launch_reg(const CeParams& p, dim3 grid, hipStream_t s) {
 
 template <int... I>
 hipError_t launch_reg_nv(int nv, const CeParams& p, dim3 grid, hipStream_t s, std::integer_sequence<int, I...>) {
+    // The instantiation whose vector count matches nv launches; the fold stops there.
     hipError_t e = hipErrorInvalidValue;
-    ((nv == I + 1 ? (e = launch_reg<I + 1>(p, grid, s), true) : false) || ...);
-    return e;
+    const bool launched = ((nv == I + 1 ? (e = launch_reg<I + 1>(p, grid, s), true) : false) || ...);
+    return launched ? e : hipErrorInvalidValue;
 }
 
 __global__ __launch_bounds__(kThreads) void ce_row_kernel(CeParams p) {

@@ -167,3 +167,103 @@ def check_bounded(got, ref, bound, what, extra_rel=2.0 ** -8):
           f"max err/bound={ratio:.3f}", flush=True)
     assert ratio <= 1.0, f"{what}: error exceeds its bound (ratio {ratio:.3f})"
     return ratio
+
+
+def expected_tilelog_intervals(P, L, B, G, row_block, key_block):
+    """:func:`expected_tilelog` built from the oracle's two-interval row encoding instead of
+    the dense mask, so it scales to long layouts (N = 15360 and beyond).
+
+    Row r sees [0, hi1) and [lo2, r] (oracle ``row_intervals``).  A key group [kb, ke) with
+    its in-range part [kb, min(ke, N)) is visited by a row group iff some row of the group
+    sees a key of it, and needs no element mask iff every row sees every key of it and
+    ke <= N.  The two intervals of a row never touch when both are non-empty (L >= 1 puts
+    the clean stream between them), so "every key" is "inside one interval".
+    """
+    N = P + 2 * L
+    R = N * G
+    nrg = -(-R // row_block)
+    nkt = -(-N // key_block)
+    kb = np.arange(nkt, dtype=np.int64) * key_block
+    ke = np.minimum(kb + key_block, N)                # in-range end
+    out = np.zeros((nrg, nkt), dtype=np.int8)
+    for rg in range(nrg):
+        pos = np.unique(np.arange(rg * row_block, min(R, (rg + 1) * row_block)) // G)
+        hi1, lo2 = O.row_intervals(P, L, B, pos)
+        r = pos[:, None]
+        hi1, lo2 = hi1[:, None], lo2[:, None]
+        any_ = (kb[None, :] < hi1) | (np.maximum(kb[None, :], lo2) <= np.minimum(ke[None, :] - 1, r))
+        all_ = (ke[None, :] <= hi1) | ((kb[None, :] >= lo2) & (ke[None, :] - 1 <= r))
+        vis = any_.any(axis=0)
+        full = all_.all(axis=0) & (kb + key_block <= N)
+        out[rg] = np.where(vis, np.where(full, 2, 1), 0)
+    return out
+
+
+def oracle_attn_slices(q, k, v, P, L, B, pairs, threads=None):
+    """The oracle's attention for the (batch, query head) slices in ``pairs``, one slice per
+    task on a thread pool (the oracle's large NumPy operations release the GIL; BLAS is held
+    to one thread per task).  q/k/v: float64 arrays [b, N, H, D].
+    Returns {(b, h): (O [N, D], LSE [N])}."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    G = q.shape[2] // k.shape[2]
+
+    def one(bh):
+        bi, h = bh
+        o, lse = O.attn(q[bi:bi + 1, :, h:h + 1], k[bi:bi + 1, :, h // G:h // G + 1],
+                        v[bi:bi + 1, :, h // G:h // G + 1], P, L, B)
+        return bh, (o[0, :, 0], lse[0, 0])
+
+    n = threads or min(16, max(1, (__import__("os").cpu_count() or 2)))
+    with threadpool_limits(1), ThreadPoolExecutor(n) as ex:
+        return dict(ex.map(one, list(pairs)))
+
+
+def lse_bound_slices(q, k, pairs, scale=None, threads=None):
+    """:func:`lse_bound` per (batch, query head) slice on a thread pool: {(b, h): bound [N]}."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    qa, ka = np.abs(q), np.abs(k)
+    b, N, hq, d = qa.shape
+    G = hq // ka.shape[2]
+    c = (1.0 / np.sqrt(d) if scale is None else scale) * np.log2(np.e)
+    u = 2.0 ** -8
+
+    def one(bh):
+        bi, h = bh
+        m = np.empty(N)
+        for r0 in range(0, N, 2048):
+            m[r0:r0 + 2048] = (qa[bi, r0:r0 + 2048, h, :] @ ka[bi, :, h // G, :].T).max(axis=1)
+        return bh, u + np.log(2.0) * u * c * m + 1e-5
+
+    n = threads or min(16, max(1, (__import__("os").cpu_count() or 2)))
+    with threadpool_limits(1), ThreadPoolExecutor(n) as ex:
+        return dict(ex.map(one, list(pairs)))
+
+
+def tie_zone_width(gate_kernel, gate64, tau):
+    """Half-width of the band around tau inside which the kernel's decision may differ from
+    the oracle's: the largest measured |gate_kernel - gate_oracle| over all rows plus the
+    rounding of tau to fp32 (the kernel compares fp32 values).  A row farther from tau than
+    this is decided the same way on both sides."""
+    err = float(np.max(np.abs(np.asarray(gate_kernel, dtype=np.float64) - gate64))) if np.size(gate64) else 0.0
+    return err + abs(float(np.float32(tau)) - tau)
+
+
+def tie_zone_sequences(gate64, tau, width=TIE_ZONE):
+    """Sequences whose acceptance count depends on a row whose gate value (the oracle's pmax or
+    margin) lies within `width` of tau: the rows that decide n are the leading run of rows
+    with gate >= tau and the first row after it; a later row cannot change n.  With tau >= 1
+    exactly one token is accepted whatever the rows hold, so nothing is in the zone."""
+    gate64 = np.asarray(gate64, dtype=np.float64)
+    b, W = gate64.shape
+    tie = np.zeros(b, dtype=bool)
+    if tau >= 1.0:
+        return tie
+    for bi in range(b):
+        run = 0
+        while run < W and gate64[bi, run] >= tau:
+            run += 1
+        deciding = gate64[bi, :min(run + 1, W)]
+        tie[bi] = bool(np.any(np.abs(deciding - tau) <= width))
+    return tie

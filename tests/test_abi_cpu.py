@@ -180,13 +180,18 @@ def test_accept_validation_errors():
         return lib.mars_accept(ctypes.byref(d), ptr, ptr, ptr, ptr, ws, ws_bytes, None)
 
     for field, val, code in [("tau", 0.0, L.MARS_EINVAL), ("tau", -0.5, L.MARS_EINVAL),
-                             ("tau", float("inf"), L.MARS_EINVAL), ("min_accept", 2, L.MARS_EINVAL),
+                             ("tau", float("inf"), L.MARS_EINVAL), ("tau", 1.0000002, L.MARS_EINVAL),
+                             ("tau", 2.0, L.MARS_EINVAL), ("tau", float("nan"), L.MARS_EINVAL),
+                             ("min_accept", 2, L.MARS_EINVAL),
                              ("window", 65, L.MARS_EUNSUPPORTED), ("window", 0, L.MARS_EINVAL),
                              ("vocab", 0, L.MARS_EINVAL),
                              ("dtype", L.MARS_DTYPE_FP32, L.MARS_EUNSUPPORTED)]:
         d = good()
         setattr(d, field, val)
         assert call(d) == code, field
+    d = good(); d.tau = 1.0                               # tau = 1 (exact AR) is inside the range
+    n = ctypes.c_size_t()
+    assert lib.mars_accept_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == L.MARS_OK
     d = good(); d.row_stride = 152063                     # rows lose 16-byte alignment
     assert call(d) == L.MARS_EINVAL
     assert call(good(), ptr=MISALIGNED) == L.MARS_EINVAL
@@ -205,7 +210,7 @@ def test_accept_margin_validation_errors():
     def call(d, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE, pmax=FAKE, margin=FAKE):
         return lib.mars_accept_margin(ctypes.byref(d), ptr, ptr, pmax, margin, ptr, ws, ws_bytes, None)
 
-    for field, val, code in [("tau", 0.0, L.MARS_EINVAL), ("min_accept", 2, L.MARS_EINVAL),
+    for field, val, code in [("tau", 0.0, L.MARS_EINVAL), ("tau", 1.5, L.MARS_EINVAL), ("min_accept", 2, L.MARS_EINVAL),
                              ("window", 65, L.MARS_EUNSUPPORTED), ("dtype", L.MARS_DTYPE_FP32, L.MARS_EUNSUPPORTED)]:
         d = good()
         setattr(d, field, val)

@@ -1,8 +1,10 @@
 """GPU parity of mars_accept against the fp64 oracle.
 
-Tokens (argmax) and n_accept are compared bit for bit; pmax within 1e-5.  The tau
-decision is taken in the kernel's precision (fp32 pmax against fp32 tau) on both sides;
-a row whose oracle pmax lies within 1e-5 of tau is a tie-zone row: reported, not failed.
+Tokens (argmax) and n_accept are compared bit for bit with the oracle's own outputs; pmax
+within 1e-5.  A sequence is left out of the n_accept comparison only when a row that decides
+its count (the leading run of rows with pmax >= tau and the first row after it) has an
+oracle pmax closer to tau than the measured pmax error (plus tau's fp32 rounding), so that the
+two sides may decide it differently; the number left out is asserted (0 on the full workload).
 """
 import numpy as np
 import pytest
@@ -11,26 +13,13 @@ import torch
 import structured_mask_attention_amd as M
 from oracle import mars_oracle as O
 from structured_mask_attention_amd import inputs as I
-from tests.gpu_helpers import PMAX_ABS, TIE_ZONE, dev, to_np64
+from tests.gpu_helpers import PMAX_ABS, dev, tie_zone_sequences, tie_zone_width, to_np64
 
 pytestmark = pytest.mark.gpu
 
 
-def expected_n(pmax64, tau):
-    """tau-prefix on the oracle's pmax, decided in fp32 like the kernel."""
-    p32 = pmax64.astype(np.float32)
-    t32 = np.float32(tau)
-    n = np.zeros(p32.shape[0], dtype=np.int32)
-    for b in range(p32.shape[0]):
-        run = 0
-        if tau < 1.0:
-            while run < p32.shape[1] and p32[b, run] >= t32:
-                run += 1
-        n[b] = max(1, run)
-    return n
 
-
-def check_accept(logits_cpu, tau, what, ws=None):
+def check_accept(logits_cpu, tau, what, ws=None, max_tie=0):
     if logits_cpu.is_contiguous():
         lg = logits_cpu.to(dev())
     else:   # keep the strided layout on the device
@@ -40,29 +29,44 @@ def check_accept(logits_cpu, tau, what, ws=None):
         lg = torch.as_strided(base.to(dev()), logits_cpu.shape, logits_cpu.stride(), logits_cpu.storage_offset())
     tok, pmax, n = M.mars_accept(lg, tau, ws=ws)
     torch.cuda.synchronize()
-    rtok, rpmax, _ = O.accept(to_np64(logits_cpu), tau)
-    rn = expected_n(rpmax, tau)
+    rtok, rpmax, rn = O.accept(to_np64(logits_cpu), tau)
     tok, pmax, n = tok.cpu().numpy(), pmax.cpu().numpy().astype(np.float64), n.cpu().numpy()
     assert np.array_equal(tok, rtok), f"{what}: argmax differs at {np.argwhere(tok != rtok)[:5]}"
     err = np.abs(pmax - rpmax).max()
     print(f"[{what}] pmax max_abs={err:.3e} n={n.tolist()[:8]}...", flush=True)
     assert err <= PMAX_ABS
-    tie = np.abs(rpmax - tau).min(axis=1) <= TIE_ZONE
-    if tie.any():
-        print(f"[{what}] tie-zone sequences (reported, not failed): {np.nonzero(tie)[0].tolist()}", flush=True)
-    assert np.array_equal(n[~tie], rn[~tie]), f"{what}: n_accept differs"
+    tie = tie_zone_sequences(rpmax, tau, tie_zone_width(pmax, rpmax, tau))
+    print(f"[{what}] tie-zone sequences left out of the n_accept comparison: {np.nonzero(tie)[0].tolist()}",
+          flush=True)
+    assert int(tie.sum()) <= max_tie, f"{what}: {int(tie.sum())} tie-zone sequences (at most {max_tie} expected)"
+    assert np.array_equal(n[~tie], rn[~tie]), f"{what}: n_accept differs at {np.nonzero(n != rn)[0].tolist()}"
     return tok, pmax, n
 
 
-@pytest.mark.parametrize("tau", [0.95, 1.0, 1e-9, 0.5, 2.0])
+@pytest.mark.parametrize("tau", [0.95, 1.0, 1e-9, 0.5])
 def test_accept_full_workload(tau):
+    """The full decode workload: no sequence of the seeded draw has a deciding row in the tie
+    zone at these thresholds, so every n_accept is compared."""
     s = I.DECODE7B
     logits = I.logits_inputs(s.batch, s.W, s.vocab, seed=s.seed)
-    _, pmax, n = check_accept(logits, tau, f"accept 7B tau={tau}")
+    _, pmax, n = check_accept(logits, tau, f"accept 7B tau={tau}", max_tie=0)
     if tau >= 1.0:
         assert (n == 1).all()
     if tau <= 1.0 / s.vocab:
         assert (n == s.W).all()
+
+
+@pytest.mark.parametrize("tau", [2.0, 0.0, -0.5, float("nan"), float("inf")])
+def test_accept_tau_outside_unit_interval_is_rejected(tau):
+    """tau must lie in (0, 1]: the call fails before any launch and leaves the outputs alone."""
+    s = I.DECODE7B
+    lg = I.logits_inputs(2, s.W, 1000, seed=3).to(dev())
+    n = torch.full((2,), -7, dtype=torch.int32, device=dev())
+    with pytest.raises(M.MarsError) as ei:
+        M.mars_accept(lg, tau, n_accept=n)
+    assert ei.value.status == -1
+    torch.cuda.synchronize()
+    assert (n == -7).all()
 
 
 @pytest.mark.parametrize("batch,W,V", [(3, 4, 1001), (2, 1, 7), (2, 7, 8193), (1, 64, 300), (5, 5, 1), (2, 3, 16384)])
@@ -72,7 +76,7 @@ def test_accept_shapes(batch, W, V):
     Vp = -(-V // 8) * 8
     padded = torch.full((batch, W, Vp), 30.0, dtype=torch.bfloat16)   # pad would win any argmax
     padded[:, :, :V] = logits
-    check_accept(padded[:, :, :V], 0.6, f"accept b{batch} W{W} V{V}")
+    check_accept(padded[:, :, :V], 0.6, f"accept b{batch} W{W} V{V}", max_tie=1)
 
 
 def test_accept_ties_take_lowest_index():
@@ -84,7 +88,7 @@ def test_accept_ties_take_lowest_index():
     x[1, 0, [16385, 16384]] = 1.0
     x[1, 1, [0, 1]] = 3.0
     x[1, 2, [19999]] = 3.0
-    tok, _, _ = check_accept(x, 0.9, "ties")
+    tok, _, _ = check_accept(x, 0.9, "ties", max_tie=0)
     assert tok.tolist() == [[17, 8191, 0], [16384, 0, 19999]]
 
 
@@ -117,4 +121,4 @@ def test_accept_extreme_logits():
     x[1, 3] = -2.0
     x[1, 3, 17] = 1.0
     for tau in (0.95, 0.5):
-        check_accept(x.to(torch.bfloat16), tau, f"extreme logits tau {tau}")
+        check_accept(x.to(torch.bfloat16), tau, f"extreme logits tau {tau}", max_tie=1)

@@ -1,8 +1,10 @@
 """GPU parity of mars_accept_margin (the margin gate) against the fp64 oracle.
 
-Tokens and n_accept bit for bit, margin and pmax within 1e-5; the gate decision is taken in
-fp32 on both sides, and a sequence whose oracle margin lies within 1e-5 of tau in some row
-is a tie-zone sequence: reported, not failed.
+Tokens and n_accept bit for bit with the oracle's own outputs, margin and pmax within 1e-5.  A
+sequence is left out of the n_accept comparison only when a row that decides its count (the
+leading run of rows with margin >= tau and the first row after it) has an oracle margin closer to
+tau than the measured margin error (plus tau's fp32 rounding), so that the two sides may decide it
+differently; the number left out is asserted (0 on the full workload).
 """
 import numpy as np
 import pytest
@@ -11,25 +13,13 @@ import torch
 import structured_mask_attention_amd as M
 from oracle import mars_oracle as O
 from structured_mask_attention_amd import inputs as I
-from tests.gpu_helpers import PMAX_ABS, TIE_ZONE, dev, to_np64
+from tests.gpu_helpers import PMAX_ABS, dev, tie_zone_sequences, tie_zone_width, to_np64
 
 pytestmark = pytest.mark.gpu
 
 
-def expected_n(gate64, tau):
-    g32 = gate64.astype(np.float32)
-    t32 = np.float32(tau)
-    n = np.zeros(g32.shape[0], dtype=np.int32)
-    for b in range(g32.shape[0]):
-        run = 0
-        if tau < 1.0:
-            while run < g32.shape[1] and g32[b, run] >= t32:
-                run += 1
-        n[b] = max(1, run)
-    return n
 
-
-def check_margin(logits_cpu, tau, what):
+def check_margin(logits_cpu, tau, what, max_tie=0):
     if logits_cpu.is_contiguous():
         lg = logits_cpu.to(dev())
     else:   # keep the strided (row-padded) layout on the device
@@ -39,18 +29,20 @@ def check_margin(logits_cpu, tau, what):
         lg = torch.as_strided(base.to(dev()), logits_cpu.shape, logits_cpu.stride(), logits_cpu.storage_offset())
     tok, pmax, mg, n = M.mars_accept_margin(lg, tau)
     torch.cuda.synchronize()
-    rtok, rpmax, rmg, _ = O.accept_margin(to_np64(logits_cpu), tau)
-    rn = expected_n(rmg, tau)
+    rtok, rpmax, rmg, rn = O.accept_margin(to_np64(logits_cpu), tau)
     tok, pmax, mg, n = (t.cpu().numpy() for t in (tok, pmax, mg, n))
     assert np.array_equal(tok, rtok), f"{what}: argmax differs at {np.argwhere(tok != rtok)[:5]}"
     e_m = np.abs(mg.astype(np.float64) - rmg).max()
     e_p = np.abs(pmax.astype(np.float64) - rpmax).max()
     print(f"[{what}] margin max_abs={e_m:.3e} pmax max_abs={e_p:.3e} n={n.tolist()[:8]}...", flush=True)
     assert e_m <= PMAX_ABS and e_p <= PMAX_ABS
-    tie = np.abs(rmg - tau).min(axis=1) <= TIE_ZONE
-    if tie.any():
-        print(f"[{what}] tie-zone sequences (reported, not failed): {np.nonzero(tie)[0].tolist()}", flush=True)
-    assert np.array_equal(n[~tie], rn[~tie]), f"{what}: n_accept differs"
+    # A tied maximum gives margin exactly 0 on both sides (the kernel forms 1 - exp(0) = 0), so
+    # those rows are decided exactly: they never count as tie-zone rows.
+    tie = tie_zone_sequences(np.where(rmg == 0.0, -np.inf, rmg), tau, tie_zone_width(mg, rmg, tau))
+    print(f"[{what}] tie-zone sequences left out of the n_accept comparison: {np.nonzero(tie)[0].tolist()}",
+          flush=True)
+    assert int(tie.sum()) <= max_tie, f"{what}: {int(tie.sum())} tie-zone sequences (at most {max_tie} expected)"
+    assert np.array_equal(n[~tie], rn[~tie]), f"{what}: n_accept differs at {np.nonzero(n != rn)[0].tolist()}"
     return tok, mg, n
 
 
@@ -71,7 +63,7 @@ def test_margin_shapes(batch, W, V):
     Vp = -(-V // 8) * 8
     padded = torch.full((batch, W, Vp), 30.0, dtype=torch.bfloat16)   # pad would win any max
     padded[:, :, :V] = logits
-    check_margin(padded[:, :, :V], 0.4, f"margin b{batch} W{W} V{V}")
+    check_margin(padded[:, :, :V], 0.4, f"margin b{batch} W{W} V{V}", max_tie=1)
 
 
 def test_margin_top_two_across_slices_and_ties():
@@ -98,4 +90,4 @@ def test_margin_extreme_logits():
     x[0, 2, -5] = 5000.0
     x[1, 3] = -2.0
     x[1, 3, 17] = 1.0
-    check_margin(x.to(torch.bfloat16), 0.3, "margin extreme logits")
+    check_margin(x.to(torch.bfloat16), 0.3, "margin extreme logits", max_tie=1)
