@@ -24,16 +24,18 @@
  *   - Every call returns an int status: MARS_OK (0) or a negative MARS_E* code.
  *   - Descriptors live in host memory and are read during the call only.
  *   - Tensor pointers are device pointers owned by the caller. The library never
- *     allocates, frees or keeps them. Scratch memory comes in as a caller workspace.
+ *     allocates, frees or keeps them. Scratch memory comes in as a caller workspace, except
+ *     for mars_decode_step_noalloc, which uses a fixed array of the library's own.
  *   - Validation is complete before any launch: on an error nothing is launched and
  *     nothing is written.
  *   - Work is enqueued on the caller's stream and the call returns without a host sync.
  *     A device fault surfaces at the caller's next synchronisation.
  *   - Calls are thread-safe. Two calls that share a workspace must not run concurrently.
- *     The library keeps one piece of state between calls: per device, the number of
+ *     The library keeps two pieces of state between calls, both per device: the number of
  *     training-forward workgroups the GPU holds at once, queried from the runtime on the
  *     device's first mars_attn_fwd call and used only to order that kernel's work items
- *     (which items start first); every output is the same whatever the count.
+ *     (which items start first; every output is the same whatever the count), and the
+ *     device address of mars_decode_step_noalloc's scratch array (see there).
  *   - Strides are in elements. The innermost dimension (head_dim or vocab) is contiguous.
  *     Tensor base pointers must be 16-byte aligned and every stride a multiple of
  *     16 bytes worth of elements (8 for bf16, 4 for fp32); MARS_EINVAL otherwise.
@@ -236,6 +238,29 @@ int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void
                      const void* v_win, const void* k_cache, const void* v_cache,
                      const int32_t* cache_len, void* o, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/*
+ * mars_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same descriptor, inputs,
+ * output and result as mars_decode_step, but the chunk partials live in a scratch array the
+ * library holds on each device it runs on, from the device's first call until the process
+ * ends; nothing is allocated or freed by the call.
+ *   - The workspace mars_decode_workspace_bytes reports for desc must not exceed the
+ *     array's size (mars_decode_scratch_bytes: 32 MiB; e.g. 32 sequences x 4 KV heads x
+ *     28 query rows (7 heads x 4 window rows) of head_dim 128 fit up to a cache capacity of
+ *     9216 positions), else MARS_EWORKSPACE and nothing is launched.
+ *   - Every call on one device shares that device's array: calls that overlap on one GPU
+ *     (other streams, other host threads) race and must be ordered by the caller.  The
+ *     array needs no initialisation; a call overwrites what it reads.
+ *   - The device's first call looks up the array's address (hipGetSymbolAddress); a
+ *     runtime error there is MARS_EHIP.
+ */
+int mars_decode_step_noalloc(const mars_decode_desc* desc, const void* q_win, const void* k_win,
+                             const void* v_win, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_len, void* o, hipStream_t stream);
+
+/* Size in bytes of mars_decode_step_noalloc's per-device scratch array. */
+int mars_decode_scratch_bytes(size_t* bytes);
 
 /* ------------------------------------------------------------------------------------
  * Training loss over the vocabulary (MARS §3.2 Eq. 3 and §3.3 Eq. 5): L = L_mask + L_AR

@@ -26,6 +26,8 @@ __all__ = [
     "mars_attn_bwd",
     "mars_decode_workspace_bytes",
     "mars_decode_step",
+    "mars_decode_step_noalloc",
+    "mars_decode_scratch_bytes",
     "mars_accept_workspace_bytes",
     "mars_accept",
     "mars_accept_margin",
@@ -325,6 +327,40 @@ def mars_decode_step(q_win, k_win, v_win, k_cache, v_cache, cache_len, scale=0.0
     _check(L.load().mars_decode_step(ctypes.byref(desc), _ptr(q_win), _ptr(k_win), _ptr(v_win), _ptr(k_cache),
                                      _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(ws), ws.numel(),
                                      _stream(q_win)), "mars_decode_step")
+    return out
+
+
+def mars_decode_scratch_bytes():
+    """Size of the per-device scratch array of :func:`mars_decode_step_noalloc`."""
+    n = ctypes.c_size_t()
+    _check(L.load().mars_decode_scratch_bytes(ctypes.byref(n)), "mars_decode_scratch_bytes")
+    return n.value
+
+
+def mars_decode_step_noalloc(q_win, k_win, v_win, k_cache, v_cache, cache_len, scale=0.0, out=None):
+    """:func:`mars_decode_step` without a workspace: the library keeps the chunk partials in
+    its own per-device scratch array (for callers that cannot allocate).  ``out`` must be
+    given when the caller cannot allocate either (otherwise one is made here)."""
+    _spec_check(q_win, "q_win", torch.bfloat16)
+    _spec_check(k_cache, "k_cache", torch.bfloat16)
+    if q_win.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q_win must be [batch, W, n_q_heads, D] and k_cache [batch, n_kv_heads, cap, D]")
+    b, W, hq, d = q_win.shape
+    hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    _validate([(q_win, "q_win", torch.bfloat16, None, False),
+               (k_win, "k_win", torch.bfloat16, (b, W, hkv, d), False),
+               (v_win, "v_win", torch.bfloat16, (b, W, hkv, d), False),
+               (k_cache, "k_cache", torch.bfloat16, (b, hkv, cap, d), False),
+               (v_cache, "v_cache", torch.bfloat16, (b, hkv, cap, d), False),
+               (cache_len, "cache_len", torch.int32, (b,), True),
+               (out, "out", torch.bfloat16, q_win.shape, False)])
+    out = torch.empty_like(q_win) if out is None else out
+    key = ("dec", b, hq, hkv, d, W, cap, float(scale), q_win.stride(), k_win.stride(), v_win.stride(),
+           k_cache.stride(), v_cache.stride(), out.stride())
+    desc = _memo(key, lambda: decode_desc(b, hq, hkv, d, W, cap, scale, q_win, k_win, v_win, k_cache, v_cache, out))
+    _check(L.load().mars_decode_step_noalloc(ctypes.byref(desc), _ptr(q_win), _ptr(k_win), _ptr(v_win),
+                                             _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(out),
+                                             _stream(q_win)), "mars_decode_step_noalloc")
     return out
 
 

@@ -78,6 +78,8 @@ _SIGNATURES = {
                                      P, P, P, P, ctypes.c_size_t, P]),
     "mars_decode_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_decode_step": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    "mars_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P]),
+    "mars_decode_scratch_bytes": (ctypes.c_int, [ctypes.POINTER(ctypes.c_size_t)]),
     "mars_kv_commit": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P, ctypes.c_int32, P]),
     "mars_shifted_ce_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(CeDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "mars_shifted_ce": (ctypes.c_int, [ctypes.POINTER(CeDesc), P, P, P, P, P, P, ctypes.c_size_t, P]),

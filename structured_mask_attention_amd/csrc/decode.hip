@@ -15,6 +15,7 @@
 //      products per row) and a log-sum-exp merge of the chunk partials.
 // Chunks past a sequence's length exit at once, so the grid is fixed while the work is
 // ragged; the cache is read exactly once.
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 
@@ -448,6 +449,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeKParams p) {
 
 }  // namespace
 
+// Scratch of the allocation-free decode step: the chunk partials of one call, on each device
+// the library runs on (held until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the address hipGetSymbolAddress reports for the
+// current device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
 size_t decode_workspace_bytes(int batch, int hkv, int G, int W, int d, int cap) {
     const int64_t nchunk = (cap + kCH - 1) / kCH;
     const int64_t R = (int64_t)G * W;
@@ -498,6 +510,26 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (a.d == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t s) {
+    // The caller has checked that the workspace fits kDecodeScratchBytes.  The device's
+    // address of `scratch` is looked up once per device (with that device current) and kept;
+    // threads racing on the first call store the same address.
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    DecodeArgs b = a;
+    b.ws = ptr;
+    return launch_decode(b, s);
 }
 
 }  // namespace mars

@@ -1,7 +1,8 @@
 // C ABI of libmars (include/mars.h): argument validation, then kernel launches on the
 // caller's stream.  Validation is complete before anything is launched, so an error
-// leaves every buffer untouched.  Nothing here allocates device memory; the only state the
-// library keeps is the forward launcher's per-device count of resident workgroups.
+// leaves every buffer untouched.  Nothing here allocates device memory; the state the library
+// keeps is the forward launcher's per-device count of resident workgroups and the per-device
+// address of the allocation-free decode step's scratch array.
 #include <math.h>
 #include <stdint.h>
 
@@ -279,12 +280,8 @@ int mars_decode_workspace_bytes(const mars_decode_desc* desc, size_t* bytes) {
     return MARS_OK;
 }
 
-int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void* k_win, const void* v_win,
-                     const void* k_cache, const void* v_cache, const int32_t* cache_len, void* o, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
-    int st = check_decode_desc(desc);
-    if (st) return st;
-    if (desc->batch == 0) return MARS_OK;
+static int check_decode_call(const mars_decode_desc* desc, const void* q_win, const void* k_win, const void* v_win,
+                             const void* k_cache, const void* v_cache, const int32_t* cache_len, const void* o) {
     if (!q_win || !k_win || !v_win || !cache_len || !o) return MARS_EINVAL;
     if (desc->cache_capacity > 0 && (!k_cache || !v_cache)) return MARS_EINVAL;
     if (!aligned16(q_win) || !aligned16(k_win) || !aligned16(v_win) || !aligned16(o) || !aligned16(k_cache) ||
@@ -296,10 +293,12 @@ int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void
     // The cache copies address 32 positions from one base with 32-bit byte offsets.
     if (desc->kc_strides[2] > kMaxCachePosStride || desc->vc_strides[2] > kMaxCachePosStride)
         return MARS_EUNSUPPORTED;
-    const size_t need = mars::decode_workspace_bytes(desc->batch, desc->n_kv_heads,
-                                                     desc->n_q_heads / desc->n_kv_heads, desc->window,
-                                                     desc->head_dim, desc->cache_capacity);
-    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MARS_EWORKSPACE;
+    return MARS_OK;
+}
+
+static mars::DecodeArgs make_decode_args(const mars_decode_desc* desc, const void* q_win, const void* k_win,
+                                         const void* v_win, const void* k_cache, const void* v_cache,
+                                         const int32_t* cache_len, void* o, void* ws) {
     mars::DecodeArgs a;
     a.qw = q_win;
     a.kw = k_win;
@@ -324,7 +323,45 @@ int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void
     a.W = desc->window;
     a.cap = desc->cache_capacity;
     a.scale = eff_scale(desc->scale, desc->head_dim);
+    return a;
+}
+
+static size_t decode_need(const mars_decode_desc* desc) {
+    return mars::decode_workspace_bytes(desc->batch, desc->n_kv_heads, desc->n_q_heads / desc->n_kv_heads,
+                                        desc->window, desc->head_dim, desc->cache_capacity);
+}
+
+int mars_decode_step(const mars_decode_desc* desc, const void* q_win, const void* k_win, const void* v_win,
+                     const void* k_cache, const void* v_cache, const int32_t* cache_len, void* o, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    int st = check_decode_desc(desc);
+    if (st) return st;
+    if (desc->batch == 0) return MARS_OK;
+    st = check_decode_call(desc, q_win, k_win, v_win, k_cache, v_cache, cache_len, o);
+    if (st) return st;
+    const size_t need = decode_need(desc);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MARS_EWORKSPACE;
+    const mars::DecodeArgs a = make_decode_args(desc, q_win, k_win, v_win, k_cache, v_cache, cache_len, o, ws);
     return map_hip(mars::launch_decode(a, stream));
+}
+
+int mars_decode_step_noalloc(const mars_decode_desc* desc, const void* q_win, const void* k_win, const void* v_win,
+                             const void* k_cache, const void* v_cache, const int32_t* cache_len, void* o,
+                             hipStream_t stream) {
+    int st = check_decode_desc(desc);
+    if (st) return st;
+    if (desc->batch == 0) return MARS_OK;
+    st = check_decode_call(desc, q_win, k_win, v_win, k_cache, v_cache, cache_len, o);
+    if (st) return st;
+    if (decode_need(desc) > mars::kDecodeScratchBytes) return MARS_EWORKSPACE;
+    const mars::DecodeArgs a = make_decode_args(desc, q_win, k_win, v_win, k_cache, v_cache, cache_len, o, nullptr);
+    return map_hip(mars::launch_decode_noalloc(a, stream));
+}
+
+int mars_decode_scratch_bytes(size_t* bytes) {
+    if (!bytes) return MARS_EINVAL;
+    *bytes = mars::kDecodeScratchBytes;
+    return MARS_OK;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -70,6 +70,10 @@ constexpr int kDecodeChunk = 512;
 constexpr int64_t kDecodeMaxCapacity = int64_t(65535) * kDecodeChunk;
 size_t decode_workspace_bytes(int batch, int hkv, int G, int W, int d, int cap);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Decode step whose partials live in the library's own per-device scratch array (a.ws is
+// ignored): at most kDecodeScratchBytes of workspace, no allocation.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t s);
 
 // KV commit and cursor advance (kv_commit.hip).
 struct CommitArgs {

@@ -184,6 +184,17 @@ static void decode() {
            MARS_OK);
     EXPECT(mars_decode_step(&d, FAKE, FAKE, FAKE, FAKE, FAKE, lens, FAKE, FAKE, need, nullptr), MARS_EHIP);
 
+    size_t scratch = 0;
+    EXPECT(mars_decode_scratch_bytes(nullptr), MARS_EINVAL);
+    EXPECT(mars_decode_scratch_bytes(&scratch), MARS_OK);
+    x = dec(32, 28, 4, 128, 4, 16384);              // partials beyond the scratch array
+    EXPECT(mars_decode_step_noalloc(&x, FAKE, FAKE, FAKE, FAKE, FAKE, lens, FAKE, nullptr), MARS_EWORKSPACE);
+    EXPECT(mars_decode_step_noalloc(&d, FAKE, FAKE, FAKE, FAKE, FAKE, nullptr, FAKE, nullptr), MARS_EINVAL);
+    x = d; x.batch = 0;
+    EXPECT(mars_decode_step_noalloc(&x, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr),
+           MARS_OK);
+    EXPECT(mars_decode_step_noalloc(&d, FAKE, FAKE, FAKE, FAKE, FAKE, lens, FAKE, nullptr), MARS_EHIP);
+
     int32_t* cl = (int32_t*)FAKE;
     EXPECT(mars_kv_commit(&d, FAKE, FAKE, lens, FAKE, FAKE, cl, nullptr, nullptr, 2, nullptr), MARS_EINVAL);
     EXPECT(mars_kv_commit(&d, FAKE, FAKE, lens, FAKE, FAKE, cl, (uint64_t*)((char*)FAKE + 4), nullptr, 0, nullptr),

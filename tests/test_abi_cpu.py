@@ -172,6 +172,25 @@ def test_decode_validation_errors():
     assert call(d, ptr=None, lens=None, ws=None) == L.MARS_OK
 
 
+def test_decode_noalloc_validation_errors():
+    lib = L.load()
+    n = ctypes.c_size_t()
+    assert lib.mars_decode_scratch_bytes(None) == L.MARS_EINVAL
+    assert lib.mars_decode_scratch_bytes(ctypes.byref(n)) == L.MARS_OK and n.value == 32 << 20
+
+    def call(d, ptr=FAKE, lens=FAKE):
+        return lib.mars_decode_step_noalloc(ctypes.byref(d), ptr, ptr, ptr, ptr, ptr, lens, ptr, None)
+
+    assert call(M.decode_desc(32, 28, 4, 128, 4, 16384)) == L.MARS_EWORKSPACE     # partials beyond the array
+    assert M.mars_decode_workspace_bytes(32, 28, 4, 128, 4, 4096) <= n.value     # the 7B decode workload fits
+    assert call(M.decode_desc(32, 28, 4, 128, 4, 4096), lens=None) == L.MARS_EINVAL
+    assert call(M.decode_desc(32, 28, 4, 128, 4, 4096), ptr=MISALIGNED) == L.MARS_EINVAL
+    d = M.decode_desc(32, 28, 4, 96, 4, 4096)
+    assert call(d) == L.MARS_EUNSUPPORTED
+    d = M.decode_desc(32, 28, 4, 128, 4, 4096); d.batch = 0
+    assert call(d, ptr=None, lens=None) == L.MARS_OK
+
+
 def test_accept_validation_errors():
     lib = L.load()
     good = lambda: M.accept_desc(32, 4, 152064, 0.95)
