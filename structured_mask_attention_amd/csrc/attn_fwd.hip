@@ -7,7 +7,8 @@
 //     (batch, kv head) pair = position u / G, head kvh*G + u % G), so every K/V tile a
 //     workgroup stages in LDS serves G heads.  A workgroup owns 128 such rows (4 waves x
 //     32 rows): small enough that the heaviest row tiles (the longest key ranges) finish
-//     early when dispatched first, and light enough on registers for 2 waves per SIMD.
+//     early when dispatched first, and light enough on registers for 4 (head_dim 64) or 3
+//     (head_dim 128) waves per SIMD.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the K
 //     tile is the A operand (read from LDS), the wave's Q rows the B operand (registers for
 //     the whole kernel).  In the output layout a lane owns one query row and 16 of the 32
@@ -114,7 +115,7 @@ __device__ inline uint16_t* att_v() {
 }
 
 template <int D, bool LOG>
-__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kernel(AttnKParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 3) void attn_fwd_bf16_kernel(AttnKParams p) {
     constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
     constexpr int NDB = D / 32;         // 32-row d blocks of O^T
     constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
@@ -425,8 +426,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
             }
         };
         scores();
-        // V^T fragments of this tile, read now (into the registers the K fragments just
-        // released) so that their LDS latency overlaps the softmax below.
+        // V^T fragments of this tile.  Head_dim 64 reads them now (into the registers the K
+        // fragments just released) so that their LDS latency overlaps the softmax below;
+        // head_dim 128 reads them just before P V, which keeps the kernel within 168 VGPRs
+        // (three waves per SIMD, whose interleaving hides that latency instead).
         bf16x8_t va[NDB][2];
         auto read_v = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
             }
         }
         };
-        read_v();
+        if constexpr (D == 64) read_v();
         // Lazy rescale.  The row max is computed while some row of the wave has no finite
         // running max yet (its first visible keys), or when this tile's P could overflow:
         // P = 2^s is formed first and its row sum checked against 2^64, which bounds every
@@ -476,10 +479,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
                         const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(off[cb] - noff);
                         l_run[cb] *= alpha;
                         if (started) {
+                            // One 16-register block at a time (scheduling barriers), so the
+                            // rescale never needs all accumulators in flight at once.
 #pragma unroll
                             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                                 for (int e = 0; e < 16; ++e) acc[cb][db][e] *= alpha;
+                                __builtin_amdgcn_sched_barrier(0);
                             }
                         }
                         const float delta = noff - off[cb];
@@ -543,6 +549,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd_bf16_kerne
         }
 #pragma unroll
         for (int cb = 0; cb < kNcb; ++cb) l_run[cb] += lt[cb];
+        if constexpr (D == 128) read_v();
         // O^T += V^T P^T.
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {

@@ -123,6 +123,16 @@ __device__ inline int rank_to_tile(int rank, int T, int tN0) {
     return (nN > m) ? (T - 1 - m - rr) : (tN0 - 1 - m - rr);
 }
 
+// A pointer the whole wave holds the same value of, made visibly wave-uniform (SGPRs) for an
+// inline-asm operand that must be scalar.
+template <class T>
+__device__ inline T* uniform_ptr(T* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // LDS byte address of a __shared__ object (the low half of its generic address).
 __device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
