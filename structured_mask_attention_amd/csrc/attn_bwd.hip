@@ -128,23 +128,26 @@ __device__ inline uint32_t span_bits(int a, int b, int base) {
 
 // A operand (rows of a [32][D] tile, lane = row hl, 8 columns per lane) and transposed A
 // operand (ds_read_b64_tr_b16: 16 tile rows x 32 columns per instruction pair) offsets.
+// Tiles read both ways are swizzled with swz_kv; rows 8..15 of a 16-row chunk have their
+// own base offset (hi = 1) because that swizzle is not periodic in 8 rows.
 template <int D>
 __device__ inline int row_read_off(int hl, int g2, int swz) {
     return hl * (2 * D) + 16 * (g2 ^ swz);
 }
 template <int D>
-__device__ inline int tr_read_off(int lane) {
+__device__ inline int tr_read_off(int lane, int hi) {
     const int s16 = lane & 15, grp = lane >> 4;
-    const int row = 4 * (grp >> 1) + (s16 >> 2);
+    const int row = 8 * hi + 4 * (grp >> 1) + (s16 >> 2);
     const int col = 16 * (grp & 1) + 4 * (s16 & 3);
-    return row * (2 * D) + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
+    return row * (2 * D) + 16 * ((col >> 3) ^ swz_kv<D>(row)) + 2 * (col & 7);
 }
 // Transposed fragment of column block db, 16-row chunk kh (rows in acc_off order).
 template <int D>
-__device__ inline bf16x8_t tr_frag(const char* tile, int off0, int db, int kh) {
-    const char* p = tile + (off0 ^ (64 * db)) + kh * 16 * (2 * D);
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)p);
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(p + 8 * (2 * D)));
+__device__ inline bf16x8_t tr_frag(const char* tile, int off_lo, int off_hi, int db, int kh) {
+    const char* pl = tile + (off_lo ^ (64 * db)) + kh * 16 * (2 * D);
+    const char* ph = tile + (off_hi ^ (64 * db)) + kh * 16 * (2 * D);
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)pl);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)ph);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
     }
 
     // Copy of step `it` (position tile, head) into stage ST.  Window slot (row r,
-    // position ps) holds logical chunk ps ^ swz_v(r) of row r; dO rows past N repeat row
+    // position ps) holds logical chunk ps ^ swz_kv(r) of row r; dO rows past N repeat row
     // N-1 (finite; such rows are always masked).  The scalar copy: wave w moves bytes
     // [64w, 64w + 64) of [-LSE2 x 32][-D x 32] with four lanes.
     const int64_t qc_row = (int64_t)p.hq * D;   // Qc position stride (elements)
@@ -337,8 +340,8 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
     for (int w = 0; w < PERW; ++w) {
         const int slot = 64 * (wave * PERW + w) + lane;
         const int r = slot / CPR, ps = slot % CPR;
-        qgo[w] = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_v<D>(r)));
-        ogo[w] = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_v<D>(r)));
+        qgo[w] = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_kv<D>(r)));
+        ogo[w] = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
     }
     // Running position of the next copy (walk order: position tile, then head): tile index
     // iti, head ih, and that step's base pointers; a head step adds one head stride, a tile
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
                 const int slot = 64 * jw + lane;
                 const int r = slot / CPR, ps = slot % CPR;
                 const int rr = min(r, p.N - 1 - ip0);
-                dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_v<D>(r))), lds_addr(ring_o<D, ST>()) + 1024 * jw);
+                dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(ring_o<D, ST>()) + 1024 * jw);
             }
         }
         if (lane < 4) dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(ring_s<D, ST>()) + 64 * wave);
@@ -392,8 +395,8 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
             dka[db][e] = 0.f;
         }
     }
-    const int roff = row_read_off<D>(hl, g2, swz_v<D>(hl));
-    const int troff = tr_read_off<D>(lane);
+    const int roff = row_read_off<D>(hl, g2, swz_kv<D>(hl));
+    const int troff = tr_read_off<D>(lane, 0), troff_hi = tr_read_off<D>(lane, 1);
 
     issue(S0{});
     if (nsteps > 1) issue(S1{});
@@ -462,8 +465,8 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
         for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ot, troff, db, kh), pb[kh], dva[db], 0, 0, 0);
-                dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt, troff, db, kh), sb[kh], dka[db], 0, 0, 0);
+                dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ot, troff, troff_hi, db, kh), pb[kh], dva[db], 0, 0, 0);
+                dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt, troff, troff_hi, db, kh), sb[kh], dka[db], 0, 0, 0);
             }
         }
     };
@@ -642,13 +645,13 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
 
     const uint16_t* kbase = p.k + b * p.ks0 + (int64_t)g * p.ks2;
     const uint16_t* vbase = p.v + b * p.vs0 + (int64_t)g * p.vs2;
-    // K tile: row reads and transposed reads (swz_v); V tile: row reads only (swz_k).
+    // K tile: row reads and transposed reads (swz_kv); V tile: row reads only (swz_k).
     uint32_t kgo[PERW], vgo[PERW];
 #pragma unroll
     for (int w = 0; w < PERW; ++w) {
         const int slot = 64 * (wave * PERW + w) + lane;
         const int r = slot / CPR, ps = slot % CPR;
-        kgo[w] = (uint32_t)(r * p.ks1 * 2 + 16 * (ps ^ swz_v<D>(r)));
+        kgo[w] = (uint32_t)(r * p.ks1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
         vgo[w] = (uint32_t)(r * p.vs1 * 2 + 16 * (ps ^ swz_k<D>(r)));
     }
     const int nfull = p.N / kT;
@@ -668,7 +671,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
                 const int slot = 64 * jw + lane;
                 const int r = slot / CPR, ps = slot % CPR;
                 const int rr = min(r, p.N - 1 - k0);
-                dma16_sv(kb, (uint32_t)(rr * p.ks1 * 2 + 16 * (ps ^ swz_v<D>(r))), lds_addr(ring_k<D, ST>()) + 1024 * jw);
+                dma16_sv(kb, (uint32_t)(rr * p.ks1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(ring_k<D, ST>()) + 1024 * jw);
                 dma16_sv(vb, (uint32_t)(rr * p.vs1 * 2 + 16 * (ps ^ swz_k<D>(r))), lds_addr(ring_v<D, ST>()) + 1024 * jw);
             }
         }
@@ -712,9 +715,9 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
     }
-    const int kroff = row_read_off<D>(hl, g2, swz_v<D>(hl));
+    const int kroff = row_read_off<D>(hl, g2, swz_kv<D>(hl));
     const int vroff = row_read_off<D>(hl, g2, swz_k<D>(hl));
-    const int troff = tr_read_off<D>(lane);
+    const int troff = tr_read_off<D>(lane, 0), troff_hi = tr_read_off<D>(lane, 1);
 
     issue(0, S0{});
     if (ntiles > 1) issue(1, S1{});
@@ -763,7 +766,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
         for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_lds, troff, db, kh), sb[kh], acc[db], 0, 0, 0);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_lds, troff, troff_hi, db, kh), sb[kh], acc[db], 0, 0, 0);
         }
     };
     for (int t0 = 0; t0 < ntiles; t0 += kStagesB) {

@@ -98,7 +98,12 @@ __device__ inline float sum32(float x) {
 // K/V tiles in LDS: rows of D bf16 (2D bytes, no padding), 16-byte chunks XOR-swizzled by
 // row so that the MFMA operand reads are free of bank conflicts:
 //   * K (ds_read_b128, lane = row, same logical chunk): chunk c of row r at c ^ swz_k(r);
-//   * V (ds_read_b64_tr_b16, 4 rows x 2 chunks per 16 lanes): chunk c of row r at c ^ swz_v(r).
+//   * V (ds_read_b64_tr_b16, 4 rows x 2 chunks per 16 lanes): chunk c of row r at c ^ swz_v(r);
+//   * tiles read both ways (the backward's Qc, dO and K tiles): chunk c of row r at
+//     c ^ swz_kv(r), which is injective on every 16 consecutive rows of one parity class
+//     (row reads) and gives the 4 rows of an aligned group disjoint chunk quads (transposed
+//     reads).  Unlike swz_v it is not periodic in 8 rows: swz_kv(r + 8) = swz_kv(r) ^ 2 for
+//     r % 16 < 8.
 // Tiles are filled with global_load_lds_dwordx4: lane L of a 64-lane instruction writes LDS
 // bytes [16L, 16L+16) of that instruction's 1 KB window, i.e. slot s = (row, position).
 // ---------------------------------------------------------------------------------------
@@ -109,6 +114,10 @@ __device__ inline int swz_k(int r) {
 template <int D>
 __device__ inline int swz_v(int r) {
     return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+template <int D>
+__device__ inline int swz_kv(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Row-tile order of the training-layout kernels that walk keys per row tile (heaviest

@@ -3,7 +3,7 @@
 Usage: python -m structured_mask_attention_amd.profile_kernels [what ...] [--reps N]
   what: attn05 (Qwen2.5-0.5B-shaped training layout), attn7 (7B-shaped), attnlong (long
         7B-shaped), decode (7B-shaped decode step), accept (152k-vocabulary accept),
-        bwd05 (training backward on the 0.5B layout), loss05 (training loss with its gradient
+        bwd05, bwd7, bwdlong (training backward on those layouts), loss05 (training loss with its gradient
         on the 0.5B layout's logits [8, 1280, 151936]), copy (a plain 256 MiB
         device-to-device copy: the calibration of byte counters).
 Inputs are the seeded synthetic workloads of ``inputs``; every launch reads fresh copies
@@ -20,6 +20,7 @@ from . import (mars_accept, mars_accept_workspace_bytes, mars_attn_bwd, mars_att
                mars_decode_workspace_bytes, mars_shifted_ce)
 
 TRAIN = {"attn05": I.QWEN05B, "attn7": I.QWEN7B, "attnlong": I.LONG7B}
+BWD = {"bwd05": I.QWEN05B, "bwd7": I.QWEN7B, "bwdlong": I.LONG7B}
 
 
 def main():
@@ -51,8 +52,8 @@ def main():
                 ws = torch.empty(mars_accept_workspace_bytes(s.batch, s.W, s.vocab), dtype=torch.uint8, device=dev)
                 for r in range(a.reps):
                     mars_accept(sets[r % a.copies][6], s.tau, ws=ws)
-        elif w == "bwd05":
-            s = I.QWEN05B
+        elif w in BWD:
+            s = BWD[w]
             host = I.train_inputs(s)
             sets = [tuple(t.to(dev) for t in host) for _ in range(a.copies)]
             do = I.grad_output(s).to(dev)
