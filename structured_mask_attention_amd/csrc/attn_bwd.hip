@@ -57,12 +57,9 @@ constexpr int kNominalSlots128 = 256;      // (256 CUs x 2 or 1 per CU, by head_
     __shared__ __attribute__((aligned(16))) uint16_t NAME##0[ELEMS];                    \
     __shared__ __attribute__((aligned(16))) uint16_t NAME##1[ELEMS];                    \
     __shared__ __attribute__((aligned(16))) uint16_t NAME##2[ELEMS];
-MARS_BRING(g_bq128_, kT * 128)
-MARS_BRING(g_bo128_, kT * 128)
 MARS_BRING(g_bq64_, kT * 64)
 MARS_BRING(g_bo64_, kT * 64)
-MARS_BRING(g_bs128_, 128)        // 256 bytes of fp32 scalars per stage
-MARS_BRING(g_bs64_, 128)
+MARS_BRING(g_bs64_, 128)         // 256 bytes of fp32 scalars per stage
 MARS_BRING(g_dk128_, kT * 128)
 MARS_BRING(g_dv128_, kT * 128)
 MARS_BRING(g_dk64_, kT * 64)
@@ -83,9 +80,28 @@ MARS_BRING(g_dv64_, kT * 64)
             else return N64##2;                                                          \
         }                                                                                \
     }
-MARS_SEL(ring_q, g_bq128_, g_bq64_)
-MARS_SEL(ring_o, g_bo128_, g_bo64_)
-MARS_SEL(ring_s, g_bs128_, g_bs64_)
+// The 4-wave dK/dV kernel runs at head_dim 64 only (its rings have no head_dim-128 copy).
+template <int D, int ST>
+__device__ inline uint16_t* ring_q() {
+    static_assert(D == 64 && ST >= 0 && ST < kStagesB, "stage");
+    if constexpr (ST == 0) return g_bq64_0;
+    else if constexpr (ST == 1) return g_bq64_1;
+    else return g_bq64_2;
+}
+template <int D, int ST>
+__device__ inline uint16_t* ring_o() {
+    static_assert(D == 64 && ST >= 0 && ST < kStagesB, "stage");
+    if constexpr (ST == 0) return g_bo64_0;
+    else if constexpr (ST == 1) return g_bo64_1;
+    else return g_bo64_2;
+}
+template <int D, int ST>
+__device__ inline uint16_t* ring_s() {
+    static_assert(D == 64 && ST >= 0 && ST < kStagesB, "stage");
+    if constexpr (ST == 0) return g_bs64_0;
+    else if constexpr (ST == 1) return g_bs64_1;
+    else return g_bs64_2;
+}
 MARS_SEL(ring_k, g_dk128_, g_dk64_)
 MARS_SEL(ring_v, g_dv128_, g_dv64_)
 #undef MARS_SEL
@@ -260,6 +276,101 @@ struct DkvParams {
     int hq, hkv, G, P, L, B, N, Npad;
     int bg_count, kblocks, nch_max, tc;
 };
+
+// dK / dV of one wave's 32 keys (key group kg of the block; j = this lane's key): stored
+// directly when the walk is one chunk, else through the chunk partials and the per-slice
+// arrival counter.
+template <int D>
+__device__ inline void dkdv_finish(const DkvParams& p, int c, int nch, int kblk, int bg, int kg, int lane, int b,
+                                   int g, int j, bool kvalid, f32x16_t (&dva)[D / 32], f32x16_t (&dka)[D / 32]) {
+    constexpr int NDB = D / 32;
+    const int g2 = lane >> 5;
+    // dV = dV^T^T; dK = ln2 * dK^T^T (Qc carries scale*log2(e) where dK needs scale).
+    // A walk in several chunks: every chunk stores its fp32 partial for its 32 keys; the
+    // wave that arrives last for this 32-key slice (per-slice counter) sums the partials in
+    // chunk order (the same order whoever is last) and stores the result.
+    auto store_final = [&](const f32x16_t* gv, const f32x16_t* gk) __attribute__((always_inline)) {
+        if (!kvalid) return;
+        uint16_t* vo = p.dv + b * p.dvs0 + (int64_t)j * p.dvs1 + (int64_t)g * p.dvs2;
+        uint16_t* ko = p.dk + b * p.dks0 + (int64_t)j * p.dks1 + (int64_t)g * p.dks2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int d = 32 * db + 8 * bb + 4 * g2;
+                uint2 wv, wk;
+                wv.x = pack_bf16x2(gv[db][4 * bb + 0], gv[db][4 * bb + 1]);
+                wv.y = pack_bf16x2(gv[db][4 * bb + 2], gv[db][4 * bb + 3]);
+                wk.x = pack_bf16x2(gk[db][4 * bb + 0] * kLn2, gk[db][4 * bb + 1] * kLn2);
+                wk.y = pack_bf16x2(gk[db][4 * bb + 2] * kLn2, gk[db][4 * bb + 3] * kLn2);
+                *reinterpret_cast<uint2*>(vo + d) = wv;
+                *reinterpret_cast<uint2*>(ko + d) = wk;
+            }
+        }
+    };
+    if (nch == 1) {
+        store_final(dva, dka);
+        return;
+    }
+    // Partial of this wave: [dV | dK][d block][4 element groups][64 lanes] x 16 bytes, so
+    // every store / load instruction moves 1 KB of contiguous memory.  Both are system
+    // coherent (sc0 sc1): written through to memory and read from it, so chunks on other
+    // XCDs see them without cache maintenance.
+    constexpr int kSlotBytes = 2 * NDB * 4 * 64 * 16;
+    auto slot_rsrc = [&](int cc) __attribute__((always_inline)) {
+        char* base = reinterpret_cast<char*>(p.part) +
+                     ((((int64_t)cc * p.kblocks + kblk) * p.bg_count + bg) * kWavesB + kg) * (int64_t)kSlotBytes;
+        return __builtin_amdgcn_make_buffer_rsrc(base, 0, kSlotBytes, 0x00020000);
+    };
+    constexpr int kSysCoherent = 1 | 16;   // sc0 | sc1
+    {
+        const __amdgpu_buffer_rsrc_t r = slot_rsrc(c);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const f32x4_t xv = {dva[db][4 * qd], dva[db][4 * qd + 1], dva[db][4 * qd + 2], dva[db][4 * qd + 3]};
+                const f32x4_t xk = {dka[db][4 * qd], dka[db][4 * qd + 1], dka[db][4 * qd + 2], dka[db][4 * qd + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(xv, r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+                __builtin_amdgcn_raw_buffer_store_b128(xk, r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+            }
+        }
+    }
+    // Every partial store of this wave completes before its arrival is counted.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(p.cnt + ((int64_t)kblk * p.bg_count + bg) * kWavesB + kg, 1,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    asm volatile("" ::: "memory");
+    if (old != nch - 1) return;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            dva[db][e] = 0.f;
+            dka[db][e] = 0.f;
+        }
+    }
+    for (int cc = 0; cc < nch; ++cc) {
+        const __amdgpu_buffer_rsrc_t r = slot_rsrc(cc);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const f32x4_t xv = __builtin_amdgcn_raw_buffer_load_b128(r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+                const f32x4_t xk = __builtin_amdgcn_raw_buffer_load_b128(r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dva[db][4 * qd + i] += xv[i];
+                    dka[db][4 * qd + i] += xk[i];
+                }
+            }
+        }
+    }
+    store_final(dva, dka);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kernel(DkvParams p) {
@@ -476,66 +587,139 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
         if (t0 + 2 < nsteps) body(t0 + 2, S2{});
     }
 
-    // dV = dV^T^T; dK = ln2 * dK^T^T (Qc carries scale*log2(e) where dK needs scale).
-    // A walk in several chunks: every chunk stores its fp32 partial for its 32 keys; the
-    // wave that arrives last for this 32-key slice (per-slice counter) sums the partials in
-    // chunk order (the same order whoever is last) and stores the result.
-    auto store_final = [&](const f32x16_t* gv, const f32x16_t* gk) __attribute__((always_inline)) {
-        if (!kvalid) return;
-        uint16_t* vo = p.dv + b * p.dvs0 + (int64_t)j * p.dvs1 + (int64_t)g * p.dvs2;
-        uint16_t* ko = p.dk + b * p.dks0 + (int64_t)j * p.dks1 + (int64_t)g * p.dks2;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const int d = 32 * db + 8 * bb + 4 * g2;
-                uint2 wv, wk;
-                wv.x = pack_bf16x2(gv[db][4 * bb + 0], gv[db][4 * bb + 1]);
-                wv.y = pack_bf16x2(gv[db][4 * bb + 2], gv[db][4 * bb + 3]);
-                wk.x = pack_bf16x2(gk[db][4 * bb + 0] * kLn2, gk[db][4 * bb + 1] * kLn2);
-                wk.y = pack_bf16x2(gk[db][4 * bb + 2] * kLn2, gk[db][4 * bb + 3] * kLn2);
-                *reinterpret_cast<uint2*>(vo + d) = wv;
-                *reinterpret_cast<uint2*>(ko + d) = wk;
-            }
+    dkdv_finish<D>(p, c, nch, kblk, bg, wave, lane, b, g, j, kvalid, dva, dka);
+}
+
+// ---------------------------------------------------------------------------------------
+// 2b. dK / dV at head_dim 128: two waves per SIMD.
+//   One kernel variant for head_dim 128, where a wave's K / V fragments plus its dK / dV
+//   accumulators leave room for one wave per SIMD only.  Here a workgroup of 8 waves owns the
+//   same 128 keys: K and V of those keys sit in LDS (read as B operands each step), and the
+//   waves w and w + 4 share key group w % 4, wave w taking the walk's even steps and wave
+//   w + 4 the odd ones; their dK / dV sums are added through LDS at the end.  Each step's
+//   Qc / dO tile and row scalars go into a 5-stage ring (two steps in use, three in
+//   flight), copied by all 8 waves.  Per step and wave the arithmetic is the 4-wave
+//   kernel's.
+// ---------------------------------------------------------------------------------------
+constexpr int kWavesP = 8;
+constexpr int kThreadsP = 64 * kWavesP;
+constexpr int kStagesP = 5;
+__shared__ __attribute__((aligned(16))) uint16_t g_pk[kKeysPerWG * 128];     // K rows of the block
+__shared__ __attribute__((aligned(16))) uint16_t g_pv[kKeysPerWG * 128];     // V rows of the block
+__shared__ __attribute__((aligned(16))) uint16_t g_pq[kStagesP][kT * 128];   // Qc tiles
+__shared__ __attribute__((aligned(16))) uint16_t g_po[kStagesP][kT * 128];   // dO tiles
+__shared__ __attribute__((aligned(16))) float g_ps[kStagesP][64];            // [-LSE2 x 32][-D x 32]
+
+__global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvParams p) {
+    constexpr int D = 128;
+    constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
+    constexpr int TSZ = kT * D * 2;                 // bytes of one Qc or dO tile
+    static_assert(kT * CPR / 64 == kWavesP, "one 1 KB copy window of each tile per wave");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kg = wave & 3, half = wave >> 2;
+    const int hl = lane & 31, g2 = lane >> 5;
+    const int c = blockIdx.x % p.nch_max;
+    const int rest = blockIdx.x / p.nch_max;
+    const int bg = rest % p.bg_count;
+    const int kblk = rest / p.bg_count;
+    const int b = bg / p.hkv, g = bg % p.hkv;
+    const int PL = p.P + p.L;
+    const int kb0 = kblk * kKeysPerWG;
+    const int kb1 = min(kb0 + kKeysPerWG, p.N);
+
+    int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
+    kblock_tile_ranges(kb0, kb1, p.P, p.L, p.B, p.N, rs, re);
+    const int n0t = re[0] - rs[0], n1t = re[1] - rs[1], n2t = re[2] - rs[2];
+    const int npt = n0t + n1t + n2t;
+    const int nch = walk_chunks(npt, p.tc);
+    if (c >= nch) return;
+    const int ct0 = (int)((int64_t)c * npt / nch), ct1 = (int)((int64_t)(c + 1) * npt / nch);
+    const int nsteps = (ct1 - ct0) * p.G;
+    auto pos_tile = [&](int ti) __attribute__((always_inline)) {
+        ti += ct0;
+        return ti < n0t ? rs[0] + ti : (ti < n0t + n1t ? rs[1] + (ti - n0t) : rs[2] + (ti - n0t - n1t));
+    };
+
+    // This lane's key and the positions that see it: [a1, b1) u [a2, b2) (as the 4-wave kernel).
+    const int j = kb0 + kg * kT + hl;
+    const bool kvalid = j < p.N;
+    int a1 = 0, b1 = 0, a2 = 0, b2 = 0;
+    if (kvalid) {
+        if (j < PL) {
+            a1 = j;
+            b1 = PL;
+            a2 = min(PL + (j < p.P ? 0 : p.B * ((j - p.P) / p.B + 1)), p.N);
+            b2 = p.N;
+        } else {
+            a1 = j;
+            b1 = min(p.N, PL + ((j - PL) / p.B + 1) * p.B);
         }
-    };
-    if (nch == 1) {
-        store_final(dva, dka);
-        return;
     }
-    // Partial of this wave: [dV | dK][d block][4 element groups][64 lanes] x 16 bytes, so
-    // every store / load instruction moves 1 KB of contiguous memory.  Both are system
-    // coherent (sc0 sc1): written through to memory and read from it, so chunks on other
-    // XCDs see them without cache maintenance.
-    constexpr int kSlotBytes = 2 * NDB * 4 * 64 * 16;
-    auto slot_rsrc = [&](int cc) __attribute__((always_inline)) {
-        char* base = reinterpret_cast<char*>(p.part) +
-                     ((((int64_t)cc * p.kblocks + kblk) * p.bg_count + bg) * kWavesB + wave) * (int64_t)kSlotBytes;
-        return __builtin_amdgcn_make_buffer_rsrc(base, 0, kSlotBytes, 0x00020000);
-    };
-    constexpr int kSysCoherent = 1 | 16;   // sc0 | sc1
+
+    // K / V rows of the block into LDS: window w (1 KB = 4 rows) of each, rows past N repeat
+    // row N-1; chunk ps of row r at ps ^ swz_k(r) (the B operand reads are row reads).
     {
-        const __amdgpu_buffer_rsrc_t r = slot_rsrc(c);
+        const uint16_t* kbase = p.k + b * p.ks0 + (int64_t)g * p.ks2;
+        const uint16_t* vbase = p.v + b * p.vs0 + (int64_t)g * p.vs2;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const f32x4_t xv = {dva[db][4 * qd], dva[db][4 * qd + 1], dva[db][4 * qd + 2], dva[db][4 * qd + 3]};
-                const f32x4_t xk = {dka[db][4 * qd], dka[db][4 * qd + 1], dka[db][4 * qd + 2], dka[db][4 * qd + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(xv, r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-                __builtin_amdgcn_raw_buffer_store_b128(xk, r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-            }
+        for (int w = 0; w < kKeysPerWG * CPR / 64 / kWavesP; ++w) {
+            const int win = wave * (kKeysPerWG * CPR / 64 / kWavesP) + w;
+            const int slot = 64 * win + lane;
+            const int r = slot / CPR, ps = slot % CPR;
+            const int rr = min(kb0 + r, p.N - 1);
+            dma16_sv(kbase, (uint32_t)(rr * p.ks1 * 2 + 16 * (ps ^ swz_k<D>(r))), lds_addr(g_pk) + 1024 * win);
+            dma16_sv(vbase, (uint32_t)(rr * p.vs1 * 2 + 16 * (ps ^ swz_k<D>(r))), lds_addr(g_pv) + 1024 * win);
         }
     }
-    // Every partial store of this wave completes before its arrival is counted.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    int old = 0;
-    if (lane == 0)
-        old = __hip_atomic_fetch_add(p.cnt + ((int64_t)kblk * p.bg_count + bg) * kWavesB + wave, 1,
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    asm volatile("" ::: "memory");
-    if (old != nch - 1) return;
+
+    // Step copies: wave w moves window w of the Qc tile and of the dO tile, waves 0..3 also
+    // 64 bytes of the row scalars (as the 4-wave kernel).  Walk order: position tile, then
+    // head; the next copy's step is (iti, ih).
+    const int64_t qc_row = (int64_t)p.hq * D;
+    uint32_t qgo, ogo;
+    {
+        const int slot = 64 * wave + lane;
+        const int r = slot / CPR, ps = slot % CPR;
+        qgo = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_kv<D>(r)));
+        ogo = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
+    }
+    int iti = 0, ih = 0, ip0 = 0;
+    const uint16_t* iq = nullptr;
+    const uint16_t* io = nullptr;
+    const float* isl = nullptr;
+    auto seek = [&]() __attribute__((always_inline)) {
+        ip0 = pos_tile(iti) * kT;
+        const int head = g * p.G;
+        iq = p.qc + ((int64_t)b * p.Npad + ip0) * qc_row + (int64_t)head * D;
+        io = p.dout + b * p.ds0 + (int64_t)ip0 * p.ds1 + (int64_t)head * p.ds2;
+        isl = ((wave & 3) < 2 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + ip0 + 16 * (wave & 1);
+    };
+    seek();
+    auto issue = [&](const int st) __attribute__((always_inline)) {
+        dma16_sv(iq, qgo, lds_addr(&g_pq[0][0]) + st * TSZ + 1024 * wave);
+        if (ip0 + kT <= p.N) {
+            dma16_sv(io, ogo, lds_addr(&g_po[0][0]) + st * TSZ + 1024 * wave);
+        } else {
+            const int slot = 64 * wave + lane;
+            const int r = slot / CPR, ps = slot % CPR;
+            const int rr = min(r, p.N - 1 - ip0);
+            dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(&g_po[0][0]) + st * TSZ + 1024 * wave);
+        }
+        if (wave < 4 && lane < 4) dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(&g_ps[0][0]) + st * 256 + 64 * wave);
+        if (++ih == p.G) {
+            ih = 0;
+            ++iti;
+            seek();
+        } else {
+            iq += D;
+            io += p.ds2;
+            isl += p.Npad;
+        }
+    };
+
+    f32x16_t dva[NDB], dka[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -544,23 +728,149 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
             dka[db][e] = 0.f;
         }
     }
-    for (int cc = 0; cc < nch; ++cc) {
-        const __amdgpu_buffer_rsrc_t r = slot_rsrc(cc);
+    const int roff = row_read_off<D>(hl, g2, swz_kv<D>(hl));
+    const int troff = tr_read_off<D>(lane, 0), troff_hi = tr_read_off<D>(lane, 1);
+    // B operand rows: this lane's key row of K / V (k = d, 8 values per lane per chunk).
+    const int kr = kg * kT + hl;
+    const int kroff = kr * (2 * D) + 16 * (g2 ^ swz_k<D>(kr));
+
+    // Prologue: K / V and steps 0..2 in flight, all drained before the walk.
+    for (int t = 0; t < 3 && t < nsteps; ++t) issue(t);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // This wave's position tile / head counters (its steps are half, half + 2, ...).
+    int cti = 0, ch = half;
+    if (ch >= p.G) {
+        ch -= p.G;
+        ++cti;
+    }
+    uint32_t vis = 0;
+    bool any = false, all = false;
+    int vis_tile = -1;
+    int st_c = half;   // ring stage of this wave's step 2t + half
+    int st_i = 3;      // stage of the next issue (step 2t + 3)
+    auto nxt = [](int st) { return st + 1 == kStagesP ? 0 : st + 1; };
+    for (int t = 0; 2 * t < nsteps; ++t) {
+        if (t > 0) {
+            // Steps 2t and 2t+1 land (issued up to iteration t-1); step 2t+2 may stay in flight.
+            if (2 * t + 2 < nsteps) {
+                if (wave < 4) wait_vmcnt<3>();
+                else wait_vmcnt<2>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            __syncthreads();
+        }
+        // Steps 2t+3 and 2t+4 into the stages steps 2t-2 and 2t-1 used (free at t = 0).
+        if (2 * t + 3 < nsteps) {
+            issue(st_i);
+            st_i = nxt(st_i);
+        }
+        if (2 * t + 4 < nsteps) {
+            issue(st_i);
+            st_i = nxt(st_i);
+        }
+        const int s = 2 * t + half;
+        if (s < nsteps) {
+            if (cti != vis_tile) {
+                const int p0 = pos_tile(cti) * kT;
+                vis = span_bits(a1, b1, p0) | span_bits(a2, b2, p0);
+                any = __builtin_amdgcn_ballot_w64(kvalid && vis != 0u) != 0ull;
+                all = __builtin_amdgcn_ballot_w64(kvalid && vis != 0xffffffffu) == 0ull;
+                vis_tile = cti;
+            }
+            if (any) {
+                const char* qt = reinterpret_cast<const char*>(&g_pq[0][0]) + st_c * TSZ;
+                const char* ot = reinterpret_cast<const char*>(&g_po[0][0]) + st_c * TSZ;
+                const char* sp = reinterpret_cast<const char*>(&g_ps[0][0]) + st_c * 256;
+                const char* kt = reinterpret_cast<const char*>(g_pk);
+                const char* vt = reinterpret_cast<const char*>(g_pv);
+                f32x16_t sa, dp;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(sp + 4 * (4 * g2 + 8 * i));
+                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sp + 128 + 4 * (4 * g2 + 8 * i));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sa[4 * i + e] = x[e];
+                        dp[4 * i + e] = y[e];
+                    }
+                }
+#pragma unroll
+                for (int cc = 0; cc < NC; ++cc) {
+                    const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + (roff ^ (32 * cc)));
+                    const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + (kroff ^ (32 * cc)));
+                    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf, sa, 0, 0, 0);
+                }
+#pragma unroll
+                for (int cc = 0; cc < NC; ++cc) {
+                    const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ot + (roff ^ (32 * cc)));
+                    const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vt + (kroff ^ (32 * cc)));
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf, dp, 0, 0, 0);
+                }
+                if (!all) apply_mask(sa, vis, g2);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    sa[e] = __builtin_amdgcn_exp2f(sa[e]);   // P
+                    dp[e] *= sa[e];                          // dS
+                }
+                bf16x8_t pb[2], sb[2];
+                pack_b(sa, pb);
+                pack_b(dp, sb);
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ot, troff, troff_hi, db, kh), pb[kh], dva[db], 0, 0, 0);
+                        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt, troff, troff_hi, db, kh), sb[kh], dka[db], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // Next step of this wave: two steps on.
+        ch += 2;
+        while (ch >= p.G) {
+            ch -= p.G;
+            ++cti;
+        }
+        st_c = nxt(nxt(st_c));
+    }
+
+    // Pair sum: waves 4..7 hand their sums to waves 0..3 through LDS (each wave its own
+    // 32 KB array, lane-contiguous 16-byte pieces), after every wave has left the walk.
+    __syncthreads();
+    char* xb = kg == 0 ? reinterpret_cast<char*>(g_pk) : kg == 1 ? reinterpret_cast<char*>(g_pv)
+             : kg == 2 ? reinterpret_cast<char*>(&g_pq[0][0]) : reinterpret_cast<char*>(&g_po[0][0]);
+    if (half == 1) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const f32x4_t xv = __builtin_amdgcn_raw_buffer_load_b128(r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-                const f32x4_t xk = __builtin_amdgcn_raw_buffer_load_b128(r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dva[db][4 * qd + i] += xv[i];
-                    dka[db][4 * qd + i] += xk[i];
-                }
+                const f32x4_t xv = {dva[db][4 * qd], dva[db][4 * qd + 1], dva[db][4 * qd + 2], dva[db][4 * qd + 3]};
+                const f32x4_t xk = {dka[db][4 * qd], dka[db][4 * qd + 1], dka[db][4 * qd + 2], dka[db][4 * qd + 3]};
+                *reinterpret_cast<f32x4_t*>(xb + ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane) = xv;
+                *reinterpret_cast<f32x4_t*>(xb + ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane) = xk;
             }
         }
     }
-    store_final(dva, dka);
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xb + ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane);
+            const f32x4_t xk = *reinterpret_cast<const f32x4_t*>(xb + ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dva[db][4 * qd + i] += xv[i];
+                dka[db][4 * qd + i] += xk[i];
+            }
+        }
+    }
+    dkdv_finish<D>(p, c, nch, kblk, bg, kg, lane, b, g, j, kvalid, dva, dka);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -910,7 +1220,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.nch_max = w.nch;
     kp.tc = w.tc;
     const dim3 kg((unsigned)((int64_t)w.nch * w.kblocks * bg_count));
-    if (a.d == 128) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128>), kg, dim3(kThreadsB), 0, s, kp);
+    if (a.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_pair_kernel, kg, dim3(kThreadsP), 0, s, kp);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), kg, dim3(kThreadsB), 0, s, kp);
 
     DqParams qp;
