@@ -798,17 +798,25 @@ __global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvPar
                         dp[4 * i + e] = y[e];
                     }
                 }
+                // S and dP chunks alternate (i even: S chunk i/2, odd: dP chunk i/2); both
+                // operands of MFMA i are read PF MFMAs ahead, in a ring of PF + 1 pairs, with a
+                // scheduling fence per MFMA (at 256 registers the compiler would otherwise wait
+                // for each pair right before its MFMA).
+                constexpr int NA = 2 * NC, PF = 3;
+                bf16x8_t ar[PF + 1], br[PF + 1];
+                auto opread = [&](const int i) __attribute__((always_inline)) {
+                    const int cc = i >> 1;
+                    ar[i % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(((i & 1) ? ot : qt) + (roff ^ (32 * cc)));
+                    br[i % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(((i & 1) ? vt : kt) + (kroff ^ (32 * cc)));
+                };
 #pragma unroll
-                for (int cc = 0; cc < NC; ++cc) {
-                    const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + (roff ^ (32 * cc)));
-                    const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + (kroff ^ (32 * cc)));
-                    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf, sa, 0, 0, 0);
-                }
+                for (int i = 0; i < PF; ++i) opread(i);
 #pragma unroll
-                for (int cc = 0; cc < NC; ++cc) {
-                    const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ot + (roff ^ (32 * cc)));
-                    const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vt + (kroff ^ (32 * cc)));
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf, dp, 0, 0, 0);
+                for (int i = 0; i < NA; ++i) {
+                    if (i + PF < NA) opread(i + PF);
+                    if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[i % (PF + 1)], br[i % (PF + 1)], dp, 0, 0, 0);
+                    else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[i % (PF + 1)], br[i % (PF + 1)], sa, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 if (!all) apply_mask(sa, vis, g2);
 #pragma unroll
