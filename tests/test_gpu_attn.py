@@ -12,7 +12,7 @@ import torch
 import structured_mask_attention_amd as M
 from oracle import mars_oracle as O
 from structured_mask_attention_amd import inputs as I
-from tests.gpu_helpers import check_close, dev, expected_tilelog, lse_bound, sample_rows, to_np64
+from tests.gpu_helpers import LSE_FIXED, check_close, dev, expected_tilelog, lse_bound, sample_rows, to_np64
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,7 @@ def test_bf16_small_all_rows(b, hq, hkv, d, P, L, B):
     err, bound = np.abs(got_lse - ref_lse), lse_bound(q, k)
     print(f"  lse max_abs={err.max():.3e} max_abs/bound={np.max(err / bound):.3f}", flush=True)
     assert np.all(err <= bound)
+    assert err.max() <= LSE_FIXED
 
 
 def test_fp32_tiny_workload():

@@ -15,8 +15,8 @@ import torch
 import structured_mask_attention_amd as M
 from oracle import mars_oracle as O
 from structured_mask_attention_amd import inputs as I
-from tests.gpu_helpers import (PMAX_ABS, bwd_bounds, check_bounded, check_close, dev, expected_tilelog_intervals,
-                               lse_bound, tie_zone_sequences, tie_zone_width, to_np64)
+from tests.gpu_helpers import (LSE_FIXED, PMAX_ABS, bwd_bounds, check_bounded, check_close, dev,
+                               expected_tilelog_intervals, lse_bound, tie_zone_sequences, tie_zone_width, to_np64)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,6 +89,7 @@ def test_sweep_forward(b, hq, hkv, d, P, L, B, seed):
     check_close(to_np64(out), ref, f"sweep O b{b} h{hq}/{hkv} d{d} P{P} L{L} B{B}")
     err = np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse)
     assert np.all(err <= lse_bound(q, k)), "LSE beyond its bound"
+    assert err.max() <= LSE_FIXED, f"LSE error {err.max()} beyond the fixed target"
     rb, kb, _ = M.mars_attn_tilelog_geometry(b, hq, hkv, d, P, L, B)
     exp = expected_tilelog_intervals(P, L, B, hq // hkv, rb, kb)
     log = log.cpu().numpy()
