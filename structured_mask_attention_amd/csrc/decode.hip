@@ -8,8 +8,7 @@
 //      32-column MFMA blocks; S^T = K Q^T (K tile read from LDS as the A operand), online
 //      softmax, O^T += V^T P^T (V read back transposed with ds_read_b64_tr_b16).  K and V
 //      32-key steps stream into a 3-stage LDS ring by global_load_lds_dwordx4 (two steps
-//      in flight; a wave-uniform base per step plus fixed per-lane offsets; the copies carry
-//      the non-temporal hint, since every cache byte is read once).  Each chunk
+//      in flight; a wave-uniform base per step plus fixed per-lane offsets).  Each chunk
 //      writes an unnormalised partial (acc, m, l) to the workspace.
 //   2. combine: one workgroup per (sequence, query head): the window keys (at most W dot
 //      products per row) and a log-sum-exp merge of the chunk partials.
@@ -118,8 +117,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
         if (__builtin_amdgcn_readfirstlane(k0 + kStep <= k_end ? 1 : 0)) {
 #pragma unroll
             for (int j = 0; j < NINS; ++j) {
-                dma16_sv_nt(kb, ko[j], lds_addr(dec_k<ST>()) + 1024 * j);
-                dma16_sv_nt(vb, vo[j], lds_addr(dec_v<ST>()) + 1024 * j);
+                dma16_sv(kb, ko[j], lds_addr(dec_k<ST>()) + 1024 * j);
+                dma16_sv(vb, vo[j], lds_addr(dec_v<ST>()) + 1024 * j);
             }
         } else {
             // Last, partial step of the chunk: rows past the end repeat the last key.
@@ -129,8 +128,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeKParams p) {
                 const int slot = 64 * j + lane;
                 const int r = slot / CPR, pos = slot % CPR;
                 const int rr = min(r, last);
-                dma16_sv_nt(kb, (uint32_t)(rr * p.kcs2 * 2 + 16 * (pos ^ swz_k<D>(r))), lds_addr(dec_k<ST>()) + 1024 * j);
-                dma16_sv_nt(vb, (uint32_t)(rr * p.vcs2 * 2 + 16 * (pos ^ swz_v<D>(r))), lds_addr(dec_v<ST>()) + 1024 * j);
+                dma16_sv(kb, (uint32_t)(rr * p.kcs2 * 2 + 16 * (pos ^ swz_k<D>(r))), lds_addr(dec_k<ST>()) + 1024 * j);
+                dma16_sv(vb, (uint32_t)(rr * p.vcs2 * 2 + 16 * (pos ^ swz_v<D>(r))), lds_addr(dec_v<ST>()) + 1024 * j);
             }
         }
     };

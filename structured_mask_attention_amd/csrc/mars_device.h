@@ -176,20 +176,6 @@ __device__ inline void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_w
         : "memory");
 }
 
-// The same copy with the non-temporal hint: for data read exactly once (a KV cache chunk),
-// so it is not kept in the caches at the expense of data that is reused.
-__device__ inline void dma16_sv_nt(const void* sbase, uint32_t voff, uint32_t lds_window) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %2, %3 nt\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_window), "v"(voff), "s"(sbase)
-        : "memory");
-}
-
 // s_waitcnt vmcnt(N) for the gfx9 encoding (expcnt/lgkmcnt left unconstrained).
 template <int N>
 __device__ inline void wait_vmcnt() {
