@@ -271,105 +271,91 @@ struct DkvParams {
     uint16_t* dk;
     uint16_t* dv;
     float* part;             // workspace [nch_max][kblocks][bg][4 waves][32 keys x 2D] fp32
-    int* cnt;                // workspace [kblocks][bg][4 waves], zero on entry
+    int* cnt;                // workspace [kblocks][bg][4 key groups][dV, dK], zero on entry
     int64_t ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
     int hq, hkv, G, P, L, B, N, Npad;
     int bg_count, kblocks, nch_max, tc;
 };
 
-// dK / dV of one wave's 32 keys (key group kg of the block; j = this lane's key): stored
-// directly when the walk is one chunk, else through the chunk partials and the per-slice
-// arrival counter.
+// dV (part 0) or dK (part 1) of one wave's 32 keys (key group kg of the block; j = this
+// lane's key), from its accumulator acc = dV^T or dK^T: stored directly when the walk is one
+// chunk, else through the chunk partials and the per-(slice, part) arrival counter.
 template <int D>
-__device__ inline void dkdv_finish(const DkvParams& p, int c, int nch, int kblk, int bg, int kg, int lane, int b,
-                                   int g, int j, bool kvalid, f32x16_t (&dva)[D / 32], f32x16_t (&dka)[D / 32]) {
+__device__ inline void dkdv_finish_part(const DkvParams& p, int part, int c, int nch, int kblk, int bg, int kg,
+                                        int lane, int b, int g, int j, bool kvalid, f32x16_t (&acc)[D / 32]) {
     constexpr int NDB = D / 32;
     const int g2 = lane >> 5;
-    // dV = dV^T^T; dK = ln2 * dK^T^T (Qc carries scale*log2(e) where dK needs scale).
-    // A walk in several chunks: every chunk stores its fp32 partial for its 32 keys; the
-    // wave that arrives last for this 32-key slice (per-slice counter) sums the partials in
-    // chunk order (the same order whoever is last) and stores the result.
-    auto store_final = [&](const f32x16_t* gv, const f32x16_t* gk) __attribute__((always_inline)) {
-        if (!kvalid) return;
-        uint16_t* vo = p.dv + b * p.dvs0 + (int64_t)j * p.dvs1 + (int64_t)g * p.dvs2;
-        uint16_t* ko = p.dk + b * p.dks0 + (int64_t)j * p.dks1 + (int64_t)g * p.dks2;
+    if (nch > 1) {
+        // A walk in several chunks: every chunk stores its fp32 partial for its 32 keys; the
+        // wave that arrives last for this 32-key slice and part (one counter each) sums the
+        // partials in chunk order (the same order whoever is last).  Slot of a slice:
+        // [dV | dK][d block][4 element groups][64 lanes] x 16 bytes, so every store / load
+        // instruction moves 1 KB of contiguous memory.  Both are system coherent (sc0 sc1):
+        // written through to memory and read from it, so chunks on other XCDs see them
+        // without cache maintenance.
+        constexpr int kPartBytes = NDB * 4 * 64 * 16;
+        constexpr int kSysCoherent = 1 | 16;   // sc0 | sc1
+        auto part_rsrc = [&](int cc) __attribute__((always_inline)) {
+            char* base = reinterpret_cast<char*>(p.part) +
+                         ((((int64_t)cc * p.kblocks + kblk) * p.bg_count + bg) * kWavesB + kg) * (int64_t)(2 * kPartBytes) +
+                         part * kPartBytes;
+            return __builtin_amdgcn_make_buffer_rsrc(base, 0, kPartBytes, 0x00020000);
+        };
+        {
+            const __amdgpu_buffer_rsrc_t r = part_rsrc(c);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const int d = 32 * db + 8 * bb + 4 * g2;
-                uint2 wv, wk;
-                wv.x = pack_bf16x2(gv[db][4 * bb + 0], gv[db][4 * bb + 1]);
-                wv.y = pack_bf16x2(gv[db][4 * bb + 2], gv[db][4 * bb + 3]);
-                wk.x = pack_bf16x2(gk[db][4 * bb + 0] * kLn2, gk[db][4 * bb + 1] * kLn2);
-                wk.y = pack_bf16x2(gk[db][4 * bb + 2] * kLn2, gk[db][4 * bb + 3] * kLn2);
-                *reinterpret_cast<uint2*>(vo + d) = wv;
-                *reinterpret_cast<uint2*>(ko + d) = wk;
+                for (int qd = 0; qd < 4; ++qd) {
+                    const f32x4_t x = {acc[db][4 * qd], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(x, r, (db * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
+                }
             }
         }
-    };
-    if (nch == 1) {
-        store_final(dva, dka);
-        return;
-    }
-    // Partial of this wave: [dV | dK][d block][4 element groups][64 lanes] x 16 bytes, so
-    // every store / load instruction moves 1 KB of contiguous memory.  Both are system
-    // coherent (sc0 sc1): written through to memory and read from it, so chunks on other
-    // XCDs see them without cache maintenance.
-    constexpr int kSlotBytes = 2 * NDB * 4 * 64 * 16;
-    auto slot_rsrc = [&](int cc) __attribute__((always_inline)) {
-        char* base = reinterpret_cast<char*>(p.part) +
-                     ((((int64_t)cc * p.kblocks + kblk) * p.bg_count + bg) * kWavesB + kg) * (int64_t)kSlotBytes;
-        return __builtin_amdgcn_make_buffer_rsrc(base, 0, kSlotBytes, 0x00020000);
-    };
-    constexpr int kSysCoherent = 1 | 16;   // sc0 | sc1
-    {
-        const __amdgpu_buffer_rsrc_t r = slot_rsrc(c);
+        // Every partial store of this wave completes before its arrival is counted.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        int old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(p.cnt + (((int64_t)kblk * p.bg_count + bg) * kWavesB + kg) * 2 + part, 1,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        asm volatile("" ::: "memory");
+        if (old != nch - 1) return;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const f32x4_t xv = {dva[db][4 * qd], dva[db][4 * qd + 1], dva[db][4 * qd + 2], dva[db][4 * qd + 3]};
-                const f32x4_t xk = {dka[db][4 * qd], dka[db][4 * qd + 1], dka[db][4 * qd + 2], dka[db][4 * qd + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(xv, r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-                __builtin_amdgcn_raw_buffer_store_b128(xk, r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-            }
+            for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
         }
-    }
-    // Every partial store of this wave completes before its arrival is counted.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    int old = 0;
-    if (lane == 0)
-        old = __hip_atomic_fetch_add(p.cnt + ((int64_t)kblk * p.bg_count + bg) * kWavesB + kg, 1,
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    asm volatile("" ::: "memory");
-    if (old != nch - 1) return;
+#pragma unroll 1
+        for (int cc = 0; cc < nch; ++cc) {
+            const __amdgpu_buffer_rsrc_t r = part_rsrc(cc);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            dva[db][e] = 0.f;
-            dka[db][e] = 0.f;
-        }
-    }
-    for (int cc = 0; cc < nch; ++cc) {
-        const __amdgpu_buffer_rsrc_t r = slot_rsrc(cc);
+                for (int qd = 0; qd < 4; ++qd) {
+                    const f32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (db * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const f32x4_t xv = __builtin_amdgcn_raw_buffer_load_b128(r, ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-                const f32x4_t xk = __builtin_amdgcn_raw_buffer_load_b128(r, ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane, 0, kSysCoherent);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dva[db][4 * qd + i] += xv[i];
-                    dka[db][4 * qd + i] += xk[i];
+                    for (int i = 0; i < 4; ++i) acc[db][4 * qd + i] += x[i];
                 }
             }
         }
     }
-    store_final(dva, dka);
+    // dV = dV^T^T; dK = ln2 * dK^T^T (Qc carries scale*log2(e) where dK needs scale).
+    if (!kvalid) return;
+    const float mul = part ? kLn2 : 1.f;
+    uint16_t* out = part ? p.dk + b * p.dks0 + (int64_t)j * p.dks1 + (int64_t)g * p.dks2
+                         : p.dv + b * p.dvs0 + (int64_t)j * p.dvs1 + (int64_t)g * p.dvs2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int d = 32 * db + 8 * bb + 4 * g2;
+            uint2 w;
+            w.x = pack_bf16x2(acc[db][4 * bb + 0] * mul, acc[db][4 * bb + 1] * mul);
+            w.y = pack_bf16x2(acc[db][4 * bb + 2] * mul, acc[db][4 * bb + 3] * mul);
+            *reinterpret_cast<uint2*>(out + d) = w;
+        }
+    }
 }
 
 template <int D>
@@ -587,7 +573,8 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
         if (t0 + 2 < nsteps) body(t0 + 2, S2{});
     }
 
-    dkdv_finish<D>(p, c, nch, kblk, bg, wave, lane, b, g, j, kvalid, dva, dka);
+    dkdv_finish_part<D>(p, 0, c, nch, kblk, bg, wave, lane, b, g, j, kvalid, dva);
+    dkdv_finish_part<D>(p, 1, c, nch, kblk, bg, wave, lane, b, g, j, kvalid, dka);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -878,7 +865,8 @@ __global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvPar
             }
         }
     }
-    dkdv_finish<D>(p, c, nch, kblk, bg, kg, lane, b, g, j, kvalid, dva, dka);
+    dkdv_finish_part<D>(p, 0, c, nch, kblk, bg, kg, lane, b, g, j, kvalid, dva);
+    dkdv_finish_part<D>(p, 1, c, nch, kblk, bg, kg, lane, b, g, j, kvalid, dka);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1060,15 +1048,25 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
             s[e] = nl;
             dp[e] = nd;
         }
+        // S and dP chunks alternate (i even: S chunk i/2, odd: dP chunk i/2), each A operand
+        // read PF MFMAs ahead with a scheduling fence per MFMA (near the register limit the
+        // compiler would otherwise wait for each read right before its MFMA).
+        {
+            constexpr int NA = 2 * NC, PF = 3;
+            bf16x8_t ar[PF + 1];
+            auto opread = [&](const int i) __attribute__((always_inline)) {
+                ar[i % (PF + 1)] = (i & 1) ? *reinterpret_cast<const bf16x8_t*>(vt_lds + (vroff ^ (32 * (i >> 1))))
+                                           : *reinterpret_cast<const bf16x8_t*>(kt_lds + (kroff ^ (32 * (i >> 1))));
+            };
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-            const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kt_lds + (kroff ^ (32 * cc)));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[cc], s, 0, 0, 0);
-        }
+            for (int i = 0; i < PF; ++i) opread(i);
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-            const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vt_lds + (vroff ^ (32 * cc)));
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[cc], dp, 0, 0, 0);
+            for (int i = 0; i < NA; ++i) {
+                if (i + PF < NA) opread(i + PF);
+                if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[i % (PF + 1)], of[i >> 1], dp, 0, 0, 0);
+                else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[i % (PF + 1)], qf[i >> 1], s, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (!(cls & 2)) {
             auto low = [](int x) { return x >= 32 ? 0xffffffffu : (1u << max(x, 0)) - 1u; };
@@ -1135,7 +1133,7 @@ void walk_plan(int P, int L, int B, int N, int bg, int d, int* tc, int* nch_max)
 }
 
 // Workspace: Qc [batch][Npad][hq][D] bf16 | -LSE2 [batch][hq][Npad] | -D [batch][hq][Npad] |
-// counters [kblocks][batch*hkv][4] int | partials [nch][kblocks][batch*hkv][4 waves][32 x 2D] fp32
+// counters [kblocks][batch*hkv][4][2] int | partials [nch][kblocks][batch*hkv][4][32 x 2D] fp32
 // (partials only when some key block's walk is split).
 struct BwdLayout {
     size_t qc, nlse, ndelta, cnt, part, total;
@@ -1151,7 +1149,7 @@ BwdLayout bwd_layout(int batch, int hq, int hkv, int d, int P, int L, int B, int
     w.nlse = r256((size_t)batch * w.Npad * hq * d * 2);
     w.ndelta = w.nlse + r256((size_t)batch * hq * w.Npad * 4);
     w.cnt = w.ndelta + r256((size_t)batch * hq * w.Npad * 4);
-    w.part = w.cnt + r256((size_t)w.kblocks * bg * kWavesB * 4);
+    w.part = w.cnt + r256((size_t)w.kblocks * bg * kWavesB * 2 * 4);
     w.total = w.part + (w.nch > 1 ? r256((size_t)w.nch * w.kblocks * bg * kKeysPerWG * 2 * d * 4) : 0);
     return w;
 }
@@ -1191,7 +1189,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     pp.hq = a.hq;
     pp.N = a.N;
     pp.Npad = Npad;
-    pp.ncnt = w.kblocks * bg_count * kWavesB;
+    pp.ncnt = w.kblocks * bg_count * kWavesB * 2;
     pp.c = c;
     int64_t prep_threads = (int64_t)a.batch * Npad * a.hq * (a.d / 8);
     if (prep_threads < pp.ncnt) prep_threads = pp.ncnt;
