@@ -9,19 +9,22 @@
 // dK and dV of a KV head summed over its G query heads.  Three kernels:
 //   1. prep (per row): Qc = bf16(Q*c) exactly as the forward rounds it, -D and
 //      -LSE*log2(e), into the workspace, positions padded to a multiple of 32 (zeros);
-//   2. dK/dV (key-stationary): a workgroup owns 128 keys of one (batch, kv head), 32 per
-//      wave with K and V fragments in registers, and walks the (32-position, head) tiles
-//      of every row that sees one of its keys (a union of at most three position
-//      intervals).  Qc and dO tiles plus the two per-row scalars stream through a 3-stage
-//      LDS ring (global_load_lds_dwordx4, XOR-swizzled chunks).  Per tile and wave:
-//      S = Qc K^T and dP = dO V^T (MFMA accumulators start at -LSE2 and -D), P = 2^S,
-//      dS = P dP, then dV^T += dO^T P and dK^T += Qc^T dS with the transposed operands read
-//      by ds_read_b64_tr_b16.  The element mask is a per-key bitmask over the tile's 32
-//      positions.  A heavy key block (prompt keys are seen by every row) splits its walk
+//   2. dK/dV (key-stationary): a workgroup owns a block of keys of one (batch, kv head) and
+//      walks the (32-position, head) tiles of every row that sees one of its keys (a union
+//      of at most three position intervals).  Qc and dO tiles plus the two per-row scalars
+//      stream through an LDS ring (global_load_lds_dwordx4, XOR-swizzled chunks).  Per
+//      tile and 32-key group: S = Qc K^T and dP = dO V^T (MFMA accumulators start at -LSE2
+//      and -D), P = 2^S, dS = P dP, then dV^T += dO^T P and dK^T += Qc^T dS with the
+//      transposed operands read by ds_read_b64_tr_b16.  Head_dim 64: 128 keys, one wave
+//      per 32 keys with K and V fragments in registers, a 3-stage ring.  Head_dim 128: 192
+//      keys, two waves per 32 keys split by role (K, S, P, dV on one; V, dP, dS, dK on the
+//      other, P handed over through LDS), three waves per SIMD, a 5-stage ring.  The
+//      element mask is a per-key bitmask over the tile's 32 positions.  A heavy key block
+//      (prompt keys are seen by every row) splits its walk
 //      into up to 8 chunks on separate workgroups (chunk size from the layout's total work);
 //      their fp32 partials are written through to memory and summed in chunk order by
-//      whichever wave of a 32-key slice arrives last (one counter per slice), so the result
-//      does not depend on the arrival order.
+//      whichever wave arrives last for a 32-key slice and gradient (one counter each), so
+//      the result does not depend on the arrival order.
 //   3. dQ (row-stationary): the forward's row packing, tile walk, tile classes and K/V
 //      ring; per tile S^T = K Qc^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 // P and dS enter the MFMAs as bf16 (round to nearest even); statistics and accumulation
@@ -40,7 +43,7 @@ constexpr int kWavesB = 4;
 constexpr int kThreadsB = 64 * kWavesB;
 constexpr int kT = 32;               // keys per dQ tile; positions per dK/dV tile; rows or keys per wave
 constexpr int kStagesB = 3;
-constexpr int kKeysPerWG = kWavesB * kT;   // dK/dV: 128 keys per workgroup
+constexpr int kKeysPerWG = kWavesB * kT;   // dK/dV at head_dim 64: 128 keys per workgroup
 constexpr int kRowsPerWGB = kWavesB * kT;  // dQ: 128 packed rows per workgroup
 constexpr int kChunkMax = 8;               // dK/dV: a key block's walk splits into at most 8 chunks
 constexpr int kChunkMinTiles = 4;          //        of at least 4 position tiles each
@@ -270,11 +273,12 @@ struct DkvParams {
     const float* ndelta;
     uint16_t* dk;
     uint16_t* dv;
-    float* part;             // workspace [nch_max][kblocks][bg][4 waves][32 keys x 2D] fp32
-    int* cnt;                // workspace [kblocks][bg][4 key groups][dV, dK], zero on entry
+    float* part;             // workspace [nch_max][kblocks][bg][key groups][32 keys x 2D] fp32
+    int* cnt;                // workspace [kblocks][bg][key groups][dV, dK], zero on entry
     int64_t ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
     int hq, hkv, G, P, L, B, N, Npad;
     int bg_count, kblocks, nch_max, tc;
+    int kgroups;             // 32-key groups per key block (4 at head_dim 64, 6 at 128)
 };
 
 // dV (part 0) or dK (part 1) of one wave's 32 keys (key group kg of the block; j = this
@@ -297,7 +301,7 @@ __device__ inline void dkdv_finish_part(const DkvParams& p, int part, int c, int
         constexpr int kSysCoherent = 1 | 16;   // sc0 | sc1
         auto part_rsrc = [&](int cc) __attribute__((always_inline)) {
             char* base = reinterpret_cast<char*>(p.part) +
-                         ((((int64_t)cc * p.kblocks + kblk) * p.bg_count + bg) * kWavesB + kg) * (int64_t)(2 * kPartBytes) +
+                         ((((int64_t)cc * p.kblocks + kblk) * p.bg_count + bg) * p.kgroups + kg) * (int64_t)(2 * kPartBytes) +
                          part * kPartBytes;
             return __builtin_amdgcn_make_buffer_rsrc(base, 0, kPartBytes, 0x00020000);
         };
@@ -316,7 +320,7 @@ __device__ inline void dkdv_finish_part(const DkvParams& p, int part, int c, int
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         int old = 0;
         if (lane == 0)
-            old = __hip_atomic_fetch_add(p.cnt + (((int64_t)kblk * p.bg_count + bg) * kWavesB + kg) * 2 + part, 1,
+            old = __hip_atomic_fetch_add(p.cnt + (((int64_t)kblk * p.bg_count + bg) * p.kgroups + kg) * 2 + part, 1,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __builtin_amdgcn_readfirstlane(old);
         asm volatile("" ::: "memory");
@@ -578,34 +582,42 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
 }
 
 // ---------------------------------------------------------------------------------------
-// 2b. dK / dV at head_dim 128: two waves per SIMD.
-//   One kernel variant for head_dim 128, where a wave's K / V fragments plus its dK / dV
-//   accumulators leave room for one wave per SIMD only.  Here a workgroup of 8 waves owns the
-//   same 128 keys: K and V of those keys sit in LDS (read as B operands each step), and the
-//   waves w and w + 4 share key group w % 4, wave w taking the walk's even steps and wave
-//   w + 4 the odd ones; their dK / dV sums are added through LDS at the end.  Each step's
-//   Qc / dO tile and row scalars go into a 5-stage ring (two steps in use, three in
-//   flight), copied by all 8 waves.  Per step and wave the arithmetic is the 4-wave
-//   kernel's.
+// 2b. dK / dV at head_dim 128: role-split wave pairs, three waves per SIMD.
+//   At head_dim 128 a wave's dK and dV sums plus its keys' K and V fragments need about
+//   400 registers.  Split by role, a wave holds one sum and one fragment set (~160
+//   registers), so three waves fit a SIMD.  A workgroup of 12 waves owns 192 keys; waves w
+//   and w + 6 share key group w and split every step's products:
+//     role 0 (wave w):     K fragments in registers; S = Qc K^T - LSE2, P = 2^S,
+//                          dV^T += dO^T P;
+//     role 1 (wave w + 6): V fragments in registers; dP = dO V^T - D, dS = P o dP,
+//                          dK^T += Qc^T dS.
+//   P goes from role 0 to role 1 in fp32 through a two-buffer LDS exchange, so role 1 runs
+//   one step behind: in iteration t it finishes step t - 1 (dS, dK MFMAs) and then issues
+//   the dP MFMAs of step t, whose result it carries into iteration t + 1.  K and V never go
+//   through LDS; each step's Qc / dO tiles serve 192 keys.  The tiles and row scalars
+//   stream through a 5-stage ring, one step per iteration (steps t - 1 and t in use, three
+//   in flight): waves 0..7 copy the tile windows, waves 8..11 the scalars.
 // ---------------------------------------------------------------------------------------
-constexpr int kWavesP = 8;
-constexpr int kThreadsP = 64 * kWavesP;
-constexpr int kStagesP = 5;
-__shared__ __attribute__((aligned(16))) uint16_t g_pk[kKeysPerWG * 128];     // K rows of the block
-__shared__ __attribute__((aligned(16))) uint16_t g_pv[kKeysPerWG * 128];     // V rows of the block
-__shared__ __attribute__((aligned(16))) uint16_t g_pq[kStagesP][kT * 128];   // Qc tiles
-__shared__ __attribute__((aligned(16))) uint16_t g_po[kStagesP][kT * 128];   // dO tiles
-__shared__ __attribute__((aligned(16))) float g_ps[kStagesP][64];            // [-LSE2 x 32][-D x 32]
+constexpr int kGroupsR = 6;                  // 32-key groups per workgroup
+constexpr int kWavesR = 2 * kGroupsR;
+constexpr int kThreadsR = 64 * kWavesR;
+constexpr int kKeysPerWGR = kGroupsR * kT;   // 192
+constexpr int kStagesR = 5;
+__shared__ __attribute__((aligned(16))) uint16_t g_rq[kStagesR][kT * 128];   // Qc tiles
+__shared__ __attribute__((aligned(16))) uint16_t g_ro[kStagesR][kT * 128];   // dO tiles
+__shared__ __attribute__((aligned(16))) float g_rs[kStagesR][64];            // [-LSE2 x 32][-D x 32]
+__shared__ __attribute__((aligned(16))) float g_rx[2][kGroupsR][16 * 64];    // P: [parity][key group][element][lane]
 
-__global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvParams p) {
+__global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvParams p) {
     constexpr int D = 128;
     constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
     constexpr int TSZ = kT * D * 2;                 // bytes of one Qc or dO tile
-    static_assert(kT * CPR / 64 == kWavesP, "one 1 KB copy window of each tile per wave");
+    static_assert(kT * CPR / 64 == 8, "one 1 KB copy window of each tile per wave of 0..7");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int kg = wave & 3, half = wave >> 2;
+    const int role = wave >= kGroupsR ? 1 : 0;
+    const int kg = wave - kGroupsR * role;
     const int hl = lane & 31, g2 = lane >> 5;
     const int c = blockIdx.x % p.nch_max;
     const int rest = blockIdx.x / p.nch_max;
@@ -613,8 +625,8 @@ __global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvPar
     const int kblk = rest / p.bg_count;
     const int b = bg / p.hkv, g = bg % p.hkv;
     const int PL = p.P + p.L;
-    const int kb0 = kblk * kKeysPerWG;
-    const int kb1 = min(kb0 + kKeysPerWG, p.N);
+    const int kb0 = kblk * kKeysPerWGR;
+    const int kb1 = min(kb0 + kKeysPerWGR, p.N);
 
     int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
     kblock_tile_ranges(kb0, kb1, p.P, p.L, p.B, p.N, rs, re);
@@ -645,29 +657,24 @@ __global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvPar
         }
     }
 
-    // K / V rows of the block into LDS: window w (1 KB = 4 rows) of each, rows past N repeat
-    // row N-1; chunk ps of row r at ps ^ swz_k(r) (the B operand reads are row reads).
+    // B operand of the S (role 0) or dP (role 1) MFMAs: this lane's key row of K or V, chunk
+    // cc = d in [16 cc + 8 g2, 16 cc + 8 g2 + 8); keys past N repeat row N - 1 (never visible).
+    bf16x8_t bfr[NC];
     {
-        const uint16_t* kbase = p.k + b * p.ks0 + (int64_t)g * p.ks2;
-        const uint16_t* vbase = p.v + b * p.vs0 + (int64_t)g * p.vs2;
+        const int jj = min(j, p.N - 1);
+        const uint16_t* src = role == 0 ? p.k + b * p.ks0 + (int64_t)jj * p.ks1 + (int64_t)g * p.ks2
+                                        : p.v + b * p.vs0 + (int64_t)jj * p.vs1 + (int64_t)g * p.vs2;
 #pragma unroll
-        for (int w = 0; w < kKeysPerWG * CPR / 64 / kWavesP; ++w) {
-            const int win = wave * (kKeysPerWG * CPR / 64 / kWavesP) + w;
-            const int slot = 64 * win + lane;
-            const int r = slot / CPR, ps = slot % CPR;
-            const int rr = min(kb0 + r, p.N - 1);
-            dma16_sv(kbase, (uint32_t)(rr * p.ks1 * 2 + 16 * (ps ^ swz_k<D>(r))), lds_addr(g_pk) + 1024 * win);
-            dma16_sv(vbase, (uint32_t)(rr * p.vs1 * 2 + 16 * (ps ^ swz_k<D>(r))), lds_addr(g_pv) + 1024 * win);
-        }
+        for (int cc = 0; cc < NC; ++cc) bfr[cc] = *reinterpret_cast<const bf16x8_t*>(src + 16 * cc + 8 * g2);
     }
 
-    // Step copies: wave w moves window w of the Qc tile and of the dO tile, waves 0..3 also
-    // 64 bytes of the row scalars (as the 4-wave kernel).  Walk order: position tile, then
+    // Step copies: wave w < 8 moves window w of the Qc tile and of the dO tile, wave 8 + i
+    // 64 bytes of the row scalars (i < 2: -LSE2, else -D).  Walk order: position tile, then
     // head; the next copy's step is (iti, ih).
     const int64_t qc_row = (int64_t)p.hq * D;
     uint32_t qgo, ogo;
     {
-        const int slot = 64 * wave + lane;
+        const int slot = 64 * (wave & 7) + lane;
         const int r = slot / CPR, ps = slot % CPR;
         qgo = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_kv<D>(r)));
         ogo = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
@@ -685,16 +692,19 @@ __global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvPar
     };
     seek();
     auto issue = [&](const int st) __attribute__((always_inline)) {
-        dma16_sv(iq, qgo, lds_addr(&g_pq[0][0]) + st * TSZ + 1024 * wave);
-        if (ip0 + kT <= p.N) {
-            dma16_sv(io, ogo, lds_addr(&g_po[0][0]) + st * TSZ + 1024 * wave);
-        } else {
-            const int slot = 64 * wave + lane;
-            const int r = slot / CPR, ps = slot % CPR;
-            const int rr = min(r, p.N - 1 - ip0);
-            dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(&g_po[0][0]) + st * TSZ + 1024 * wave);
+        if (wave < 8) {
+            dma16_sv(iq, qgo, lds_addr(&g_rq[0][0]) + st * TSZ + 1024 * wave);
+            if (ip0 + kT <= p.N) {
+                dma16_sv(io, ogo, lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * wave);
+            } else {
+                const int slot = 64 * wave + lane;
+                const int r = slot / CPR, ps = slot % CPR;
+                const int rr = min(r, p.N - 1 - ip0);
+                dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * wave);
+            }
+        } else if (lane < 4) {
+            dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(&g_rs[0][0]) + st * 256 + 64 * (wave & 3));
         }
-        if (wave < 4 && lane < 4) dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(&g_ps[0][0]) + st * 256 + 64 * wave);
         if (++ih == p.G) {
             ih = 0;
             ++iti;
@@ -706,167 +716,149 @@ __global__ __launch_bounds__(kThreadsP, 1) void attn_bwd_dkdv_pair_kernel(DkvPar
         }
     };
 
-    f32x16_t dva[NDB], dka[NDB];
+    f32x16_t acc[NDB];   // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            dva[db][e] = 0.f;
-            dka[db][e] = 0.f;
-        }
+        for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
     }
     const int roff = row_read_off<D>(hl, g2, swz_kv<D>(hl));
     const int troff = tr_read_off<D>(lane, 0), troff_hi = tr_read_off<D>(lane, 1);
-    // B operand rows: this lane's key row of K / V (k = d, 8 values per lane per chunk).
-    const int kr = kg * kT + hl;
-    const int kroff = kr * (2 * D) + 16 * (g2 ^ swz_k<D>(kr));
+    char* const xw = reinterpret_cast<char*>(&g_rx[0][kg][0]) + 16 * lane;   // + parity * 16 KB + e4 * 1 KB
 
-    // Prologue: K / V and steps 0..2 in flight, all drained before the walk.
+    // Prologue: the key fragments and steps 0..2 in flight, all drained before the walk.
     for (int t = 0; t < 3 && t < nsteps; ++t) issue(t);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
     __syncthreads();
 
-    // This wave's position tile / head counters (its steps are half, half + 2, ...).
-    int cti = 0, ch = half;
-    if (ch >= p.G) {
-        ch -= p.G;
-        ++cti;
-    }
-    uint32_t vis = 0;
-    bool any = false, all = false;
-    int vis_tile = -1;
-    int st_c = half;   // ring stage of this wave's step 2t + half
-    int st_i = 3;      // stage of the next issue (step 2t + 3)
-    auto nxt = [](int st) { return st + 1 == kStagesP ? 0 : st + 1; };
-    for (int t = 0; 2 * t < nsteps; ++t) {
-        if (t > 0) {
-            // Steps 2t and 2t+1 land (issued up to iteration t-1); step 2t+2 may stay in flight.
-            if (2 * t + 2 < nsteps) {
-                if (wave < 4) wait_vmcnt<3>();
-                else wait_vmcnt<2>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            __syncthreads();
+    // S (role 0) or dP (role 1) of a step: the accumulator starts at the rows' -LSE2 or -D
+    // (scalars at byte offset 0 or 128 of the stage); its A operand (Qc or dO rows) is read
+    // PF MFMAs ahead with a scheduling fence per MFMA.
+    auto row_product = [&](const char* at, const char* sp, f32x16_t& x) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sp + 4 * (4 * g2 + 8 * i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * i + e] = y[e];
         }
-        // Steps 2t+3 and 2t+4 into the stages steps 2t-2 and 2t-1 used (free at t = 0).
-        if (2 * t + 3 < nsteps) {
-            issue(st_i);
-            st_i = nxt(st_i);
+        constexpr int PF = 3;
+        bf16x8_t ar[PF + 1];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) ar[i] = *reinterpret_cast<const bf16x8_t*>(at + (roff ^ (32 * i)));
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            if (i + PF < NC) ar[(i + PF) % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(at + (roff ^ (32 * (i + PF))));
+            x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[i % (PF + 1)], bfr[i], x, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (2 * t + 4 < nsteps) {
-            issue(st_i);
-            st_i = nxt(st_i);
+    };
+    // acc += (tile^T) y, the transposed tile read as A operands (dO for dV, Qc for dK).
+    auto col_product = [&](const char* tt, const bf16x8_t (&y)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tt, troff, troff_hi, db, kh), y[kh], acc[db], 0, 0, 0);
         }
-        const int s = 2 * t + half;
-        if (s < nsteps) {
-            if (cti != vis_tile) {
-                const int p0 = pos_tile(cti) * kT;
-                vis = span_bits(a1, b1, p0) | span_bits(a2, b2, p0);
-                any = __builtin_amdgcn_ballot_w64(kvalid && vis != 0u) != 0ull;
-                all = __builtin_amdgcn_ballot_w64(kvalid && vis != 0xffffffffu) == 0ull;
-                vis_tile = cti;
-            }
-            if (any) {
-                const char* qt = reinterpret_cast<const char*>(&g_pq[0][0]) + st_c * TSZ;
-                const char* ot = reinterpret_cast<const char*>(&g_po[0][0]) + st_c * TSZ;
-                const char* sp = reinterpret_cast<const char*>(&g_ps[0][0]) + st_c * 256;
-                const char* kt = reinterpret_cast<const char*>(g_pk);
-                const char* vt = reinterpret_cast<const char*>(g_pv);
-                f32x16_t sa, dp;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(sp + 4 * (4 * g2 + 8 * i));
-                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sp + 128 + 4 * (4 * g2 + 8 * i));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sa[4 * i + e] = x[e];
-                        dp[4 * i + e] = y[e];
-                    }
-                }
-                // S and dP chunks alternate (i even: S chunk i/2, odd: dP chunk i/2); both
-                // operands of MFMA i are read PF MFMAs ahead, in a ring of PF + 1 pairs, with a
-                // scheduling fence per MFMA (at 256 registers the compiler would otherwise wait
-                // for each pair right before its MFMA).
-                constexpr int NA = 2 * NC, PF = 3;
-                bf16x8_t ar[PF + 1], br[PF + 1];
-                auto opread = [&](const int i) __attribute__((always_inline)) {
-                    const int cc = i >> 1;
-                    ar[i % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(((i & 1) ? ot : qt) + (roff ^ (32 * cc)));
-                    br[i % (PF + 1)] = *reinterpret_cast<const bf16x8_t*>(((i & 1) ? vt : kt) + (kroff ^ (32 * cc)));
-                };
-#pragma unroll
-                for (int i = 0; i < PF; ++i) opread(i);
-#pragma unroll
-                for (int i = 0; i < NA; ++i) {
-                    if (i + PF < NA) opread(i + PF);
-                    if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[i % (PF + 1)], br[i % (PF + 1)], dp, 0, 0, 0);
-                    else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[i % (PF + 1)], br[i % (PF + 1)], sa, 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (!all) apply_mask(sa, vis, g2);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    sa[e] = __builtin_amdgcn_exp2f(sa[e]);   // P
-                    dp[e] *= sa[e];                          // dS
-                }
-                bf16x8_t pb[2], sb[2];
-                pack_b(sa, pb);
-                pack_b(dp, sb);
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ot, troff, troff_hi, db, kh), pb[kh], dva[db], 0, 0, 0);
-                        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt, troff, troff_hi, db, kh), sb[kh], dka[db], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        // Next step of this wave: two steps on.
-        ch += 2;
-        while (ch >= p.G) {
-            ch -= p.G;
-            ++cti;
-        }
-        st_c = nxt(nxt(st_c));
-    }
+    };
 
-    // Pair sum: waves 4..7 hand their sums to waves 0..3 through LDS (each wave its own
-    // 32 KB array, lane-contiguous 16-byte pieces), after every wave has left the walk.
-    __syncthreads();
-    char* xb = kg == 0 ? reinterpret_cast<char*>(g_pk) : kg == 1 ? reinterpret_cast<char*>(g_pv)
-             : kg == 2 ? reinterpret_cast<char*>(&g_pq[0][0]) : reinterpret_cast<char*>(&g_po[0][0]);
-    if (half == 1) {
+    // Walk: iteration t handles step t (role 0; role 1 its dP) and step t - 1 (role 1's dS, dK).
+    auto walk = [&](auto role_c) __attribute__((always_inline)) {
+        constexpr int R = decltype(role_c)::value;
+        int cti = 0, ch = 0;             // position tile / head of step t
+        uint32_t vis = 0;
+        bool any = false, all = false, any_prev = false;
+        int vis_tile = -1;
+        int st_c = 0, st_p = 0;          // ring stages of steps t and t - 1
+        int st_i = 3;                    // stage of the next issue (step t + 3)
+        f32x16_t dp;                     // role 1: dP - D of step t - 1
+        if constexpr (R == 1) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const f32x4_t xv = {dva[db][4 * qd], dva[db][4 * qd + 1], dva[db][4 * qd + 2], dva[db][4 * qd + 3]};
-                const f32x4_t xk = {dka[db][4 * qd], dka[db][4 * qd + 1], dka[db][4 * qd + 2], dka[db][4 * qd + 3]};
-                *reinterpret_cast<f32x4_t*>(xb + ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane) = xv;
-                *reinterpret_cast<f32x4_t*>(xb + ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane) = xk;
-            }
+            for (int e = 0; e < 16; ++e) dp[e] = 0.f;
         }
-    }
-    __syncthreads();
-    if (half == 1) return;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xb + ((0 * NDB + db) * 4 + qd) * 1024 + 16 * lane);
-            const f32x4_t xk = *reinterpret_cast<const f32x4_t*>(xb + ((1 * NDB + db) * 4 + qd) * 1024 + 16 * lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dva[db][4 * qd + i] += xv[i];
-                dka[db][4 * qd + i] += xk[i];
+        auto nxt = [](int st) { return st + 1 == kStagesR ? 0 : st + 1; };
+        for (int t = 0; t <= nsteps; ++t) {
+            if (t > 0) {
+                // Step t lands (issued three iterations earlier or in the prologue); steps t + 1
+                // and t + 2 may stay in flight.  Per step a wave issues 2 copies (waves 0..7) or 1.
+                const int later = nsteps - 1 - t;
+                if (later >= 2) {
+                    if (wave < 8) wait_vmcnt<4>();
+                    else wait_vmcnt<2>();
+                } else if (later == 1) {
+                    if (wave < 8) wait_vmcnt<2>();
+                    else wait_vmcnt<1>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                __syncthreads();
             }
+            // Step t + 3 into the stage step t - 2 used.
+            if (t + 3 < nsteps) {
+                issue(st_i);
+                st_i = nxt(st_i);
+            }
+            any_prev = any;
+            if (t < nsteps) {
+                if (cti != vis_tile) {
+                    const int p0 = pos_tile(cti) * kT;
+                    vis = span_bits(a1, b1, p0) | span_bits(a2, b2, p0);
+                    any = __builtin_amdgcn_ballot_w64(kvalid && vis != 0u) != 0ull;
+                    all = __builtin_amdgcn_ballot_w64(kvalid && vis != 0xffffffffu) == 0ull;
+                    vis_tile = cti;
+                }
+            } else {
+                any = false;
+            }
+            char* const xc = xw + (t & 1) * (kGroupsR * 16 * 64 * 4);          // exchange buffer of step t
+            char* const xp = xw + ((t & 1) ^ 1) * (kGroupsR * 16 * 64 * 4);    // and of step t - 1
+            const char* const qt_c = reinterpret_cast<const char*>(&g_rq[0][0]) + st_c * TSZ;
+            const char* const ot_c = reinterpret_cast<const char*>(&g_ro[0][0]) + st_c * TSZ;
+            const char* const sp_c = reinterpret_cast<const char*>(&g_rs[0][0]) + st_c * 256;
+            if constexpr (R == 0) {
+                if (any) {
+                    f32x16_t sa;
+                    row_product(qt_c, sp_c, sa);
+                    if (!all) apply_mask(sa, vis, g2);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) sa[e] = __builtin_amdgcn_exp2f(sa[e]);   // P
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const f32x4_t y = {sa[4 * e4], sa[4 * e4 + 1], sa[4 * e4 + 2], sa[4 * e4 + 3]};
+                        *reinterpret_cast<f32x4_t*>(xc + 1024 * e4) = y;
+                    }
+                    bf16x8_t pb[2];
+                    pack_b(sa, pb);
+                    col_product(ot_c, pb);
+                }
+            } else {
+                if (any_prev) {
+                    const char* const qt_p = reinterpret_cast<const char*>(&g_rq[0][0]) + st_p * TSZ;
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(xp + 1024 * e4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dp[4 * e4 + i] *= y[i];      // dS
+                    }
+                    bf16x8_t sb[2];
+                    pack_b(dp, sb);
+                    col_product(qt_p, sb);
+                }
+                if (any) row_product(ot_c, sp_c + 128, dp);
+            }
+            if (++ch == p.G) {
+                ch = 0;
+                ++cti;
+            }
+            st_p = st_c;
+            st_c = nxt(st_c);
         }
-    }
-    dkdv_finish_part<D>(p, 0, c, nch, kblk, bg, kg, lane, b, g, j, kvalid, dva);
-    dkdv_finish_part<D>(p, 1, c, nch, kblk, bg, kg, lane, b, g, j, kvalid, dka);
+    };
+    if (role == 0) walk(std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 1>{});
+
+    dkdv_finish_part<D>(p, role, c, nch, kblk, bg, kg, lane, b, g, j, kvalid, acc);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1115,12 +1107,12 @@ size_t r256(size_t x) { return (x + 255) / 256 * 256; }
 // Chunk size of the dK/dV walks (position tiles): about half the mean number of tiles a
 // resident workgroup gets, at least kChunkMinTiles; and the largest chunk count over the
 // key blocks (sizes the partial buffer).
-void walk_plan(int P, int L, int B, int N, int bg, int d, int* tc, int* nch_max) {
+void walk_plan(int P, int L, int B, int N, int bg, int d, int kpb, int* tc, int* nch_max) {
     int64_t total = 0;
     int maxnpt = 0;
-    for (int kb0 = 0; kb0 < N; kb0 += kKeysPerWG) {
+    for (int kb0 = 0; kb0 < N; kb0 += kpb) {
         int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
-        const int n = kblock_tile_ranges(kb0, kb0 + kKeysPerWG < N ? kb0 + kKeysPerWG : N, P, L, B, N, rs, re);
+        const int n = kblock_tile_ranges(kb0, kb0 + kpb < N ? kb0 + kpb : N, P, L, B, N, rs, re);
         int npt = 0;
         for (int i = 0; i < n; ++i) npt += re[i] - rs[i];
         total += npt;
@@ -1133,24 +1125,27 @@ void walk_plan(int P, int L, int B, int N, int bg, int d, int* tc, int* nch_max)
 }
 
 // Workspace: Qc [batch][Npad][hq][D] bf16 | -LSE2 [batch][hq][Npad] | -D [batch][hq][Npad] |
-// counters [kblocks][batch*hkv][4][2] int | partials [nch][kblocks][batch*hkv][4][32 x 2D] fp32
+// counters [kblocks][batch*hkv][groups][2] int | partials [nch][kblocks][batch*hkv][groups][32 x 2D] fp32
+// (groups = 32-key groups per key block: 4 at head_dim 64, 6 at head_dim 128)
 // (partials only when some key block's walk is split).
 struct BwdLayout {
     size_t qc, nlse, ndelta, cnt, part, total;
-    int Npad, kblocks, nch, tc;
+    int Npad, kpb, kgroups, kblocks, nch, tc;
 };
 BwdLayout bwd_layout(int batch, int hq, int hkv, int d, int P, int L, int B, int N) {
     BwdLayout w;
     w.Npad = pad32(N);
-    w.kblocks = (N + kKeysPerWG - 1) / kKeysPerWG;
+    w.kpb = d == 128 ? kKeysPerWGR : kKeysPerWG;   // keys per dK/dV workgroup
+    w.kgroups = w.kpb / kT;
+    w.kblocks = (N + w.kpb - 1) / w.kpb;
     const size_t bg = (size_t)batch * hkv;
-    walk_plan(P, L, B, N, (int)bg, d, &w.tc, &w.nch);
+    walk_plan(P, L, B, N, (int)bg, d, w.kpb, &w.tc, &w.nch);
     w.qc = 0;
     w.nlse = r256((size_t)batch * w.Npad * hq * d * 2);
     w.ndelta = w.nlse + r256((size_t)batch * hq * w.Npad * 4);
     w.cnt = w.ndelta + r256((size_t)batch * hq * w.Npad * 4);
-    w.part = w.cnt + r256((size_t)w.kblocks * bg * kWavesB * 2 * 4);
-    w.total = w.part + (w.nch > 1 ? r256((size_t)w.nch * w.kblocks * bg * kKeysPerWG * 2 * d * 4) : 0);
+    w.part = w.cnt + r256((size_t)w.kblocks * bg * w.kgroups * 2 * 4);
+    w.total = w.part + (w.nch > 1 ? r256((size_t)w.nch * w.kblocks * bg * w.kpb * 2 * d * 4) : 0);
     return w;
 }
 
@@ -1189,7 +1184,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     pp.hq = a.hq;
     pp.N = a.N;
     pp.Npad = Npad;
-    pp.ncnt = w.kblocks * bg_count * kWavesB * 2;
+    pp.ncnt = w.kblocks * bg_count * w.kgroups * 2;
     pp.c = c;
     int64_t prep_threads = (int64_t)a.batch * Npad * a.hq * (a.d / 8);
     if (prep_threads < pp.ncnt) prep_threads = pp.ncnt;
@@ -1223,10 +1218,11 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.Npad = Npad;
     kp.bg_count = bg_count;
     kp.kblocks = w.kblocks;
+    kp.kgroups = w.kgroups;
     kp.nch_max = w.nch;
     kp.tc = w.tc;
     const dim3 kg((unsigned)((int64_t)w.nch * w.kblocks * bg_count));
-    if (a.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_pair_kernel, kg, dim3(kThreadsP), 0, s, kp);
+    if (a.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_role_kernel, kg, dim3(kThreadsR), 0, s, kp);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), kg, dim3(kThreadsB), 0, s, kp);
 
     DqParams qp;
