@@ -612,7 +612,7 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
     constexpr int D = 128;
     constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
     constexpr int TSZ = kT * D * 2;                 // bytes of one Qc or dO tile
-    static_assert(kT * CPR / 64 == 8, "one 1 KB copy window of each tile per wave of 0..7");
+    static_assert(kT * CPR / 64 == 8, "eight 1 KB copy windows per tile, two per copying wave");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -668,16 +668,18 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
         for (int cc = 0; cc < NC; ++cc) bfr[cc] = *reinterpret_cast<const bf16x8_t*>(src + 16 * cc + 8 * g2);
     }
 
-    // Step copies: wave w < 8 moves window w of the Qc tile and of the dO tile, wave 8 + i
-    // 64 bytes of the row scalars (i < 2: -LSE2, else -D).  Walk order: position tile, then
-    // head; the next copy's step is (iti, ih).
+    // Step copies, by the role-0 waves only (role 1 has the longer step): wave w < 4 moves
+    // windows 2w and 2w + 1 of the Qc tile and of the dO tile, waves 4 and 5 the 128 bytes
+    // of -LSE2 and of -D.  Walk order: position tile, then head; the next copy's step is
+    // (iti, ih).
     const int64_t qc_row = (int64_t)p.hq * D;
-    uint32_t qgo, ogo;
-    {
-        const int slot = 64 * (wave & 7) + lane;
+    uint32_t qgo[2], ogo[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int slot = 64 * (2 * (wave & 3) + jj) + lane;
         const int r = slot / CPR, ps = slot % CPR;
-        qgo = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_kv<D>(r)));
-        ogo = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
+        qgo[jj] = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_kv<D>(r)));
+        ogo[jj] = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
     }
     int iti = 0, ih = 0, ip0 = 0;
     const uint16_t* iq = nullptr;
@@ -688,22 +690,26 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
         const int head = g * p.G;
         iq = p.qc + ((int64_t)b * p.Npad + ip0) * qc_row + (int64_t)head * D;
         io = p.dout + b * p.ds0 + (int64_t)ip0 * p.ds1 + (int64_t)head * p.ds2;
-        isl = ((wave & 3) < 2 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + ip0 + 16 * (wave & 1);
+        isl = (wave == 4 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + ip0;
     };
     seek();
     auto issue = [&](const int st) __attribute__((always_inline)) {
-        if (wave < 8) {
-            dma16_sv(iq, qgo, lds_addr(&g_rq[0][0]) + st * TSZ + 1024 * wave);
-            if (ip0 + kT <= p.N) {
-                dma16_sv(io, ogo, lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * wave);
-            } else {
-                const int slot = 64 * wave + lane;
-                const int r = slot / CPR, ps = slot % CPR;
-                const int rr = min(r, p.N - 1 - ip0);
-                dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * wave);
+        if (wave < 4) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int win = 2 * wave + jj;
+                dma16_sv(iq, qgo[jj], lds_addr(&g_rq[0][0]) + st * TSZ + 1024 * win);
+                if (ip0 + kT <= p.N) {
+                    dma16_sv(io, ogo[jj], lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * win);
+                } else {
+                    const int slot = 64 * win + lane;
+                    const int r = slot / CPR, ps = slot % CPR;
+                    const int rr = min(r, p.N - 1 - ip0);
+                    dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * win);
+                }
             }
-        } else if (lane < 4) {
-            dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(&g_rs[0][0]) + st * 256 + 64 * (wave & 3));
+        } else if (wave < 6 && lane < 8) {
+            dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(&g_rs[0][0]) + st * 256 + 128 * (wave - 4));
         }
         if (++ih == p.G) {
             ih = 0;
@@ -781,13 +787,14 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
         for (int t = 0; t <= nsteps; ++t) {
             if (t > 0) {
                 // Step t lands (issued three iterations earlier or in the prologue); steps t + 1
-                // and t + 2 may stay in flight.  Per step a wave issues 2 copies (waves 0..7) or 1.
+                // and t + 2 may stay in flight.  Per step a wave issues 4 copies (waves 0..3),
+                // 1 (waves 4, 5) or none.
                 const int later = nsteps - 1 - t;
                 if (later >= 2) {
-                    if (wave < 8) wait_vmcnt<4>();
+                    if (wave < 4) wait_vmcnt<8>();
                     else wait_vmcnt<2>();
                 } else if (later == 1) {
-                    if (wave < 8) wait_vmcnt<2>();
+                    if (wave < 4) wait_vmcnt<4>();
                     else wait_vmcnt<1>();
                 } else {
                     wait_vmcnt<0>();
