@@ -732,8 +732,8 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
     const int troff = tr_read_off<D>(lane, 0), troff_hi = tr_read_off<D>(lane, 1);
     char* const xw = reinterpret_cast<char*>(&g_rx[0][kg][0]) + 16 * lane;   // + parity * 16 KB + e4 * 1 KB
 
-    // Prologue: the key fragments and steps 0..2 in flight, all drained before the walk.
-    for (int t = 0; t < 3 && t < nsteps; ++t) issue(t);
+    // Prologue: the key fragments and steps 0, 1 in flight, all drained before the walk.
+    for (int t = 0; t < 2 && t < nsteps; ++t) issue(t);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
     __syncthreads();
@@ -769,31 +769,34 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
         }
     };
 
-    // Walk: iteration t handles step t (role 0; role 1 its dP) and step t - 1 (role 1's dS, dK).
+    // Walk: iteration t handles step t (role 0), the dP of step t - 1 and the dS, dK of step
+    // t - 2 (role 1).  Role 1 reads P of step t - 1 at the end of iteration t, after its
+    // MFMAs, so the LDS latency of the hand-over is hidden behind the barrier; it carries
+    // that P and its dP into iteration t + 1.
     auto walk = [&](auto role_c) __attribute__((always_inline)) {
         constexpr int R = decltype(role_c)::value;
         int cti = 0, ch = 0;             // position tile / head of step t
         uint32_t vis = 0;
-        bool any = false, all = false, any_prev = false;
+        bool any = false, all = false;   // of step t
+        bool any_p = false, any_pp = false;   // of steps t - 1 and t - 2
         int vis_tile = -1;
-        int st_c = 0, st_p = 0;          // ring stages of steps t and t - 1
-        int st_i = 3;                    // stage of the next issue (step t + 3)
-        f32x16_t dp;                     // role 1: dP - D of step t - 1
+        int st_c = 0, st_p = 0, st_pp = 0;    // ring stages of steps t, t - 1, t - 2
+        int st_i = 2;                    // stage of the next issue (step t + 2)
+        f32x16_t dp;                     // role 1: dP - D of step t - 2 (at the top of iteration t)
+        f32x4_t xr[4];                   // role 1: P of step t - 2
         if constexpr (R == 1) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) xr[e4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         auto nxt = [](int st) { return st + 1 == kStagesR ? 0 : st + 1; };
-        for (int t = 0; t <= nsteps; ++t) {
+        for (int t = 0; t <= nsteps + 1; ++t) {
             if (t > 0) {
-                // Step t lands (issued three iterations earlier or in the prologue); steps t + 1
-                // and t + 2 may stay in flight.  Per step a wave issues 4 copies (waves 0..3),
-                // 1 (waves 4, 5) or none.
-                const int later = nsteps - 1 - t;
-                if (later >= 2) {
-                    if (wave < 4) wait_vmcnt<8>();
-                    else wait_vmcnt<2>();
-                } else if (later == 1) {
+                // Step t lands (issued two iterations earlier or in the prologue); step t + 1
+                // may stay in flight.  Per step a wave issues 4 copies (waves 0..3), 1 (waves
+                // 4, 5) or none.
+                if (t + 1 < nsteps) {
                     if (wave < 4) wait_vmcnt<4>();
                     else wait_vmcnt<1>();
                 } else {
@@ -801,12 +804,13 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
                 }
                 __syncthreads();
             }
-            // Step t + 3 into the stage step t - 2 used.
-            if (t + 3 < nsteps) {
+            // Step t + 2 into the stage step t - 3 used.
+            if (t + 2 < nsteps) {
                 issue(st_i);
                 st_i = nxt(st_i);
             }
-            any_prev = any;
+            any_pp = any_p;
+            any_p = any;
             if (t < nsteps) {
                 if (cti != vis_tile) {
                     const int p0 = pos_tile(cti) * kT;
@@ -818,13 +822,12 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
             } else {
                 any = false;
             }
-            char* const xc = xw + (t & 1) * (kGroupsR * 16 * 64 * 4);          // exchange buffer of step t
-            char* const xp = xw + ((t & 1) ^ 1) * (kGroupsR * 16 * 64 * 4);    // and of step t - 1
-            const char* const qt_c = reinterpret_cast<const char*>(&g_rq[0][0]) + st_c * TSZ;
-            const char* const ot_c = reinterpret_cast<const char*>(&g_ro[0][0]) + st_c * TSZ;
-            const char* const sp_c = reinterpret_cast<const char*>(&g_rs[0][0]) + st_c * 256;
             if constexpr (R == 0) {
                 if (any) {
+                    char* const xc = xw + (t & 1) * (kGroupsR * 16 * 64 * 4);   // exchange buffer of step t
+                    const char* const qt_c = reinterpret_cast<const char*>(&g_rq[0][0]) + st_c * TSZ;
+                    const char* const ot_c = reinterpret_cast<const char*>(&g_ro[0][0]) + st_c * TSZ;
+                    const char* const sp_c = reinterpret_cast<const char*>(&g_rs[0][0]) + st_c * 256;
                     f32x16_t sa;
                     row_product(qt_c, sp_c, sa);
                     if (!all) apply_mask(sa, vis, g2);
@@ -840,24 +843,31 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
                     col_product(ot_c, pb);
                 }
             } else {
-                if (any_prev) {
-                    const char* const qt_p = reinterpret_cast<const char*>(&g_rq[0][0]) + st_p * TSZ;
+                if (any_pp) {
+                    const char* const qt_pp = reinterpret_cast<const char*>(&g_rq[0][0]) + st_pp * TSZ;
 #pragma unroll
                     for (int e4 = 0; e4 < 4; ++e4) {
-                        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(xp + 1024 * e4);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) dp[4 * e4 + i] *= y[i];      // dS
+                        for (int i = 0; i < 4; ++i) dp[4 * e4 + i] *= xr[e4][i];      // dS
                     }
                     bf16x8_t sb[2];
                     pack_b(dp, sb);
-                    col_product(qt_p, sb);
+                    col_product(qt_pp, sb);
                 }
-                if (any) row_product(ot_c, sp_c + 128, dp);
+                if (any_p) {
+                    const char* const ot_p = reinterpret_cast<const char*>(&g_ro[0][0]) + st_p * TSZ;
+                    const char* const sp_p = reinterpret_cast<const char*>(&g_rs[0][0]) + st_p * 256;
+                    row_product(ot_p, sp_p + 128, dp);
+                    const char* const xp = xw + ((t & 1) ^ 1) * (kGroupsR * 16 * 64 * 4);   // of step t - 1
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) xr[e4] = *reinterpret_cast<const f32x4_t*>(xp + 1024 * e4);
+                }
             }
             if (++ch == p.G) {
                 ch = 0;
                 ++cti;
             }
+            st_pp = st_p;
             st_p = st_c;
             st_c = nxt(st_c);
         }
