@@ -188,8 +188,9 @@ int mars_attn_bwd_workspace_bytes(const mars_attn_desc* desc, size_t* bytes);
  * dq, dk, dv: outputs (bf16, rounded to nearest even), fully overwritten; they must not
  *   alias any input or each other.
  * ws: device workspace of at least mars_attn_bwd_workspace_bytes, 16-byte aligned; no
- *   initialisation needed (it holds Q * scale * log2(e) in bf16 and two fp32 scalars per
- *   row); MARS_EWORKSPACE if null or too small.
+ *   initialisation needed (it holds Q * scale * log2(e) in bf16, two fp32 scalars per row,
+ *   the dK/dV arrival counters, which the call zeroes itself, and the fp32 partial sums of
+ *   key blocks whose walk is split); MARS_EWORKSPACE if null or too small.
  * Errors as mars_attn_fwd; key position strides (k, v) <= 2^25 elements and the d_o
  *   position stride <= 2^25 elements, else MARS_EUNSUPPORTED.
  */
