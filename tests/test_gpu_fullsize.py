@@ -5,7 +5,8 @@ bench times (MARS §3.2 Eq. 2: the mask whose tiles the kernel skips).
 * every row of two whole KV groups (14 of the 28 query heads) of the long layout;
 * the kernel's visited-tile log, bit for bit, on the three layouts and on one layout whose
   rows see more than 32768 keys (more than 1024 key tiles per walk);
-* every dQ row and every dK/dV key of one (batch, KV group) of the 0.5B layout's backward.
+* every dQ row and every dK/dV key of one (batch, KV group) of the 0.5B and the 7B layouts'
+  backward.
 
 The oracle runs one (batch, head) slice per thread (tests/gpu_helpers.py).
 """
@@ -107,12 +108,7 @@ def test_tilelog_beyond_1024_key_tiles():
     _tilelog_case(1, 2, 1, 64, P, L, B, seed=4242, rows_check=rows)
 
 
-@pytest.mark.timeout(600)
-def test_bwd_whole_pair_qwen05b():
-    """Every dQ row (7 heads) and every dK/dV key of batch 7, KV group 1 of the 0.5B layout's
-    backward, from one launch over the whole workload."""
-    s = I.QWEN05B
-    bsel, g = 7, 1
+def _bwd_whole_pair(s, bsel, g):
     G = s.hq // s.hkv
     hs = slice(g * G, (g + 1) * G)
     print(f"case bwd whole pair {s.name} b={bsel} g={g}", flush=True)
@@ -136,3 +132,18 @@ def test_bwd_whole_pair_qwen05b():
         check_bounded(to_np64(got), ref, bnd, f"{s.name} {name} b{bsel} g{g} whole")
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
+
+
+@pytest.mark.timeout(600)
+def test_bwd_whole_pair_qwen05b():
+    """Every dQ row (7 heads) and every dK/dV key of batch 7, KV group 1 of the 0.5B layout's
+    backward, from one launch over the whole workload."""
+    _bwd_whole_pair(I.QWEN05B, 7, 1)
+
+
+@pytest.mark.timeout(600)
+def test_bwd_whole_pair_qwen7b():
+    """Every dQ row (7 heads) and every dK/dV key of batch 1, KV group 2 of the 7B layout's
+    backward (head_dim 128: 192-key blocks, walks split into chunks whose partials are
+    summed by the last arrival), from one launch over the whole workload."""
+    _bwd_whole_pair(I.QWEN7B, 1, 2)
