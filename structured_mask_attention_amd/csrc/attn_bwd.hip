@@ -47,8 +47,8 @@ constexpr int kKeysPerWG = kWavesB * kT;   // dK/dV at head_dim 64: 128 keys per
 constexpr int kRowsPerWGB = kWavesB * kT;  // dQ: 128 packed rows per workgroup
 constexpr int kChunkMax = 8;               // dK/dV: a key block's walk splits into at most 8 chunks
 constexpr int kChunkMinTiles = 4;          //        of at least 4 position tiles each
-constexpr int kNominalSlots64 = 512;       // resident dK/dV workgroups the chunk size aims at
-constexpr int kNominalSlots128 = 256;      // (256 CUs x 2 or 1 per CU, by head_dim)
+constexpr int kNominalSlots64 = 512;       // workgroup slots the dK/dV chunk size aims at: 2 per CU at
+constexpr int kNominalSlots128 = 256;      // head_dim 64 (3 fit; 768 measured the same), 1 at head_dim 128
 
 // ---------------------------------------------------------------------------------------
 // LDS rings.  One file-scope object per stage, array and head_dim.
