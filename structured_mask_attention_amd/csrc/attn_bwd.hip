@@ -602,11 +602,11 @@ constexpr int kGroupsR = 6;                  // 32-key groups per workgroup
 constexpr int kWavesR = 2 * kGroupsR;
 constexpr int kThreadsR = 64 * kWavesR;
 constexpr int kKeysPerWGR = kGroupsR * kT;   // 192
-constexpr int kStagesR = 5;
+constexpr int kStagesR = 6;
 __shared__ __attribute__((aligned(16))) uint16_t g_rq[kStagesR][kT * 128];   // Qc tiles
 __shared__ __attribute__((aligned(16))) uint16_t g_ro[kStagesR][kT * 128];   // dO tiles
 __shared__ __attribute__((aligned(16))) float g_rs[kStagesR][64];            // [-LSE2 x 32][-D x 32]
-__shared__ __attribute__((aligned(16))) float g_rx[2][kGroupsR][16 * 64];    // P: [parity][key group][element][lane]
+__shared__ __attribute__((aligned(16))) uint16_t g_rx[2][2][kGroupsR][16 * 64];   // bf16 P: [parity][step][key group][half][lane]
 
 __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvParams p) {
     constexpr int D = 128;
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
     }
     const int roff = row_read_off<D>(hl, g2, swz_kv<D>(hl));
     const int troff = tr_read_off<D>(lane, 0), troff_hi = tr_read_off<D>(lane, 1);
-    char* const xw = reinterpret_cast<char*>(&g_rx[0][kg][0]) + 16 * lane;   // + parity * 16 KB + e4 * 1 KB
+    char* const xw = reinterpret_cast<char*>(&g_rx[0][0][kg][0]) + 16 * lane;   // + (2 parity + step) * 12 KB + half * 1 KB
 
     // Prologue: the key fragments and steps 0, 1 in flight, all drained before the walk.
     for (int t = 0; t < 2 && t < nsteps; ++t) issue(t);
@@ -769,107 +769,103 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
         }
     };
 
-    // Walk: iteration t handles step t (role 0), the dP of step t - 1 and the dS, dK of step
-    // t - 2 (role 1).  Role 1 reads P of step t - 1 at the end of iteration t, after its
-    // MFMAs, so the LDS latency of the hand-over is hidden behind the barrier; it carries
-    // that P and its dP into iteration t + 1.
+    // Walk, two steps per iteration: iteration t handles steps 2t and 2t + 1 on role 0 and
+    // steps 2t - 2 and 2t - 1 on role 1, which reads their P (bf16, as the dV MFMAs use it)
+    // from the exchange buffers role 0 filled in iteration t - 1.  Copies: steps 2t + 2 and
+    // 2t + 3 go into the stages of steps 2t - 4 and 2t - 3 (ring of 6: steps 2t - 2 ... 2t + 3).
+    constexpr int XSTEP = kGroupsR * 2 * 1024;   // bytes between the (parity, step) buffers
     auto walk = [&](auto role_c) __attribute__((always_inline)) {
         constexpr int R = decltype(role_c)::value;
-        int cti = 0, ch = 0;             // position tile / head of step t
+        int cti = 0, ch = 0;             // position tile / head of this role's next step
         uint32_t vis = 0;
-        bool any = false, all = false;   // of step t
-        bool any_p = false, any_pp = false;   // of steps t - 1 and t - 2
+        bool any = false, all = false;
         int vis_tile = -1;
-        int st_c = 0, st_p = 0, st_pp = 0;    // ring stages of steps t, t - 1, t - 2
-        int st_i = 2;                    // stage of the next issue (step t + 2)
-        f32x16_t dp;                     // role 1: dP - D of step t - 2 (at the top of iteration t)
-        f32x4_t xr[4];                   // role 1: P of step t - 2
-        if constexpr (R == 1) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) dp[e] = 0.f;
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) xr[e4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        auto nxt = [](int st) { return st + 1 == kStagesR ? 0 : st + 1; };
-        for (int t = 0; t <= nsteps + 1; ++t) {
-            if (t > 0) {
-                // Step t lands (issued two iterations earlier or in the prologue); step t + 1
-                // may stay in flight.  Per step a wave issues 4 copies (waves 0..3), 1 (waves
-                // 4, 5) or none.
-                if (t + 1 < nsteps) {
-                    if (wave < 4) wait_vmcnt<4>();
-                    else wait_vmcnt<1>();
-                } else {
-                    wait_vmcnt<0>();
-                }
-                __syncthreads();
-            }
-            // Step t + 2 into the stage step t - 3 used.
-            if (t + 2 < nsteps) {
-                issue(st_i);
-                st_i = nxt(st_i);
-            }
-            any_pp = any_p;
-            any_p = any;
-            if (t < nsteps) {
-                if (cti != vis_tile) {
-                    const int p0 = pos_tile(cti) * kT;
-                    vis = span_bits(a1, b1, p0) | span_bits(a2, b2, p0);
-                    any = __builtin_amdgcn_ballot_w64(kvalid && vis != 0u) != 0ull;
-                    all = __builtin_amdgcn_ballot_w64(kvalid && vis != 0xffffffffu) == 0ull;
-                    vis_tile = cti;
-                }
-            } else {
-                any = false;
-            }
-            if constexpr (R == 0) {
-                if (any) {
-                    char* const xc = xw + (t & 1) * (kGroupsR * 16 * 64 * 4);   // exchange buffer of step t
-                    const char* const qt_c = reinterpret_cast<const char*>(&g_rq[0][0]) + st_c * TSZ;
-                    const char* const ot_c = reinterpret_cast<const char*>(&g_ro[0][0]) + st_c * TSZ;
-                    const char* const sp_c = reinterpret_cast<const char*>(&g_rs[0][0]) + st_c * 256;
-                    f32x16_t sa;
-                    row_product(qt_c, sp_c, sa);
-                    if (!all) apply_mask(sa, vis, g2);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) sa[e] = __builtin_amdgcn_exp2f(sa[e]);   // P
-#pragma unroll
-                    for (int e4 = 0; e4 < 4; ++e4) {
-                        const f32x4_t y = {sa[4 * e4], sa[4 * e4 + 1], sa[4 * e4 + 2], sa[4 * e4 + 3]};
-                        *reinterpret_cast<f32x4_t*>(xc + 1024 * e4) = y;
-                    }
-                    bf16x8_t pb[2];
-                    pack_b(sa, pb);
-                    col_product(ot_c, pb);
-                }
-            } else {
-                if (any_pp) {
-                    const char* const qt_pp = reinterpret_cast<const char*>(&g_rq[0][0]) + st_pp * TSZ;
-#pragma unroll
-                    for (int e4 = 0; e4 < 4; ++e4) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) dp[4 * e4 + i] *= xr[e4][i];      // dS
-                    }
-                    bf16x8_t sb[2];
-                    pack_b(dp, sb);
-                    col_product(qt_pp, sb);
-                }
-                if (any_p) {
-                    const char* const ot_p = reinterpret_cast<const char*>(&g_ro[0][0]) + st_p * TSZ;
-                    const char* const sp_p = reinterpret_cast<const char*>(&g_rs[0][0]) + st_p * 256;
-                    row_product(ot_p, sp_p + 128, dp);
-                    const char* const xp = xw + ((t & 1) ^ 1) * (kGroupsR * 16 * 64 * 4);   // of step t - 1
-#pragma unroll
-                    for (int e4 = 0; e4 < 4; ++e4) xr[e4] = *reinterpret_cast<const f32x4_t*>(xp + 1024 * e4);
-                }
+        int st = 0;                      // ring stage of this role's next step
+        int st_i = 2;                    // stage of the next issue (step 2t + 2)
+        auto nxt = [](int x) { return x + 1 == kStagesR ? 0 : x + 1; };
+        // Classify this role's next step, then advance the counters past it.
+        auto classify = [&]() __attribute__((always_inline)) {
+            if (cti != vis_tile) {
+                const int p0 = pos_tile(cti) * kT;
+                vis = span_bits(a1, b1, p0) | span_bits(a2, b2, p0);
+                any = __builtin_amdgcn_ballot_w64(kvalid && vis != 0u) != 0ull;
+                all = __builtin_amdgcn_ballot_w64(kvalid && vis != 0xffffffffu) == 0ull;
+                vis_tile = cti;
             }
             if (++ch == p.G) {
                 ch = 0;
                 ++cti;
             }
-            st_pp = st_p;
-            st_p = st_c;
-            st_c = nxt(st_c);
+        };
+        const int npairs = (nsteps + 1) / 2;
+        for (int t = 0; t <= npairs; ++t) {
+            if (t > 0) {
+                // Steps 2t and 2t + 1 land (issued at the start of iteration t - 1).
+                wait_vmcnt<0>();
+                __syncthreads();
+            }
+            if (2 * t + 2 < nsteps) {
+                issue(st_i);
+                st_i = nxt(st_i);
+            }
+            if (2 * t + 3 < nsteps) {
+                issue(st_i);
+                st_i = nxt(st_i);
+            }
+            if constexpr (R == 0) {
+#pragma unroll
+                for (int jx = 0; jx < 2; ++jx) {
+                    if (2 * t + jx < nsteps) {
+                        classify();
+                        if (any) {
+                            const char* const qt = reinterpret_cast<const char*>(&g_rq[0][0]) + st * TSZ;
+                            const char* const ot = reinterpret_cast<const char*>(&g_ro[0][0]) + st * TSZ;
+                            const char* const sp = reinterpret_cast<const char*>(&g_rs[0][0]) + st * 256;
+                            f32x16_t sa;
+                            row_product(qt, sp, sa);
+                            if (!all) apply_mask(sa, vis, g2);
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) sa[e] = __builtin_amdgcn_exp2f(sa[e]);   // P
+                            bf16x8_t pb[2];
+                            pack_b(sa, pb);
+                            char* const xc = xw + (2 * (t & 1) + jx) * XSTEP;
+                            *reinterpret_cast<bf16x8_t*>(xc) = pb[0];
+                            *reinterpret_cast<bf16x8_t*>(xc + 1024) = pb[1];
+                            col_product(ot, pb);
+                        }
+                        st = nxt(st);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int jx = 0; jx < 2; ++jx) {
+                    const int s = 2 * t - 2 + jx;
+                    if (t > 0 && s < nsteps) {
+                        classify();
+                        if (any) {
+                            const char* const qt = reinterpret_cast<const char*>(&g_rq[0][0]) + st * TSZ;
+                            const char* const ot = reinterpret_cast<const char*>(&g_ro[0][0]) + st * TSZ;
+                            const char* const sp = reinterpret_cast<const char*>(&g_rs[0][0]) + st * 256;
+                            const char* const xp = xw + (2 * ((t - 1) & 1) + jx) * XSTEP;
+                            const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(xp);
+                            const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(xp + 1024);
+                            f32x16_t dp;
+                            row_product(ot, sp + 128, dp);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {   // dS = P (dP - D), P as the bf16 pairs role 0 packed
+                                dp[2 * i] *= __uint_as_float(x0[i] << 16);
+                                dp[2 * i + 1] *= __uint_as_float(x0[i] & 0xffff0000u);
+                                dp[8 + 2 * i] *= __uint_as_float(x1[i] << 16);
+                                dp[8 + 2 * i + 1] *= __uint_as_float(x1[i] & 0xffff0000u);
+                            }
+                            bf16x8_t sb[2];
+                            pack_b(dp, sb);
+                            col_product(qt, sb);
+                        }
+                        st = nxt(st);
+                    }
+                }
+            }
         }
     };
     if (role == 0) walk(std::integral_constant<int, 0>{});

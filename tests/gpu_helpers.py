@@ -104,7 +104,8 @@ def bwd_bounds(q, k, v, do, o_in, lse_err, P, L, B, rows=None, keys=None, scale=
         most u*c*sum_d |q_id||k_jd| (log2 units), so P_ij by a relative 2^(u c m_i) - 1 with
         m_i the max over keys; the LSE input adds e^lse_err - 1;
       * D_i = sum dO.O from the given O: |dD_i| <= sum_d |dO_id||O_in - O_exact|_id;
-      * P (for dV) and dS (for dQ, dK) are rounded to bf16 (u each), Q*c as well (dK);
+      * P (for dV) and dS (for dQ, dK) are rounded to bf16 (u each), Q*c as well (dK); at
+        head_dim 128 the dK side forms dS from the bf16 P the dV side uses (one more u on dS);
       * fp32 accumulation over n terms: n*2^-24 of the sum of absolute terms;
       * the bf16 output rounding: u |grad|.
     Returns (bq [b,R,Hq,D], bk [b,K,Hkv,D], bv [b,K,Hkv,D]) for rows / keys (all by default).
@@ -153,7 +154,8 @@ def bwd_bounds(q, k, v, do, o_in, lse_err, P, L, B, rows=None, keys=None, scale=
                     bq[bi, :, h] = scale * (dds @ np.abs(k[bi, :, g])) * (1 + gam) \
                         + gam * scale * (np.abs(ds) @ np.abs(k[bi, :, g])) + u * np.abs(dq) + 1e-6
                 else:
-                    pk, dsk, ddsk = p[:, keys], ds[:, keys], dds[:, keys]
+                    ddk = dds + (u * (1 + rel) * p * (np.abs(x) + eD) if D == 128 else 0.0)
+                    pk, dsk, ddsk = p[:, keys], ds[:, keys], ddk[:, keys]
                     relv = rel + u * (1 + rel)
                     bv[bi, :, g] += (pk * relv).T @ np.abs(dO) + gam * (pk.T @ np.abs(dO))
                     bk[bi, :, g] += scale * ((ddsk + u * np.abs(dsk)).T @ np.abs(qa)) \
