@@ -15,8 +15,9 @@
 //     keys, its partner lane (l ^ 32) the other 16, so row max/sum need one permlane32 swap.
 //   * O^T += V^T P^T: P^T comes straight from the score registers (bf16, RNE); V^T is read
 //     from the natural [key][d] LDS tile with ds_read_b64_tr_b16 (transposing 16-bit read).
-//   * K/V tiles reach LDS by global_load_lds_dwordx4 into a 3-stage ring (two tiles in
-//     flight); 16-byte chunks are XOR-swizzled per row so operand reads are conflict-free.
+//   * K/V tiles reach LDS by global_load_lds_dwordx4 into a ring: 3 stages with one tile per
+//     barrier at head_dim 128, 4 stages with two tiles per barrier at head_dim 64; 16-byte
+//     chunks are XOR-swizzled per row so operand reads are conflict-free.
 //   * Keys are walked in 32-key tiles over at most two intervals per workgroup (the union
 //     of its rows' visible keys, see mars_device.h); each wave classifies every tile for its
 //     own rows: skipped, computed with the element mask, or computed without it.
@@ -73,9 +74,10 @@ struct AttnKParams {
 };
 
 
-// K/V ring: 3 stages, one file-scope __shared__ object per stage, tensor and head_dim, so
-// every access names its array directly (no generic pointers to LDS).
-constexpr int kStages = 3;
+// K/V ring: 3 stages at head_dim 128, 4 at head_dim 64 (two tiles per barrier); one
+// file-scope __shared__ object per stage, tensor and head_dim, so every access names its
+// array directly (no generic pointers to LDS).
+template <int D> constexpr int fwd_stages() { return D == 64 ? 4 : 3; }
 __shared__ __attribute__((aligned(16))) uint16_t g_ak0_128[kKT * 128];
 __shared__ __attribute__((aligned(16))) uint16_t g_ak1_128[kKT * 128];
 __shared__ __attribute__((aligned(16))) uint16_t g_ak2_128[kKT * 128];
@@ -88,6 +90,8 @@ __shared__ __attribute__((aligned(16))) uint16_t g_ak2_64[kKT * 64];
 __shared__ __attribute__((aligned(16))) uint16_t g_av0_64[kKT * 64];
 __shared__ __attribute__((aligned(16))) uint16_t g_av1_64[kKT * 64];
 __shared__ __attribute__((aligned(16))) uint16_t g_av2_64[kKT * 64];
+__shared__ __attribute__((aligned(16))) uint16_t g_ak3_64[kKT * 64];
+__shared__ __attribute__((aligned(16))) uint16_t g_av3_64[kKT * 64];
 
 template <int D, int ST>
 __device__ inline uint16_t* att_k() {
@@ -98,7 +102,8 @@ __device__ inline uint16_t* att_k() {
     } else {
         if constexpr (ST == 0) return g_ak0_64;
         else if constexpr (ST == 1) return g_ak1_64;
-        else return g_ak2_64;
+        else if constexpr (ST == 2) return g_ak2_64;
+        else return g_ak3_64;
     }
 }
 template <int D, int ST>
@@ -110,7 +115,8 @@ __device__ inline uint16_t* att_v() {
     } else {
         if constexpr (ST == 0) return g_av0_64;
         else if constexpr (ST == 1) return g_av1_64;
-        else return g_av2_64;
+        else if constexpr (ST == 2) return g_av2_64;
+        else return g_av3_64;
     }
 }
 
@@ -119,6 +125,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 3) void attn_fwd_bf16_kerne
     constexpr int NC = D / 16;          // 16-wide d chunks of the QK^T contraction
     constexpr int NDB = D / 32;         // 32-row d blocks of O^T
     constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+    constexpr int kStages = fwd_stages<D>();
     constexpr int NINS = kKT * CPR / 64;            // 1 KB copy windows per tile and tensor
     constexpr int PERW = NINS / kWaves;             // windows per wave and tensor
     constexpr int GROUPW = 2 * PERW;                // copy instructions per wave and tile
@@ -366,14 +373,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 3) void attn_fwd_bf16_kerne
         if (it < ntiles) cls_bits |= (uint32_t)tile_class(it) << (2 * j);
     }
 
-    auto body = [&](const int it, auto stage) __attribute__((always_inline)) {
+    // The computation of tile `it` from ring stage ST (its copy has landed).
+    auto tile_body = [&](const int it, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        // Tile `it` is this wave's oldest copy group in flight; once every wave has it, the
-        // barrier also guarantees that the stage read in iteration it-1 is free for tile it+2.
-        if (it + 1 < ntiles) wait_vmcnt<GROUPW>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        if (it + 2 < ntiles) issue(std::integral_constant<int, (ST + 2) % kStages>{});
 
         const int kt = tile_of(it);
         const int kb = kt * kKT;
@@ -562,10 +564,39 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 3) void attn_fwd_bf16_kerne
         }
     };
 
-    for (int t0 = 0; t0 < ntiles; t0 += kStages) {
-        body(t0, S0{});
-        if (t0 + 1 < ntiles) body(t0 + 1, S1{});
-        if (t0 + 2 < ntiles) body(t0 + 2, S2{});
+    if constexpr (D == 128) {
+        // One tile per barrier: tile `it` is the oldest copy group in flight; once every wave
+        // has it, the barrier also guarantees that the stage read for tile it-1 is free for
+        // tile it+2.
+        auto body = [&](const int it, auto stage) __attribute__((always_inline)) {
+            constexpr int ST = decltype(stage)::value;
+            if (it + 1 < ntiles) wait_vmcnt<GROUPW>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (it + 2 < ntiles) issue(std::integral_constant<int, (ST + 2) % kStages>{});
+            tile_body(it, stage);
+        };
+        for (int t0 = 0; t0 < ntiles; t0 += kStages) {
+            body(t0, S0{});
+            if (t0 + 1 < ntiles) body(t0 + 1, S1{});
+            if (t0 + 2 < ntiles) body(t0 + 2, S2{});
+        }
+    } else {
+        // Two tiles per barrier: tiles it and it+1 landed (issued before the previous
+        // barrier); tiles it+2 and it+3 go into the stages tiles it-2 and it-1 used.
+        auto body2 = [&](const int it, auto stage) __attribute__((always_inline)) {
+            constexpr int ST = decltype(stage)::value;
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (it + 2 < ntiles) issue(std::integral_constant<int, (ST + 2) % kStages>{});
+            if (it + 3 < ntiles) issue(std::integral_constant<int, (ST + 3) % kStages>{});
+            tile_body(it, stage);
+            if (it + 1 < ntiles) tile_body(it + 1, std::integral_constant<int, ST + 1>{});
+        };
+        for (int t0 = 0; t0 < ntiles; t0 += kStages) {
+            body2(t0, S0{});
+            if (t0 + 2 < ntiles) body2(t0 + 2, S2{});
+        }
     }
 
     // Epilogue: O = acc / l (bf16, RNE); LSE = (m + log2 l) ln 2.
