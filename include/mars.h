@@ -188,11 +188,11 @@ int mars_attn_bwd_workspace_bytes(const mars_attn_desc* desc, size_t* bytes);
  * dq, dk, dv: outputs (bf16, rounded to nearest even), fully overwritten; they must not
  *   alias any input or each other.
  * ws: device workspace of at least mars_attn_bwd_workspace_bytes, 16-byte aligned; no
- *   initialisation needed (it holds Q * scale * log2(e) in bf16, two fp32 scalars per row,
- *   the dK/dV arrival counters, which the call zeroes itself, and the fp32 partial sums of
- *   key blocks whose walk is split); MARS_EWORKSPACE if null or too small.
- * Errors as mars_attn_fwd; key position strides (k, v) <= 2^25 elements and the d_o
- *   position stride <= 2^25 elements, else MARS_EUNSUPPORTED.
+ *   initialisation needed (it holds two fp32 scalars per row, the dK/dV arrival counters,
+ *   which the call zeroes itself, and the fp32 partial sums of key blocks whose walk is
+ *   split); MARS_EWORKSPACE if null or too small.
+ * Errors as mars_attn_fwd; key position strides (k, v) <= 2^25 elements and the q and d_o
+ *   position strides <= 2^25 elements, else MARS_EUNSUPPORTED.
  */
 int mars_attn_bwd(const mars_attn_desc* desc, const mars_attn_bwd_strides* gs, const void* q,
                   const void* k, const void* v, const void* o, const float* lse, const void* d_o,

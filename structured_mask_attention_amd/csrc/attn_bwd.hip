@@ -7,18 +7,20 @@
 // of the forward (scores s = c q.k, c = scale*log2(e); P = 2^(s - LSE*log2(e))):
 //   dV = P^T dO,   dS = P o (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q,
 // dK and dV of a KV head summed over its G query heads.  Three kernels:
-//   1. prep (per row): Qc = bf16(Q*c) exactly as the forward rounds it, -D and
-//      -LSE*log2(e), into the workspace, positions padded to a multiple of 32 (zeros);
+//   1. prep (per row): -D and -LSE*log2(e) into the workspace, positions padded to a
+//      multiple of 32 (zeros);
 //   2. dK/dV (key-stationary): a workgroup owns a block of keys of one (batch, kv head) and
 //      walks the (32-position, head) tiles of every row that sees one of its keys (a union
-//      of at most three position intervals).  Qc and dO tiles plus the two per-row scalars
-//      stream through an LDS ring (global_load_lds_dwordx4, XOR-swizzled chunks).  Per
-//      tile and 32-key group: S = Qc K^T and dP = dO V^T (MFMA accumulators start at -LSE2
-//      and -D), P = 2^S, dS = P dP, then dV^T += dO^T P and dK^T += Qc^T dS with the
-//      transposed operands read by ds_read_b64_tr_b16.  Head_dim 64: 128 keys, one wave
-//      per 32 keys with K and V fragments in registers, a 3-stage ring.  Head_dim 128: 192
-//      keys, two waves per 32 keys split by role (K, S, P, dV on one; V, dP, dS, dK on the
-//      other, P handed over through LDS), three waves per SIMD, a 5-stage ring.  The
+//      of at most three position intervals).  Q and dO tiles plus the two per-row scalars
+//      stream through an LDS ring (global_load_lds_dwordx4, XOR-swizzled chunks).  The
+//      key-stationary side carries the score scale: its K fragments are Kc = bf16(K*c),
+//      rounded once per workgroup.  Per tile and 32-key group: S = Q Kc^T and dP = dO V^T
+//      (MFMA accumulators start at -LSE2 and -D), P = 2^S, dS = P dP, then dV^T += dO^T P
+//      and dK^T += Q^T dS (dK takes the scale at the end) with the transposed operands read
+//      by ds_read_b64_tr_b16.  Head_dim 64: 128 keys, one wave per 32 keys with K and V
+//      fragments in registers, a 3-stage ring.  Head_dim 128: 192 keys, two waves per 32
+//      keys split by role (K, S, P, dV on one; V, dP, dS, dK on the other, P handed over
+//      through LDS), three waves per SIMD, two steps per barrier over a 6-stage ring.  The
 //      element mask is a per-key bitmask over the tile's 32 positions.  A heavy key block
 //      (prompt keys are seen by every row) splits its walk
 //      into up to 8 chunks on separate workgroups (chunk size from the layout's total work);
@@ -26,7 +28,8 @@
 //      whichever wave arrives last for a 32-key slice and gradient (one counter each), so
 //      the result does not depend on the arrival order.
 //   3. dQ (row-stationary): the forward's row packing, tile walk, tile classes and K/V
-//      ring; per tile S^T = K Qc^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+//      ring; each lane rounds its row's Qc = bf16(Q*c) in registers exactly as the forward
+//      does; per tile S^T = K Qc^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 // P and dS enter the MFMAs as bf16 (round to nearest even); statistics and accumulation
 // are fp32; gradients are stored as bf16.
 #include <cmath>
@@ -52,7 +55,7 @@ constexpr int kNominalSlots128 = 256;      // head_dim 64 (3 fit; 768 measured t
 
 // ---------------------------------------------------------------------------------------
 // LDS rings.  One file-scope object per stage, array and head_dim.
-//   dK/dV: Qc tile, dO tile ([32 positions][D] bf16 each) and the scalars of the tile's
+//   dK/dV: Q tile, dO tile ([32 positions][D] bf16 each) and the scalars of the tile's
 //          rows ([-LSE2 x 32][-D x 32] fp32).
 //   dQ:    K tile and V tile ([32 keys][D] bf16 each).
 // ---------------------------------------------------------------------------------------
@@ -201,6 +204,15 @@ __host__ __device__ inline int kblock_tile_ranges(int kb0, int kb1, int P, int L
     return nm;
 }
 
+// bf16(x * c) of eight bf16 values: fp32 product, then round to nearest even.
+__device__ inline bf16x8_t scale_bf16x8(bf16x8_t x, float c) {
+    const u32x4_t w = __builtin_bit_cast(u32x4_t, x);
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(__uint_as_float(w[i] << 16) * c, __uint_as_float(w[i] & 0xffff0000u) * c);
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
 // Chunks of a key block's walk of npt position tiles, at most tc tiles per chunk.
 __host__ __device__ inline int walk_chunks(int npt, int tc) {
     const int c = (npt + tc - 1) / tc;
@@ -211,17 +223,14 @@ __host__ __device__ inline int walk_chunks(int npt, int tc) {
 // 1. Row prologue.
 // ---------------------------------------------------------------------------------------
 struct PrepParams {
-    const uint16_t* q;
     const uint16_t* o;
     const uint16_t* dout;
     const float* lse;
-    uint16_t* qc;
     float* nlse;
     float* ndelta;
     int* cnt;            // dK/dV arrival counters, zeroed here
-    int64_t qs0, qs1, qs2, os0, os1, os2, ds0, ds1, ds2;
+    int64_t os0, os1, os2, ds0, ds1, ds2;
     int batch, hq, N, Npad, ncnt;
-    float c;
 };
 
 template <int D>
@@ -237,21 +246,16 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(PrepParams p) {
     const int64_t bp = row / p.hq;
     const int pos = (int)(bp % p.Npad);
     const int b = (int)(bp / p.Npad);
-    u32x4_t qc4 = {0u, 0u, 0u, 0u};
     float dot = 0.f;
     if (pos < p.N) {
-        const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(p.q + b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)h * p.qs2 + 8 * c8);
         const u32x4_t ow = *reinterpret_cast<const u32x4_t*>(p.o + b * p.os0 + (int64_t)pos * p.os1 + (int64_t)h * p.os2 + 8 * c8);
         const u32x4_t dw = *reinterpret_cast<const u32x4_t*>(p.dout + b * p.ds0 + (int64_t)pos * p.ds1 + (int64_t)h * p.ds2 + 8 * c8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // Same rounding as the forward's Q operand: fp32 product, then bf16 RNE.
-            qc4[i] = pack_bf16x2(__uint_as_float(qw[i] << 16) * p.c, __uint_as_float(qw[i] & 0xffff0000u) * p.c);
             dot = fmaf(__uint_as_float(ow[i] << 16), __uint_as_float(dw[i] << 16), dot);
             dot = fmaf(__uint_as_float(ow[i] & 0xffff0000u), __uint_as_float(dw[i] & 0xffff0000u), dot);
         }
     }
-    *reinterpret_cast<u32x4_t*>(p.qc + ((int64_t)(b * (int64_t)p.Npad + pos) * p.hq + h) * D + 8 * c8) = qc4;
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
     if (c8 == 0) {
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(PrepParams p) {
 // 2. dK / dV.
 // ---------------------------------------------------------------------------------------
 struct DkvParams {
-    const uint16_t* qc;      // workspace [batch][Npad][hq][D]
+    const uint16_t* q;
     const uint16_t* dout;
     const uint16_t* k;
     const uint16_t* v;
@@ -275,10 +279,12 @@ struct DkvParams {
     uint16_t* dv;
     float* part;             // workspace [nch_max][kblocks][bg][key groups][32 keys x 2D] fp32
     int* cnt;                // workspace [kblocks][bg][key groups][dV, dK], zero on entry
-    int64_t ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
+    int64_t qs0, qs2, ds0, ds2, ks0, ks1, ks2, vs0, vs1, vs2, dks0, dks1, dks2, dvs0, dvs1, dvs2;
+    int qs1, ds1;            // position strides of Q and dO (at most 2^25 elements)
     int hq, hkv, G, P, L, B, N, Npad;
     int bg_count, kblocks, nch_max, tc;
     int kgroups;             // 32-key groups per key block (4 at head_dim 64, 6 at 128)
+    float c, scale;          // scale * log2(e) (folded into K), scale (applied to dK)
 };
 
 // dV (part 0) or dK (part 1) of one wave's 32 keys (key group kg of the block; j = this
@@ -344,9 +350,9 @@ __device__ inline void dkdv_finish_part(const DkvParams& p, int part, int c, int
             }
         }
     }
-    // dV = dV^T^T; dK = ln2 * dK^T^T (Qc carries scale*log2(e) where dK needs scale).
+    // dV = dV^T^T; dK = scale * dK^T^T (the walk multiplies by Q itself).
     if (!kvalid) return;
-    const float mul = part ? kLn2 : 1.f;
+    const float mul = part ? p.scale : 1.f;
     uint16_t* out = part ? p.dk + b * p.dks0 + (int64_t)j * p.dks1 + (int64_t)g * p.dks2
                          : p.dv + b * p.dvs0 + (int64_t)j * p.dvs1 + (int64_t)g * p.dvs2;
 #pragma unroll
@@ -363,7 +369,7 @@ __device__ inline void dkdv_finish_part(const DkvParams& p, int part, int c, int
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kernel(DkvParams p) {
+__global__ __launch_bounds__(kThreadsB, D == 64 ? 3 : 1) void attn_bwd_dkdv_kernel(DkvParams p) {
     constexpr int NC = D / 16;                    // 16-wide d chunks of the S / dP contractions
     constexpr int NDB = D / 32;                   // 32-row d blocks of dK^T / dV^T
     constexpr int CPR = D / 8;                    // 16-byte chunks per tile row
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
         const uint16_t* vp = p.v + b * p.vs0 + (int64_t)jj * p.vs1 + (int64_t)g * p.vs2 + 8 * g2;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-            kf[cc] = *reinterpret_cast<const bf16x8_t*>(kp + 16 * cc);
+            kf[cc] = scale_bf16x8(*reinterpret_cast<const bf16x8_t*>(kp + 16 * cc), p.c);
             vf[cc] = *reinterpret_cast<const bf16x8_t*>(vp + 16 * cc);
         }
     }
@@ -432,16 +438,15 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
     }
 
     // Copy of step `it` (position tile, head) into stage ST.  Window slot (row r,
-    // position ps) holds logical chunk ps ^ swz_kv(r) of row r; dO rows past N repeat row
-    // N-1 (finite; such rows are always masked).  The scalar copy: wave w moves bytes
+    // position ps) holds logical chunk ps ^ swz_kv(r) of row r; Q and dO rows past N repeat
+    // row N-1 (finite; such rows are always masked).  The scalar copy: wave w moves bytes
     // [64w, 64w + 64) of [-LSE2 x 32][-D x 32] with four lanes.
-    const int64_t qc_row = (int64_t)p.hq * D;   // Qc position stride (elements)
     uint32_t qgo[PERW], ogo[PERW];
 #pragma unroll
     for (int w = 0; w < PERW; ++w) {
         const int slot = 64 * (wave * PERW + w) + lane;
         const int r = slot / CPR, ps = slot % CPR;
-        qgo[w] = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_kv<D>(r)));
+        qgo[w] = (uint32_t)(r * p.qs1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
         ogo[w] = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
     }
     // Running position of the next copy (walk order: position tile, then head): tile index
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
     auto seek = [&]() __attribute__((always_inline)) {
         ip0 = pos_tile(iti) * kT;
         const int head = g * p.G;
-        iq = p.qc + ((int64_t)b * p.Npad + ip0) * qc_row + (int64_t)head * D;
+        iq = p.q + b * p.qs0 + (int64_t)ip0 * p.qs1 + (int64_t)head * p.qs2;
         io = p.dout + b * p.ds0 + (int64_t)ip0 * p.ds1 + (int64_t)head * p.ds2;
         isl = (wave < 2 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + ip0 + 16 * (wave & 1);
     };
@@ -465,15 +470,16 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
 #pragma unroll
         for (int w = 0; w < PERW; ++w) {
             const int jw = wave * PERW + w;
-            dma16_sv(iq, qgo[w], lds_addr(ring_q<D, ST>()) + 1024 * jw);
-            if (full) {
-                dma16_sv(io, ogo[w], lds_addr(ring_o<D, ST>()) + 1024 * jw);
-            } else {
+            uint32_t oq = qgo[w], oo = ogo[w];
+            if (!full) {
                 const int slot = 64 * jw + lane;
                 const int r = slot / CPR, ps = slot % CPR;
                 const int rr = min(r, p.N - 1 - ip0);
-                dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(ring_o<D, ST>()) + 1024 * jw);
+                oq = (uint32_t)(rr * p.qs1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
+                oo = (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
             }
+            dma16_sv(iq, oq, lds_addr(ring_q<D, ST>()) + 1024 * jw);
+            dma16_sv(io, oo, lds_addr(ring_o<D, ST>()) + 1024 * jw);
         }
         if (lane < 4) dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(ring_s<D, ST>()) + 64 * wave);
         if (++ih == p.G) {
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
             ++iti;
             seek();
         } else {
-            iq += D;
+            iq += p.qs2;
             io += p.ds2;
             isl += p.Npad;
         }
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
         const char* qt = reinterpret_cast<const char*>(ring_q<D, ST>());
         const char* ot = reinterpret_cast<const char*>(ring_o<D, ST>());
         const char* st = reinterpret_cast<const char*>(ring_s<D, ST>());
-        // S = Qc K^T - LSE2 and dP = dO V^T - D; element e is tile row 4*g2 + acc_off(e).
+        // S = Q Kc^T - LSE2 and dP = dO V^T - D; element e is tile row 4*g2 + acc_off(e).
         f32x16_t s, dp;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -561,7 +567,7 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
         bf16x8_t pb[2], sb[2];
         pack_b(s, pb);
         pack_b(dp, sb);
-        // dV^T += dO^T P,  dK^T += Qc^T dS  (A operands: transposed tile reads).
+        // dV^T += dO^T P,  dK^T += Q^T dS  (A operands: transposed tile reads).
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -587,23 +593,24 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 2 : 1) void attn_bwd_dkdv_kern
 //   400 registers.  Split by role, a wave holds one sum and one fragment set (~160
 //   registers), so three waves fit a SIMD.  A workgroup of 12 waves owns 192 keys; waves w
 //   and w + 6 share key group w and split every step's products:
-//     role 0 (wave w):     K fragments in registers; S = Qc K^T - LSE2, P = 2^S,
+//     role 0 (wave w):     Kc fragments in registers; S = Q Kc^T - LSE2, P = 2^S,
 //                          dV^T += dO^T P;
 //     role 1 (wave w + 6): V fragments in registers; dP = dO V^T - D, dS = P o dP,
-//                          dK^T += Qc^T dS.
-//   P goes from role 0 to role 1 in fp32 through a two-buffer LDS exchange, so role 1 runs
-//   one step behind: in iteration t it finishes step t - 1 (dS, dK MFMAs) and then issues
-//   the dP MFMAs of step t, whose result it carries into iteration t + 1.  K and V never go
-//   through LDS; each step's Qc / dO tiles serve 192 keys.  The tiles and row scalars
-//   stream through a 5-stage ring, one step per iteration (steps t - 1 and t in use, three
-//   in flight): waves 0..7 copy the tile windows, waves 8..11 the scalars.
+//                          dK^T += Q^T dS.
+//   An iteration covers two steps and one barrier.  P goes from role 0 to role 1 in bf16
+//   (the values the dV MFMAs take) through an LDS exchange of two parities, so role 1 runs
+//   one iteration behind: in iteration t role 0 does steps 2t and 2t + 1, role 1 steps
+//   2t - 2 and 2t - 1, forming each step's dP right before its dS.  K and V never go
+//   through LDS; each step's Q / dO tiles serve 192 keys.  The tiles and row scalars
+//   stream through a 6-stage ring (steps 2t - 2 .. 2t + 1 in use, 2t + 2 and 2t + 3 in
+//   flight): role-0 waves 0..3 copy the tile windows, waves 4 and 5 the scalars.
 // ---------------------------------------------------------------------------------------
 constexpr int kGroupsR = 6;                  // 32-key groups per workgroup
 constexpr int kWavesR = 2 * kGroupsR;
 constexpr int kThreadsR = 64 * kWavesR;
 constexpr int kKeysPerWGR = kGroupsR * kT;   // 192
 constexpr int kStagesR = 6;
-__shared__ __attribute__((aligned(16))) uint16_t g_rq[kStagesR][kT * 128];   // Qc tiles
+__shared__ __attribute__((aligned(16))) uint16_t g_rq[kStagesR][kT * 128];   // Q tiles
 __shared__ __attribute__((aligned(16))) uint16_t g_ro[kStagesR][kT * 128];   // dO tiles
 __shared__ __attribute__((aligned(16))) float g_rs[kStagesR][64];            // [-LSE2 x 32][-D x 32]
 __shared__ __attribute__((aligned(16))) uint16_t g_rx[2][2][kGroupsR][16 * 64];   // bf16 P: [parity][step][key group][half][lane]
@@ -611,7 +618,7 @@ __shared__ __attribute__((aligned(16))) uint16_t g_rx[2][2][kGroupsR][16 * 64]; 
 __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvParams p) {
     constexpr int D = 128;
     constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8;
-    constexpr int TSZ = kT * D * 2;                 // bytes of one Qc or dO tile
+    constexpr int TSZ = kT * D * 2;                 // bytes of one Q or dO tile
     static_assert(kT * CPR / 64 == 8, "eight 1 KB copy windows per tile, two per copying wave");
 
     const int lane = threadIdx.x & 63;
@@ -665,20 +672,22 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
         const uint16_t* src = role == 0 ? p.k + b * p.ks0 + (int64_t)jj * p.ks1 + (int64_t)g * p.ks2
                                         : p.v + b * p.vs0 + (int64_t)jj * p.vs1 + (int64_t)g * p.vs2;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) bfr[cc] = *reinterpret_cast<const bf16x8_t*>(src + 16 * cc + 8 * g2);
+        for (int cc = 0; cc < NC; ++cc) {
+            const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(src + 16 * cc + 8 * g2);
+            bfr[cc] = role == 0 ? scale_bf16x8(x, p.c) : x;
+        }
     }
 
     // Step copies, by the role-0 waves only (role 1 has the longer step): wave w < 4 moves
-    // windows 2w and 2w + 1 of the Qc tile and of the dO tile, waves 4 and 5 the 128 bytes
+    // windows 2w and 2w + 1 of the Q tile and of the dO tile, waves 4 and 5 the 128 bytes
     // of -LSE2 and of -D.  Walk order: position tile, then head; the next copy's step is
-    // (iti, ih).
-    const int64_t qc_row = (int64_t)p.hq * D;
+    // (iti, ih).  Q and dO rows past N repeat row N - 1 (finite; always masked).
     uint32_t qgo[2], ogo[2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
         const int slot = 64 * (2 * (wave & 3) + jj) + lane;
         const int r = slot / CPR, ps = slot % CPR;
-        qgo[jj] = (uint32_t)(r * qc_row * 2 + 16 * (ps ^ swz_kv<D>(r)));
+        qgo[jj] = (uint32_t)(r * p.qs1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
         ogo[jj] = (uint32_t)(r * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
     }
     int iti = 0, ih = 0, ip0 = 0;
@@ -688,7 +697,7 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
     auto seek = [&]() __attribute__((always_inline)) {
         ip0 = pos_tile(iti) * kT;
         const int head = g * p.G;
-        iq = p.qc + ((int64_t)b * p.Npad + ip0) * qc_row + (int64_t)head * D;
+        iq = p.q + b * p.qs0 + (int64_t)ip0 * p.qs1 + (int64_t)head * p.qs2;
         io = p.dout + b * p.ds0 + (int64_t)ip0 * p.ds1 + (int64_t)head * p.ds2;
         isl = (wave == 4 ? p.nlse : p.ndelta) + ((int64_t)b * p.hq + head) * p.Npad + ip0;
     };
@@ -698,15 +707,16 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int win = 2 * wave + jj;
-                dma16_sv(iq, qgo[jj], lds_addr(&g_rq[0][0]) + st * TSZ + 1024 * win);
-                if (ip0 + kT <= p.N) {
-                    dma16_sv(io, ogo[jj], lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * win);
-                } else {
+                uint32_t oq = qgo[jj], oo = ogo[jj];
+                if (ip0 + kT > p.N) {
                     const int slot = 64 * win + lane;
                     const int r = slot / CPR, ps = slot % CPR;
                     const int rr = min(r, p.N - 1 - ip0);
-                    dma16_sv(io, (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r))), lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * win);
+                    oq = (uint32_t)(rr * p.qs1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
+                    oo = (uint32_t)(rr * p.ds1 * 2 + 16 * (ps ^ swz_kv<D>(r)));
                 }
+                dma16_sv(iq, oq, lds_addr(&g_rq[0][0]) + st * TSZ + 1024 * win);
+                dma16_sv(io, oo, lds_addr(&g_ro[0][0]) + st * TSZ + 1024 * win);
             }
         } else if (wave < 6 && lane < 8) {
             dma16_sv(isl, (uint32_t)(16 * lane), lds_addr(&g_rs[0][0]) + st * 256 + 128 * (wave - 4));
@@ -716,7 +726,7 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
             ++iti;
             seek();
         } else {
-            iq += D;
+            iq += p.qs2;
             io += p.ds2;
             isl += p.Npad;
         }
@@ -739,7 +749,7 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
     __syncthreads();
 
     // S (role 0) or dP (role 1) of a step: the accumulator starts at the rows' -LSE2 or -D
-    // (scalars at byte offset 0 or 128 of the stage); its A operand (Qc or dO rows) is read
+    // (scalars at byte offset 0 or 128 of the stage); its A operand (Q or dO rows) is read
     // PF MFMAs ahead with a scheduling fence per MFMA.
     auto row_product = [&](const char* at, const char* sp, f32x16_t& x) __attribute__((always_inline)) {
 #pragma unroll
@@ -759,7 +769,7 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // acc += (tile^T) y, the transposed tile read as A operands (dO for dV, Qc for dK).
+    // acc += (tile^T) y, the transposed tile read as A operands (dO for dV, Q for dK).
     auto col_product = [&](const char* tt, const bf16x8_t (&y)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
@@ -878,17 +888,17 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
 // 3. dQ.
 // ---------------------------------------------------------------------------------------
 struct DqParams {
-    const uint16_t* qc;
+    const uint16_t* q;
     const uint16_t* dout;
     const uint16_t* k;
     const uint16_t* v;
     const float* nlse;
     const float* ndelta;
     uint16_t* dq;
-    int64_t ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, qs0, qs1, qs2;
+    int64_t qs0, qs1, qs2, ds0, ds1, ds2, ks0, ks1, ks2, vs0, vs1, vs2, dqs0, dqs1, dqs2;
     int hq, hkv, G, P, L, B, N, Npad;
     int rows_per_pair, tiles_per_pair, tN0, bg_count;
-    float scale;
+    float scale, c;
 };
 
 template <int D>
@@ -921,13 +931,15 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
     const int pos = uu / p.G;
     const int head = g * p.G + uu % p.G;
     const RowBounds rb = row_bounds(pos, p.P, p.L, p.B);
+    // The lane's half row (d = 16 cc + 8 g2 + [0, 8)) of Qc = bf16(Q c), rounded as the
+    // forward rounds its Q operand, and of dO.
     bf16x8_t qf[NC], of[NC];
     {
-        const uint16_t* qp = p.qc + ((int64_t)b * p.Npad + pos) * ((int64_t)p.hq * D) + (int64_t)head * D + 8 * g2;
+        const uint16_t* qp = p.q + b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)head * p.qs2 + 8 * g2;
         const uint16_t* op = p.dout + b * p.ds0 + (int64_t)pos * p.ds1 + (int64_t)head * p.ds2 + 8 * g2;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-            qf[cc] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * cc);
+            qf[cc] = scale_bf16x8(*reinterpret_cast<const bf16x8_t*>(qp + 16 * cc), p.c);
             of[cc] = *reinterpret_cast<const bf16x8_t*>(op + 16 * cc);
         }
     }
@@ -1098,7 +1110,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void attn_bwd_dq_kernel(DqParams p) {
 
     // dQ = scale * dQ^T^T (bf16).
     if (valid) {
-        uint16_t* qo = p.dq + b * p.qs0 + (int64_t)pos * p.qs1 + (int64_t)head * p.qs2;
+        uint16_t* qo = p.dq + b * p.dqs0 + (int64_t)pos * p.dqs1 + (int64_t)head * p.dqs2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -1137,12 +1149,12 @@ void walk_plan(int P, int L, int B, int N, int bg, int d, int kpb, int* tc, int*
     *nch_max = walk_chunks(maxnpt, *tc);
 }
 
-// Workspace: Qc [batch][Npad][hq][D] bf16 | -LSE2 [batch][hq][Npad] | -D [batch][hq][Npad] |
+// Workspace: -LSE2 [batch][hq][Npad] | -D [batch][hq][Npad] |
 // counters [kblocks][batch*hkv][groups][2] int | partials [nch][kblocks][batch*hkv][groups][32 x 2D] fp32
 // (groups = 32-key groups per key block: 4 at head_dim 64, 6 at head_dim 128)
 // (partials only when some key block's walk is split).
 struct BwdLayout {
-    size_t qc, nlse, ndelta, cnt, part, total;
+    size_t nlse, ndelta, cnt, part, total;
     int Npad, kpb, kgroups, kblocks, nch, tc;
 };
 BwdLayout bwd_layout(int batch, int hq, int hkv, int d, int P, int L, int B, int N) {
@@ -1153,8 +1165,7 @@ BwdLayout bwd_layout(int batch, int hq, int hkv, int d, int P, int L, int B, int
     w.kblocks = (N + w.kpb - 1) / w.kpb;
     const size_t bg = (size_t)batch * hkv;
     walk_plan(P, L, B, N, (int)bg, d, w.kpb, &w.tc, &w.nch);
-    w.qc = 0;
-    w.nlse = r256((size_t)batch * w.Npad * hq * d * 2);
+    w.nlse = 0;
     w.ndelta = w.nlse + r256((size_t)batch * hq * w.Npad * 4);
     w.cnt = w.ndelta + r256((size_t)batch * hq * w.Npad * 4);
     w.part = w.cnt + r256((size_t)w.kblocks * bg * w.kgroups * 2 * 4);
@@ -1172,7 +1183,6 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     const BwdLayout w = bwd_layout(a.batch, a.hq, a.hkv, a.d, a.P, a.L, a.B, a.N);
     const int Npad = w.Npad;
     char* ws = static_cast<char*>(a.ws);
-    uint16_t* qc = reinterpret_cast<uint16_t*>(ws + w.qc);
     float* nlse = reinterpret_cast<float*>(ws + w.nlse);
     float* ndelta = reinterpret_cast<float*>(ws + w.ndelta);
     int* cnt = reinterpret_cast<int*>(ws + w.cnt);
@@ -1182,15 +1192,12 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     const int bg_count = a.batch * a.hkv;
 
     PrepParams pp;
-    pp.q = static_cast<const uint16_t*>(a.q);
     pp.o = static_cast<const uint16_t*>(a.o);
     pp.dout = static_cast<const uint16_t*>(a.dout);
     pp.lse = a.lse;
-    pp.qc = qc;
     pp.nlse = nlse;
     pp.ndelta = ndelta;
     pp.cnt = cnt;
-    pp.qs0 = a.qs[0]; pp.qs1 = a.qs[1]; pp.qs2 = a.qs[2];
     pp.os0 = a.os[0]; pp.os1 = a.os[1]; pp.os2 = a.os[2];
     pp.ds0 = a.dos[0]; pp.ds1 = a.dos[1]; pp.ds2 = a.dos[2];
     pp.batch = a.batch;
@@ -1198,7 +1205,6 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     pp.N = a.N;
     pp.Npad = Npad;
     pp.ncnt = w.kblocks * bg_count * w.kgroups * 2;
-    pp.c = c;
     int64_t prep_threads = (int64_t)a.batch * Npad * a.hq * (a.d / 8);
     if (prep_threads < pp.ncnt) prep_threads = pp.ncnt;
     const dim3 pg((unsigned)((prep_threads + 255) / 256));
@@ -1206,7 +1212,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL((attn_bwd_prep_kernel<64>), pg, dim3(256), 0, s, pp);
 
     DkvParams kp;
-    kp.qc = qc;
+    kp.q = static_cast<const uint16_t*>(a.q);
     kp.dout = pp.dout;
     kp.k = static_cast<const uint16_t*>(a.k);
     kp.v = static_cast<const uint16_t*>(a.v);
@@ -1216,7 +1222,8 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.dv = static_cast<uint16_t*>(a.dv);
     kp.part = part;
     kp.cnt = cnt;
-    kp.ds0 = a.dos[0]; kp.ds1 = a.dos[1]; kp.ds2 = a.dos[2];
+    kp.qs0 = a.qs[0]; kp.qs1 = (int)a.qs[1]; kp.qs2 = a.qs[2];
+    kp.ds0 = a.dos[0]; kp.ds1 = (int)a.dos[1]; kp.ds2 = a.dos[2];
     kp.ks0 = a.ks[0]; kp.ks1 = a.ks[1]; kp.ks2 = a.ks[2];
     kp.vs0 = a.vs[0]; kp.vs1 = a.vs[1]; kp.vs2 = a.vs[2];
     kp.dks0 = a.dks[0]; kp.dks1 = a.dks[1]; kp.dks2 = a.dks[2];
@@ -1234,12 +1241,14 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.kgroups = w.kgroups;
     kp.nch_max = w.nch;
     kp.tc = w.tc;
+    kp.c = c;
+    kp.scale = a.scale;
     const dim3 kg((unsigned)((int64_t)w.nch * w.kblocks * bg_count));
     if (a.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_role_kernel, kg, dim3(kThreadsR), 0, s, kp);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), kg, dim3(kThreadsB), 0, s, kp);
 
     DqParams qp;
-    qp.qc = qc;
+    qp.q = kp.q;
     qp.dout = pp.dout;
     qp.k = kp.k;
     qp.v = kp.v;
@@ -1249,7 +1258,8 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     qp.ds0 = a.dos[0]; qp.ds1 = a.dos[1]; qp.ds2 = a.dos[2];
     qp.ks0 = a.ks[0]; qp.ks1 = a.ks[1]; qp.ks2 = a.ks[2];
     qp.vs0 = a.vs[0]; qp.vs1 = a.vs[1]; qp.vs2 = a.vs[2];
-    qp.qs0 = a.dqs[0]; qp.qs1 = a.dqs[1]; qp.qs2 = a.dqs[2];
+    qp.qs0 = a.qs[0]; qp.qs1 = a.qs[1]; qp.qs2 = a.qs[2];
+    qp.dqs0 = a.dqs[0]; qp.dqs1 = a.dqs[1]; qp.dqs2 = a.dqs[2];
     qp.hq = a.hq;
     qp.hkv = a.hkv;
     qp.G = G;
@@ -1266,6 +1276,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     qp.tN0 = tN0;
     qp.bg_count = bg_count;
     qp.scale = a.scale;
+    qp.c = c;
     const dim3 qg((unsigned)((int64_t)qp.tiles_per_pair * qp.bg_count));
     if (a.d == 128) hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), qg, dim3(kThreadsB), 0, s, qp);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<64>), qg, dim3(kThreadsB), 0, s, qp);

@@ -143,7 +143,8 @@ int mars_attn_bwd(const mars_attn_desc* desc, const mars_attn_bwd_strides* gs, c
     if (!strides_ok(gs->do_strides, 2) || !strides_ok(gs->dq_strides, 2) || !strides_ok(gs->dk_strides, 2) ||
         !strides_ok(gs->dv_strides, 2))
         return MARS_EINVAL;
-    if (gs->do_strides[1] > kMaxKeyPosStride) return MARS_EUNSUPPORTED;
+    // The backward's Q and dO tile copies address 32 positions with 32-bit byte offsets.
+    if (gs->do_strides[1] > kMaxKeyPosStride || desc->q_strides[1] > kMaxKeyPosStride) return MARS_EUNSUPPORTED;
     const size_t need = mars::attn_bwd_workspace_bytes(desc->batch, desc->n_q_heads, desc->n_kv_heads,
                                                        desc->head_dim, desc->prompt_len, desc->resp_len, desc->block);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MARS_EWORKSPACE;

@@ -100,12 +100,13 @@ def bwd_bounds(q, k, v, do, o_in, lse_err, P, L, B, rows=None, keys=None, scale=
     q, k, v, do: float64 copies of the bf16 inputs; o_in: the O handed to the kernel;
     lse_err: [b, Hq, N] bound on |LSE_in - LSE_exact| (nats).  Sources of error, each bounded
     by its largest effect (u = 2^-8, bf16's unit roundoff):
-      * the scores use bf16(Q*scale*log2 e) as the forward does: score (i, j) moves by at
-        most u*c*sum_d |q_id||k_jd| (log2 units), so P_ij by a relative 2^(u c m_i) - 1 with
-        m_i the max over keys; the LSE input adds e^lse_err - 1;
+      * the scores round one operand times c = scale*log2 e to bf16 (Q in dQ, as the forward
+        does; K in dK/dV): score (i, j) moves by at most u*c*sum_d |q_id||k_jd| (log2 units),
+        so P_ij by a relative 2^(u c m_i) - 1 with m_i the max over keys; the LSE input adds
+        e^lse_err - 1;
       * D_i = sum dO.O from the given O: |dD_i| <= sum_d |dO_id||O_in - O_exact|_id;
-      * P (for dV) and dS (for dQ, dK) are rounded to bf16 (u each), Q*c as well (dK); at
-        head_dim 128 the dK side forms dS from the bf16 P the dV side uses (one more u on dS);
+      * P (for dV) and dS (for dQ, dK) are rounded to bf16 (u each); at head_dim 128 the dK
+        side forms dS from the bf16 P the dV side uses (one more u on dS);
       * fp32 accumulation over n terms: n*2^-24 of the sum of absolute terms;
       * the bf16 output rounding: u |grad|.
     Returns (bq [b,R,Hq,D], bk [b,K,Hkv,D], bv [b,K,Hkv,D]) for rows / keys (all by default).

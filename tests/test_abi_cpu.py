@@ -112,13 +112,13 @@ def test_attn_bwd_validation_errors():
     assert lib.mars_attn_bwd_workspace_bytes(ctypes.byref(good()), ctypes.byref(n)) == L.MARS_OK
     N, Np = 50, 64                                           # positions padded to a multiple of 32
     r256 = lambda x: (x + 255) // 256 * 256
-    # Qc, -LSE2, -D, two counters (dV, dK) per (key block, pair, 32-key group); no partials
+    # -LSE2, -D, two counters (dV, dK) per (key block, pair, 32-key group); no partials
     # (one chunk per block)
-    assert n.value == r256(2 * Np * 14 * 64 * 2) + 2 * r256(2 * 14 * Np * 4) + r256(1 * 4 * 4 * 2 * 4)
+    assert n.value == 2 * r256(2 * 14 * Np * 4) + r256(1 * 4 * 4 * 2 * 4)
     big = ctypes.c_size_t()
     assert lib.mars_attn_bwd_workspace_bytes(ctypes.byref(M.attn_desc(1, 2, 1, 64, 256, 512, 4)), ctypes.byref(big)) == 0
     Nb = 1280                                                # prompt keys walk all 40 tiles: 8 chunks
-    assert big.value == (r256(Nb * 2 * 64 * 2) + 2 * r256(2 * Nb * 4) + r256(10 * 1 * 4 * 2 * 4)
+    assert big.value == (2 * r256(2 * Nb * 4) + r256(10 * 1 * 4 * 2 * 4)
                          + r256(8 * 10 * 1 * 128 * 2 * 64 * 4))
     assert lib.mars_attn_bwd_workspace_bytes(ctypes.byref(good()), None) == L.MARS_EINVAL
     d = good(); d.dtype = L.MARS_DTYPE_FP32
@@ -132,6 +132,8 @@ def test_attn_bwd_validation_errors():
     assert _bwd(good(), gs) == L.MARS_EINVAL
     gs = strides(); gs.do_strides[1] = (1 << 25) + 8
     assert _bwd(good(), gs) == L.MARS_EUNSUPPORTED
+    d = good(); d.q_strides[1] = (1 << 25) + 8             # the backward copies Q tiles too
+    assert _bwd(d, strides()) == L.MARS_EUNSUPPORTED
     d = good(); d.head_dim = 96
     assert _bwd(d, strides()) == L.MARS_EUNSUPPORTED
     assert _bwd(good(), strides(), ws=None) == L.MARS_EWORKSPACE
