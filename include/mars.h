@@ -169,6 +169,9 @@ int mars_attn_fwd_tilelog(const mars_attn_desc* desc, const void* q, const void*
  *   dV = P^T dO,   dS = P o (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q;
  * dK and dV of KV head g sum the contributions of its query heads h (g = h / G).
  * Rows and keys outside the mask contribute nothing; skipped tiles are never computed.
+ * Precision: bf16 MFMA operands, fp32 accumulation.  Scores are recomputed with one operand
+ * times scale*log2(e) rounded to bf16: Q for dQ (as the forward rounds it), K for dK and dV.
+ * P and dS enter their products in bf16; results are rounded to nearest even.
  * ------------------------------------------------------------------------------------ */
 typedef struct mars_attn_bwd_strides {
     int64_t do_strides[3]; /* d_o [batch][N][n_q_heads][head_dim]: batch, position, head */

@@ -99,7 +99,7 @@ __device__ inline float sum32(float x) {
 // row so that the MFMA operand reads are free of bank conflicts:
 //   * K (ds_read_b128, lane = row, same logical chunk): chunk c of row r at c ^ swz_k(r);
 //   * V (ds_read_b64_tr_b16, 4 rows x 2 chunks per 16 lanes): chunk c of row r at c ^ swz_v(r);
-//   * tiles read both ways (the backward's Qc, dO and K tiles): chunk c of row r at
+//   * tiles read both ways (the backward's Q, dO and K tiles): chunk c of row r at
 //     c ^ swz_kv(r), which is injective on every 16 consecutive rows of one parity class
 //     (row reads) and gives the 4 rows of an aligned group disjoint chunk quads (transposed
 //     reads).  Unlike swz_v it is not periodic in 8 rows: swz_kv(r + 8) = swz_kv(r) ^ 2 for
