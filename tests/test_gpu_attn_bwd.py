@@ -111,6 +111,15 @@ def test_bwd_deterministic():
         assert torch.equal(x, y)
 
 
+def _head_major(x):
+    """x [b, N, H, D] copied into head-major storage with one spare head: a [b, N, H, D] view
+    whose position stride is D and head stride N * D."""
+    bb, n, h, d = x.shape
+    big = torch.zeros((bb, h + 1, n, d), dtype=x.dtype, device=x.device)
+    big[:, :h] = x.permute(0, 2, 1, 3)
+    return big[:, :h].permute(0, 2, 1, 3)
+
+
 def test_bwd_strided_views():
     """Gradient outputs and dO as strided views of larger buffers (head-major storage);
     the padding around them stays untouched."""
@@ -121,9 +130,7 @@ def test_bwd_strided_views():
     lse = torch.empty((b, hq, N), dtype=torch.float32, device=dev())
     o = M.mars_attn_fwd(q, k, v, P, L, B, lse=lse)
     ref = M.mars_attn_bwd(q, k, v, o, lse, do_c, P, L, B)
-    big_do = torch.zeros((b, hq + 1, N, d), dtype=torch.bfloat16, device=dev())
-    big_do[:, :hq] = do_c.permute(0, 2, 1, 3)
-    do_v = big_do[:, :hq].permute(0, 2, 1, 3)
+    do_v = _head_major(do_c)
     bufs = [torch.full((b, h + 1, N, d), 7.0, dtype=torch.bfloat16, device=dev()) for h in (hq, hkv, hkv)]
     views = [buf[:, :h].permute(0, 2, 1, 3) for buf, h in zip(bufs, (hq, hkv, hkv))]
     M.mars_attn_bwd(q, k, v, o, lse, do_v, P, L, B, dq=views[0], dk=views[1], dv=views[2])
@@ -131,6 +138,27 @@ def test_bwd_strided_views():
     for r, vw, buf, h in zip(ref, views, bufs, (hq, hkv, hkv)):
         assert torch.equal(r, vw)
         assert torch.all(buf[:, h:] == 7.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_strided_inputs(d):
+    """Q, K, V, O and dO all head-major views (position stride D, head stride N*D): the
+    dK/dV kernels copy the caller's Q and dO tiles with those strides, rows past N (N = 88,
+    a ragged last tile) repeating row N - 1.  Bit-identical to the contiguous call."""
+    b, hq, hkv, P, L, B = 2, 4, 2, 8, 40, 4
+    N = P + 2 * L
+    print(f"case bwd strided inputs d={d} N={N}", flush=True)
+    q, k, v = (t.to(dev()) for t in I.small_train_inputs(b, hq, hkv, d, P, L, 19))
+    do_c = I.small_grad_output(b, hq, d, P, L, 19).to(dev())
+    lse = torch.empty((b, hq, N), dtype=torch.float32, device=dev())
+    o = M.mars_attn_fwd(q, k, v, P, L, B, lse=lse)
+    ref = M.mars_attn_bwd(q, k, v, o, lse, do_c, P, L, B)
+    qs, ks, vs, os_, dos = (_head_major(t) for t in (q, k, v, o, do_c))
+    assert qs.stride(1) == d and qs.stride(2) == N * d
+    got = M.mars_attn_bwd(qs, ks, vs, os_, lse, dos, P, L, B)
+    torch.cuda.synchronize()
+    for r, g_ in zip(ref, got):
+        assert torch.equal(r, g_)
 
 
 @pytest.mark.parametrize("shape", [I.QWEN05B, I.QWEN7B, I.LONG7B], ids=lambda s: s.name)
