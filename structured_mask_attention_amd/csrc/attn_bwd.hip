@@ -51,7 +51,8 @@ constexpr int kRowsPerWGB = kWavesB * kT;  // dQ: 128 packed rows per workgroup
 constexpr int kChunkMax = 8;               // dK/dV: a key block's walk splits into at most 8 chunks
 constexpr int kChunkMinTiles = 4;          //        of at least 4 position tiles each
 constexpr int kNominalSlots64 = 512;       // workgroup slots the dK/dV chunk size aims at: 2 per CU at
-constexpr int kNominalSlots128 = 256;      // head_dim 64 (3 fit; 768 measured the same), 1 at head_dim 128
+constexpr int kNominalSlots128 = 192;      // head_dim 64 (3 fit; 768 measured the same); at head_dim 128
+                                           // (one per CU) 3/4 of the CUs: longer chunks, fewer partials
 
 // ---------------------------------------------------------------------------------------
 // LDS rings.  One file-scope object per stage, array and head_dim.
@@ -283,6 +284,7 @@ struct DkvParams {
     int qs1, ds1;            // position strides of Q and dO (at most 2^25 elements)
     int hq, hkv, G, P, L, B, N, Npad;
     int bg_count, kblocks, nch_max, tc;
+    int rot;                 // 1: chunk index rotated by the key block (see the launch)
     int kgroups;             // 32-key groups per key block (4 at head_dim 64, 6 at 128)
     float c, scale;          // scale * log2(e) (folded into K), scale (applied to dK)
 };
@@ -383,11 +385,12 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 3 : 1) void attn_bwd_dkdv_kern
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane & 31, g2 = lane >> 5;
-    // Work item: chunk c (fastest) of the walk of key block kblk of pair bg.
-    const int c = blockIdx.x % p.nch_max;
+    // Work item: chunk c (fastest, rotated by the key block when p.rot) of the walk of key
+    // block kblk of pair bg.
     const int rest = blockIdx.x / p.nch_max;
     const int bg = rest % p.bg_count;
     const int kblk = rest / p.bg_count;
+    const int c = ((int)(blockIdx.x % p.nch_max) + (p.rot ? p.nch_max - kblk % p.nch_max : 0)) % p.nch_max;
     const int b = bg / p.hkv, g = bg % p.hkv;
     const int PL = p.P + p.L;
     const int kb0 = kblk * kKeysPerWG;
@@ -626,10 +629,10 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
     const int role = wave >= kGroupsR ? 1 : 0;
     const int kg = wave - kGroupsR * role;
     const int hl = lane & 31, g2 = lane >> 5;
-    const int c = blockIdx.x % p.nch_max;
     const int rest = blockIdx.x / p.nch_max;
     const int bg = rest % p.bg_count;
     const int kblk = rest / p.bg_count;
+    const int c = ((int)(blockIdx.x % p.nch_max) + (p.rot ? p.nch_max - kblk % p.nch_max : 0)) % p.nch_max;
     const int b = bg / p.hkv, g = bg % p.hkv;
     const int PL = p.P + p.L;
     const int kb0 = kblk * kKeysPerWGR;
@@ -1243,6 +1246,18 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.tc = w.tc;
     kp.c = c;
     kp.scale = a.scale;
+    {
+        // Workgroup i runs on XCD i mod 8, each XCD taking its share in order.  The plain
+        // order (chunk fastest, then pair, then key block) keeps a (pair, chunk) of nearby key
+        // blocks on one XCD, where they share their Q / dO tiles in L2.  But when it sends
+        // every walk's chunk 0 to only some XCDs (short walks are chunk 0 alone), those XCDs
+        // get most of the work: then the chunk index is rotated by the key block instead.
+        unsigned seen = 0;
+        const int64_t S = (int64_t)bg_count * w.nch;
+        for (int kb = 0; kb < w.kblocks && kb < 8; ++kb)
+            for (int bi = 0; bi < bg_count && bi < 8; ++bi) seen |= 1u << (int)((kb * S + (int64_t)bi * w.nch) & 7);
+        kp.rot = seen == 0xffu ? 0 : 1;
+    }
     const dim3 kg((unsigned)((int64_t)w.nch * w.kblocks * bg_count));
     if (a.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_role_kernel, kg, dim3(kThreadsR), 0, s, kp);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), kg, dim3(kThreadsB), 0, s, kp);
