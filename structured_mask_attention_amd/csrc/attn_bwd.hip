@@ -50,6 +50,7 @@ constexpr int kKeysPerWG = kWavesB * kT;   // dK/dV at head_dim 64: 128 keys per
 constexpr int kRowsPerWGB = kWavesB * kT;  // dQ: 128 packed rows per workgroup
 constexpr int kChunkMax = 8;               // dK/dV: a key block's walk splits into at most 8 chunks
 constexpr int kChunkMinTiles = 4;          //        of at least 4 position tiles each
+constexpr int kOrderMax = 1024;            // dK/dV work list passed with the launch (entries)
 constexpr int kNominalSlots64 = 512;       // workgroup slots the dK/dV chunk size aims at: 2 per CU at
 constexpr int kNominalSlots128 = 192;      // head_dim 64 (3 fit; 768 measured the same); at head_dim 128
                                            // (one per CU) 3/4 of the CUs: longer chunks, fewer partials
@@ -285,9 +286,30 @@ struct DkvParams {
     int hq, hkv, G, P, L, B, N, Npad;
     int bg_count, kblocks, nch_max, tc;
     int rot;                 // 1: chunk index rotated by the key block (see the launch)
+    int nord;                // > 0: the grid follows ord (longest chunks first), bg_count
+                             // workgroups per entry; 0: the closed-form order
+    uint16_t ord[kOrderMax]; // entry = key block << 3 | chunk
     int kgroups;             // 32-key groups per key block (4 at head_dim 64, 6 at 128)
     float c, scale;          // scale * log2(e) (folded into K), scale (applied to dK)
 };
+
+// Work item of this workgroup.  With a work list (p.nord > 0): entry blockIdx.x / bg_count,
+// pair blockIdx.x % bg_count, so the pairs of one (key block, chunk) go to consecutive XCDs
+// and the longest chunks start first.  Without: chunk fastest (rotated by the key block when
+// p.rot), then pair, then key block.
+__device__ inline void dkdv_item(const DkvParams& p, int& bg, int& kblk, int& c) {
+    if (p.nord > 0) {
+        bg = (int)(blockIdx.x % (unsigned)p.bg_count);
+        const int e = p.ord[blockIdx.x / (unsigned)p.bg_count];
+        kblk = e >> 3;
+        c = e & 7;
+    } else {
+        const int rest = (int)(blockIdx.x / (unsigned)p.nch_max);
+        bg = rest % p.bg_count;
+        kblk = rest / p.bg_count;
+        c = ((int)(blockIdx.x % (unsigned)p.nch_max) + (p.rot ? p.nch_max - kblk % p.nch_max : 0)) % p.nch_max;
+    }
+}
 
 // dV (part 0) or dK (part 1) of one wave's 32 keys (key group kg of the block; j = this
 // lane's key), from its accumulator acc = dV^T or dK^T: stored directly when the walk is one
@@ -385,12 +407,9 @@ __global__ __launch_bounds__(kThreadsB, D == 64 ? 3 : 1) void attn_bwd_dkdv_kern
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane & 31, g2 = lane >> 5;
-    // Work item: chunk c (fastest, rotated by the key block when p.rot) of the walk of key
-    // block kblk of pair bg.
-    const int rest = blockIdx.x / p.nch_max;
-    const int bg = rest % p.bg_count;
-    const int kblk = rest / p.bg_count;
-    const int c = ((int)(blockIdx.x % p.nch_max) + (p.rot ? p.nch_max - kblk % p.nch_max : 0)) % p.nch_max;
+    // Work item: chunk c of the walk of key block kblk of pair bg.
+    int bg, kblk, c;
+    dkdv_item(p, bg, kblk, c);
     const int b = bg / p.hkv, g = bg % p.hkv;
     const int PL = p.P + p.L;
     const int kb0 = kblk * kKeysPerWG;
@@ -629,10 +648,8 @@ __global__ __launch_bounds__(kThreadsR, 1) void attn_bwd_dkdv_role_kernel(DkvPar
     const int role = wave >= kGroupsR ? 1 : 0;
     const int kg = wave - kGroupsR * role;
     const int hl = lane & 31, g2 = lane >> 5;
-    const int rest = blockIdx.x / p.nch_max;
-    const int bg = rest % p.bg_count;
-    const int kblk = rest / p.bg_count;
-    const int c = ((int)(blockIdx.x % p.nch_max) + (p.rot ? p.nch_max - kblk % p.nch_max : 0)) % p.nch_max;
+    int bg, kblk, c;
+    dkdv_item(p, bg, kblk, c);
     const int b = bg / p.hkv, g = bg % p.hkv;
     const int PL = p.P + p.L;
     const int kb0 = kblk * kKeysPerWGR;
@@ -1246,19 +1263,57 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.tc = w.tc;
     kp.c = c;
     kp.scale = a.scale;
-    {
-        // Workgroup i runs on XCD i mod 8, each XCD taking its share in order.  The plain
-        // order (chunk fastest, then pair, then key block) keeps a (pair, chunk) of nearby key
-        // blocks on one XCD, where they share their Q / dO tiles in L2.  But when it sends
-        // every walk's chunk 0 to only some XCDs (short walks are chunk 0 alone), those XCDs
-        // get most of the work: then the chunk index is rotated by the key block instead.
+    // Grid order.  Workgroups are dispatched in index order, workgroup i to XCD i mod 8, so
+    // the order decides both when a chunk starts and where it runs.  Work list: every
+    // (key block, chunk) that exists, longest chunk first (a counting sort on the chunk's
+    // tile count, ties in key block and chunk order), with the pairs of an entry on
+    // consecutive workgroups: the heaviest chunks no longer start late and every XCD gets
+    // a similar mix.
+    kp.nord = 0;
+    kp.rot = 0;
+    int64_t kgrid = (int64_t)w.nch * w.kblocks * bg_count;
+    if ((int64_t)w.kblocks * w.nch <= kOrderMax) {
+        int len[kOrderMax];
+        int hist[kOrderMax + 2] = {0};
+        int n = 0, maxlen = 0;
+        for (int kb = 0; kb < w.kblocks; ++kb) {
+            const int kb0 = kb * w.kpb;
+            int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
+            const int nr = kblock_tile_ranges(kb0, kb0 + w.kpb < a.N ? kb0 + w.kpb : a.N, a.P, a.L, a.B, a.N, rs, re);
+            int npt = 0;
+            for (int i = 0; i < nr; ++i) npt += re[i] - rs[i];
+            const int nch = walk_chunks(npt, w.tc);
+            for (int cc = 0; cc < nch; ++cc) {
+                len[n] = (int)((int64_t)(cc + 1) * npt / nch - (int64_t)cc * npt / nch);
+                if (len[n] > kOrderMax) len[n] = kOrderMax;   // only the rank matters
+                maxlen = len[n] > maxlen ? len[n] : maxlen;
+                kp.ord[n++] = (uint16_t)(kb << 3 | cc);
+            }
+        }
+        // start of each length's run, longest first
+        for (int i = 0; i < n; ++i) ++hist[len[i]];
+        int at = 0;
+        for (int l = maxlen; l >= 0; --l) {
+            const int cnt = hist[l];
+            hist[l] = at;
+            at += cnt;
+        }
+        uint16_t sorted[kOrderMax];
+        for (int i = 0; i < n; ++i) sorted[hist[len[i]]++] = kp.ord[i];
+        for (int i = 0; i < n; ++i) kp.ord[i] = sorted[i];
+        kp.nord = n;
+        kgrid = (int64_t)n * bg_count;
+    } else {
+        // Closed-form order: chunk fastest, then pair, then key block; it keeps a (pair, chunk)
+        // of nearby key blocks on one XCD, but when it sends every walk's chunk 0 (a short
+        // walk's only chunk) to some XCDs only, the chunk index is rotated by the key block.
         unsigned seen = 0;
         const int64_t S = (int64_t)bg_count * w.nch;
         for (int kb = 0; kb < w.kblocks && kb < 8; ++kb)
             for (int bi = 0; bi < bg_count && bi < 8; ++bi) seen |= 1u << (int)((kb * S + (int64_t)bi * w.nch) & 7);
         kp.rot = seen == 0xffu ? 0 : 1;
     }
-    const dim3 kg((unsigned)((int64_t)w.nch * w.kblocks * bg_count));
+    const dim3 kg((unsigned)kgrid);
     if (a.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_role_kernel, kg, dim3(kThreadsR), 0, s, kp);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), kg, dim3(kThreadsB), 0, s, kp);
 
