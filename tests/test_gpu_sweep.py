@@ -3,7 +3,8 @@
 The shapes are drawn once from a fixed NumPy generator (seed 20261202), so every run checks
 the same cases; each case prints its shape before it runs.  Training-layout forward: batch,
 GQA group, KV heads, head_dim, prompt, response and block length (MARS §3.2 Eq. 2), with the
-visited-tile log checked bit for bit; backward on the same kind of shapes; decode step: batch,
+visited-tile log checked bit for bit; backward on the same kind of shapes and on five
+mid-size ones (about 1000-4000 positions, so the dK/dV walks split into chunks); decode step: batch,
 group, KV heads, head_dim, window, cache capacity and per-sequence lengths (0 and the capacity
 included; MARS Fig. 2 right); acceptance: batch, window, vocabulary and tau (the MARS author
 blog, "Inference: a knob, not a mode switch").
@@ -116,6 +117,33 @@ def test_sweep_backward(b, hq, hkv, d, P, L, B, seed):
     bq, bk, bv = bwd_bounds(q64, k64, v64, do64, to_np64(od), lse_err, P, L, B)
     for name, g, r, bb in (("dQ", dq, rq, bq), ("dK", dk, rk, bk), ("dV", dv, rv, bv)):
         check_bounded(to_np64(g), r, bb, f"sweep {name} b{b} h{hq}/{hkv} d{d} P{P} L{L} B{B}")
+
+
+def _mid_bwd_shapes(n):
+    """Backward layouts long enough that the dK/dV walks split into several chunks of tens of
+    tiles (positions ~1000-4000), from a generator of their own so the cases above stay fixed."""
+    rng = np.random.default_rng(20261203)
+    out = []
+    for _ in range(n):
+        G = int(rng.choice([1, 2, 4, 7]))
+        hkv = int(rng.integers(1, 3))
+        d = int(rng.choice([64, 128]))
+        P = int(rng.integers(0, 1500))
+        L = int(rng.integers(200, 1200))
+        B = int(rng.choice([1, 4, 8, 16, 32]))
+        out.append((1, G * hkv, hkv, d, P, L, B, int(rng.integers(0, 1 << 30))))
+    return out
+
+
+MID_BWD_SHAPES = _mid_bwd_shapes(5)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("b,hq,hkv,d,P,L,B,seed", MID_BWD_SHAPES)
+def test_sweep_backward_mid(b, hq, hkv, d, P, L, B, seed):
+    """Whole dQ, dK, dV against the oracle at mid-size layouts (chunked walks, the
+    longest-chunk-first grid)."""
+    test_sweep_backward(b, hq, hkv, d, P, L, B, seed)
 
 
 @pytest.mark.parametrize("batch,hq,hkv,d,W,cap,lens,seed", DEC_SHAPES)
