@@ -235,35 +235,51 @@ struct PrepParams {
     int batch, hq, N, Npad, ncnt;
 };
 
+constexpr int kPrepPasses = 4;   // rows per prep thread (their loads issued together)
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(PrepParams p) {
-    constexpr int TPR = D / 8;   // lanes per (batch, position, head) row, 8 elements each
+    constexpr int TPR = D / 8;          // lanes per (batch, head, position) row, 8 elements each
+    constexpr int RPP = 256 / TPR;      // rows per workgroup pass
+    // Rows in [batch][head][position] order, the order of the two scalars written, so their
+    // stores and the LSE reads are contiguous; a thread takes the same lane of kPrepPasses
+    // rows RPP apart and issues all of their loads before using any.
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = t / TPR;
-    const int c8 = (int)(t % TPR);
-    const int64_t rows = (int64_t)p.batch * p.Npad * p.hq;
     if (t < p.ncnt) p.cnt[t] = 0;
-    if (row >= rows) return;   // whole TPR-lane groups leave together
-    const int h = (int)(row % p.hq);
-    const int64_t bp = row / p.hq;
-    const int pos = (int)(bp % p.Npad);
-    const int b = (int)(bp / p.Npad);
-    float dot = 0.f;
-    if (pos < p.N) {
-        const u32x4_t ow = *reinterpret_cast<const u32x4_t*>(p.o + b * p.os0 + (int64_t)pos * p.os1 + (int64_t)h * p.os2 + 8 * c8);
-        const u32x4_t dw = *reinterpret_cast<const u32x4_t*>(p.dout + b * p.ds0 + (int64_t)pos * p.ds1 + (int64_t)h * p.ds2 + 8 * c8);
+    const int c8 = (int)(threadIdx.x % TPR);
+    const int64_t rows = (int64_t)p.batch * p.hq * p.Npad;
+    const int64_t r0 = (int64_t)blockIdx.x * (RPP * kPrepPasses) + threadIdx.x / TPR;
+    u32x4_t ow[kPrepPasses], dw[kPrepPasses];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dot = fmaf(__uint_as_float(ow[i] << 16), __uint_as_float(dw[i] << 16), dot);
-            dot = fmaf(__uint_as_float(ow[i] & 0xffff0000u), __uint_as_float(dw[i] & 0xffff0000u), dot);
+    for (int k = 0; k < kPrepPasses; ++k) {
+        const int64_t r = r0 + (int64_t)k * RPP;
+        const int pos = (int)(r % p.Npad);
+        const int64_t bh = r / p.Npad;
+        ow[k] = u32x4_t{0u, 0u, 0u, 0u};
+        dw[k] = u32x4_t{0u, 0u, 0u, 0u};
+        if (r < rows && pos < p.N) {
+            const int h = (int)(bh % p.hq), b = (int)(bh / p.hq);
+            ow[k] = *reinterpret_cast<const u32x4_t*>(p.o + b * p.os0 + (int64_t)pos * p.os1 + (int64_t)h * p.os2 + 8 * c8);
+            dw[k] = *reinterpret_cast<const u32x4_t*>(p.dout + b * p.ds0 + (int64_t)pos * p.ds1 + (int64_t)h * p.ds2 + 8 * c8);
         }
     }
 #pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
-    if (c8 == 0) {
-        const int64_t idx = ((int64_t)b * p.hq + h) * p.Npad + pos;
-        p.nlse[idx] = pos < p.N ? -p.lse[((int64_t)b * p.hq + h) * p.N + pos] * kLog2e : 0.f;
-        p.ndelta[idx] = pos < p.N ? -dot : 0.f;
+    for (int k = 0; k < kPrepPasses; ++k) {
+        const int64_t r = r0 + (int64_t)k * RPP;
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dot = fmaf(__uint_as_float(ow[k][i] << 16), __uint_as_float(dw[k][i] << 16), dot);
+            dot = fmaf(__uint_as_float(ow[k][i] & 0xffff0000u), __uint_as_float(dw[k][i] & 0xffff0000u), dot);
+        }
+#pragma unroll
+        for (int m = TPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+        if (c8 == 0 && r < rows) {
+            const int pos = (int)(r % p.Npad);
+            const int64_t bh = r / p.Npad;
+            p.nlse[r] = pos < p.N ? -p.lse[bh * p.N + pos] * kLog2e : 0.f;
+            p.ndelta[r] = pos < p.N ? -dot : 0.f;
+        }
     }
 }
 
@@ -1225,9 +1241,11 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     pp.N = a.N;
     pp.Npad = Npad;
     pp.ncnt = w.kblocks * bg_count * w.kgroups * 2;
-    int64_t prep_threads = (int64_t)a.batch * Npad * a.hq * (a.d / 8);
-    if (prep_threads < pp.ncnt) prep_threads = pp.ncnt;
-    const dim3 pg((unsigned)((prep_threads + 255) / 256));
+    const int64_t prep_rows = (int64_t)a.batch * a.hq * Npad;
+    const int64_t rows_per_wg = (int64_t)(256 / (a.d / 8)) * kPrepPasses;
+    int64_t prep_wgs = (prep_rows + rows_per_wg - 1) / rows_per_wg;
+    if (prep_wgs * 256 < pp.ncnt) prep_wgs = ((int64_t)pp.ncnt + 255) / 256;
+    const dim3 pg((unsigned)prep_wgs);
     if (a.d == 128) hipLaunchKernelGGL((attn_bwd_prep_kernel<128>), pg, dim3(256), 0, s, pp);
     else hipLaunchKernelGGL((attn_bwd_prep_kernel<64>), pg, dim3(256), 0, s, pp);
 
