@@ -639,12 +639,32 @@ struct AttnF32Params {
 
 template <int D>
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnF32Params p) {
+    // One 64-lane workgroup per 64 consecutive positions of one (batch, head), a row per
+    // lane.  The workgroup walks the 64-key tiles of the union of its rows' two key intervals
+    // ([0, hi1) and [lo2, r]), staged in LDS and read by broadcast; each lane forms dot
+    // products only for the keys its own row sees (exact fp32, online softmax).
+    constexpr int KT = 64;
+    __shared__ float sk[KT][D];
+    __shared__ float sv[KT][D];
     const int r0 = blockIdx.x * 64;
     const int r = r0 + threadIdx.x;
     const int h = blockIdx.y, b = blockIdx.z, g = h / p.G;
     const bool valid = r < p.N;
     const int rr = valid ? r : p.N - 1;
     const RowBounds rb = row_bounds(rr, p.P, p.L, p.B);
+
+    // Tiles of the workgroup's key union: [0, ahi) and [clo, chi).
+    int ahi = rb.hi1, clo = rb.lo2 <= rr ? rb.lo2 : 0x7fffffff, chi = rb.lo2 <= rr ? rr + 1 : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        ahi = max(ahi, __shfl_xor(ahi, m));
+        clo = min(clo, __shfl_xor(clo, m));
+        chi = max(chi, __shfl_xor(chi, m));
+    }
+    const int nA = (ahi + KT - 1) / KT;
+    const int c0 = clo < chi ? max(clo / KT, nA) : nA;
+    const int c1 = clo < chi ? (chi + KT - 1) / KT : nA;
+    const int ntiles = nA + (c1 > c0 ? c1 - c0 : 0);
 
     float q[D], acc[D];
     const float* qp = p.q + b * p.qs0 + (int64_t)rr * p.qs1 + (int64_t)h * p.qs2;
@@ -654,23 +674,36 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnF32Params p) {
         acc[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    const int jmax = min(r0 + 63, p.N - 1);
     const float* kb = p.k + b * p.ks0 + (int64_t)g * p.ks2;
     const float* vb = p.v + b * p.vs0 + (int64_t)g * p.vs2;
-    for (int j = 0; j <= jmax; ++j) {
-        const float* kp = kb + (int64_t)j * p.ks1;
-        float sdot = 0.f;
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int k0 = (ti < nA ? ti : c0 + (ti - nA)) * KT;
+        __syncthreads();   // the previous tile's readers are done
+        {
+            const int j = min(k0 + (int)threadIdx.x, p.N - 1);
+            const float* kp = kb + (int64_t)j * p.ks1;
+            const float* vp = vb + (int64_t)j * p.vs1;
 #pragma unroll
-        for (int d = 0; d < D; ++d) sdot = fmaf(q[d], kp[d], sdot);
-        if (key_visible(rr, j, rb)) {
+            for (int d = 0; d < D; ++d) {
+                sk[threadIdx.x][d] = kp[d];
+                sv[threadIdx.x][d] = vp[d];
+            }
+        }
+        __syncthreads();
+        const int kend = min(KT, p.N - k0);
+        for (int jj = 0; jj < kend; ++jj) {
+            const int j = k0 + jj;
+            if (!key_visible(rr, j, rb)) continue;
+            float sdot = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) sdot = fmaf(q[d], sk[jj][d], sdot);
             const float sc = sdot * p.scale;
             const float mnew = fmaxf(m, sc);
             const float alpha = expf(m - mnew);
             const float pj = expf(sc - mnew);
             l = fmaf(l, alpha, pj);
-            const float* vp = vb + (int64_t)j * p.vs1;
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], alpha, pj * vp[d]);
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], alpha, pj * sv[jj][d]);
             m = mnew;
         }
     }

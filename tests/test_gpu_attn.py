@@ -69,6 +69,22 @@ def test_fp32_tiny_workload():
     assert mx <= 1e-4, "fp32 path should be far inside the bf16 bar"
 
 
+@pytest.mark.parametrize("b,hq,hkv,d,P,L,B", [
+    (2, 4, 2, 128, 40, 150, 8),     # head_dim 128, G = 2, ragged last workgroup
+    (1, 3, 1, 128, 0, 100, 16),     # no prompt
+    (1, 2, 2, 64, 300, 400, 32),    # long noisy stream: key tiles between the intervals skipped
+    (2, 7, 1, 64, 70, 61, 5),       # G = 7, workgroups straddling P + L, short last block
+    (1, 1, 1, 64, 5, 0, 3),         # prompt only
+])
+def test_fp32_layouts(b, hq, hkv, d, P, L, B):
+    """The fp32 path (exact fp32, LDS key tiles over the union of a workgroup's two key
+    intervals) on every row, O and LSE."""
+    got, ref, got_lse, ref_lse = run_case(b, hq, hkv, d, P, L, B, seed=b * 1000 + P + L, dtype="fp32")
+    mx, _ = check_close(got, ref, f"fp32 O b{b} h{hq}/{hkv} d{d} P{P} L{L} B{B}")
+    assert mx <= 1e-4
+    assert np.max(np.abs(got_lse - ref_lse)) <= 1e-4
+
+
 @pytest.mark.parametrize("shape", [I.QWEN05B, I.QWEN7B, I.LONG7B], ids=lambda s: s.name)
 def test_full_size_sampled_rows(shape):
     s = shape
