@@ -53,7 +53,7 @@ constexpr int kChunkMinTiles = 4;          //        of at least 4 position tile
 constexpr int kOrderMax = 1024;            // dK/dV work list passed with the launch (entries)
 constexpr int kNominalSlots64 = 512;       // workgroup slots the dK/dV chunk size aims at: 2 per CU at
 constexpr int kNominalSlots128 = 192;      // head_dim 64 (3 fit; 768 measured the same); at head_dim 128
-                                           // (one per CU) 3/4 of the CUs: longer chunks, fewer partials
+                                           // (one per CU) 3/4 of the CUs, measured best of 160-1024
 
 // ---------------------------------------------------------------------------------------
 // LDS rings.  One file-scope object per stage, array and head_dim.
@@ -1165,9 +1165,11 @@ int pad32(int n) { return (n + kT - 1) / kT * kT; }
 
 size_t r256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Chunk size of the dK/dV walks (position tiles): about half the mean number of tiles a
-// resident workgroup gets, at least kChunkMinTiles; and the largest chunk count over the
-// key blocks (sizes the partial buffer).
+// Chunk size of the dK/dV walks (position tiles): half the mean number of tiles per
+// workgroup slot for a nominal slot count (kNominalSlots64 / kNominalSlots128, chosen by
+// measurement: at head_dim 128 the 256 real slots would put chunks at half a slot's load,
+// which packs worse than two thirds), at least kChunkMinTiles; and the largest chunk count
+// over the key blocks (sizes the partial buffer).
 void walk_plan(int P, int L, int B, int N, int bg, int d, int kpb, int* tc, int* nch_max) {
     int64_t total = 0;
     int maxnpt = 0;
