@@ -1292,16 +1292,24 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.nord = 0;
     kp.rot = 0;
     int64_t kgrid = (int64_t)w.nch * w.kblocks * bg_count;
-    if ((int64_t)w.kblocks * w.nch <= kOrderMax) {
+    auto kblock_tiles = [&](int kb) {   // query tiles key block kb visits
+        const int kb0 = kb * w.kpb;
+        int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
+        const int nr = kblock_tile_ranges(kb0, kb0 + w.kpb < a.N ? kb0 + w.kpb : a.N, a.P, a.L, a.B, a.N, rs, re);
+        int npt = 0;
+        for (int i = 0; i < nr; ++i) npt += re[i] - rs[i];
+        return npt;
+    };
+    // The list holds the chunks that exist, which is fewer than key blocks x the largest
+    // chunk count wherever walks differ in length.
+    int64_t nent = 0;
+    for (int kb = 0; kb < w.kblocks && nent <= kOrderMax; ++kb) nent += walk_chunks(kblock_tiles(kb), w.tc);
+    if (nent <= kOrderMax) {
         int len[kOrderMax];
         int hist[kOrderMax + 2] = {0};
         int n = 0, maxlen = 0;
         for (int kb = 0; kb < w.kblocks; ++kb) {
-            const int kb0 = kb * w.kpb;
-            int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
-            const int nr = kblock_tile_ranges(kb0, kb0 + w.kpb < a.N ? kb0 + w.kpb : a.N, a.P, a.L, a.B, a.N, rs, re);
-            int npt = 0;
-            for (int i = 0; i < nr; ++i) npt += re[i] - rs[i];
+            const int npt = kblock_tiles(kb);
             const int nch = walk_chunks(npt, w.tc);
             for (int cc = 0; cc < nch; ++cc) {
                 len[n] = (int)((int64_t)(cc + 1) * npt / nch - (int64_t)cc * npt / nch);

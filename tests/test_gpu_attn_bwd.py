@@ -162,16 +162,18 @@ def test_bwd_strided_inputs(d):
 
 
 @pytest.mark.timeout(300)
-def test_bwd_closed_form_order():
-    """A layout whose (key block, chunk) list is longer than the launch's work list (head_dim
-    64, N = 16512: 129 key blocks x 8 chunks > 1024 entries), so dK/dV take the closed-form
-    grid order.  dQ on sampled rows; dK/dV on keys whose rows the oracle affords: key block
-    110, whose walk is split into chunks, the end of the prompt and the noisy stream.  Over
-    every key of the KV head, at any size: sum_j dV_j = sum_i dO_i (rows of P sum to one) and
-    sum_j dK_j = 0 (rows of dS sum to zero).  Two launches bit-identical."""
-    b, hq, hkv, d, P, L, B = 1, 2, 1, 64, 16384, 64, 8
+@pytest.mark.parametrize("P,kblk", [(16384, 110), (26000, 180)], ids=["list804", "closed1064"])
+def test_bwd_long_walk_order(P, kblk):
+    """Head_dim 64, one KV head, long prompts.  N = 16512: 129 key blocks x 8 chunks exceed the
+    launch's 1024-entry work list, but only 804 (key block, chunk) entries exist, so the list is
+    used.  N = 26128: 205 key blocks, 1064 entries, so dK/dV take the closed-form grid order.
+    dQ on sampled rows; dK/dV on keys whose rows the oracle affords: key block kblk, whose walk
+    is split into chunks, the end of the prompt and the noisy stream.  Over every key of the KV
+    head, at any size: sum_j dV_j = sum_i dO_i (rows of P sum to one) and sum_j dK_j = 0 (rows
+    of dS sum to zero).  Two launches bit-identical."""
+    b, hq, hkv, d, L, B = 1, 2, 1, 64, 64, 8
     N = P + 2 * L
-    print(f"case bwd closed-form order d={d} P={P} L={L} B={B} N={N}", flush=True)
+    print(f"case bwd long walk order d={d} P={P} L={L} B={B} N={N}", flush=True)
     q, k, v = I.small_train_inputs(b, hq, hkv, d, P, L, 77)
     do = I.small_grad_output(b, hq, d, P, L, 77)
     qd, kd, vd, dod = q.to(dev()), k.to(dev()), v.to(dev()), do.to(dev())
@@ -184,12 +186,12 @@ def test_bwd_closed_form_order():
         assert torch.equal(x, y)
     from tests.gpu_helpers import sample_rows
     rows = sample_rows(P, L, B, 12, 77)
-    keys = np.array([110 * 128, 110 * 128 + 1, 110 * 128 + 63, 111 * 128 - 1, P - 1, P, P + L - 1, P + L, N - 1])
+    keys = np.array([kblk * 128, kblk * 128 + 1, kblk * 128 + 63, (kblk + 1) * 128 - 1, P - 1, P, P + L - 1, P + L, N - 1])
     q64, k64, v64, do64 = (to_np64(t) for t in (q, k, v, do))
     rq, rk, rv = O.attn_bwd(q64, k64, v64, do64, P, L, B, rows=rows, keys=keys)
     bq, bk, bv = bwd_bounds(q64, k64, v64, do64, to_np64(od), lse_bound(q, k), P, L, B, rows=rows, keys=keys)
     check_all((to_np64(dq)[:, rows], to_np64(dk)[:, keys], to_np64(dv)[:, keys]), (rq, rk, rv), (bq, bk, bv),
-              "closed-form order")
+              "long walk order")
     # identities over all keys (per KV head; bf16 outputs: tolerance 2^-7 of the magnitude sums)
     gdv, gdk = to_np64(dv)[0, :, 0], to_np64(dk)[0, :, 0]
     sdo = do64[0].sum(axis=(0, 1))
