@@ -183,6 +183,17 @@ typedef struct mars_attn_bwd_strides {
 /* Workspace bytes of mars_attn_bwd for desc (bf16 only; MARS_EUNSUPPORTED for fp32). */
 int mars_attn_bwd_workspace_bytes(const mars_attn_desc* desc, size_t* bytes);
 
+/* Test support: the dK/dV schedule mars_attn_bwd launches for desc, computed on the host
+ * (nothing is launched or read on the device).  A key block's walk over the position
+ * tiles whose rows see its keys is split into at most 8 chunks of at most *chunk_tiles
+ * tiles; *max_chunks is the largest chunk count over the key blocks, *items the number of
+ * (key block, chunk) chunks that exist, and *work_list 1 when they are dispatched from the
+ * host-built longest-first list (items <= 1024), 0 when the grid falls back to the
+ * closed-form order (key blocks x max_chunks entries, the missing chunks exiting at once).
+ * Errors as mars_attn_bwd_workspace_bytes; MARS_EINVAL for a null output pointer. */
+int mars_attn_bwd_plan(const mars_attn_desc* desc, int32_t* chunk_tiles, int32_t* max_chunks, int64_t* items,
+                       int32_t* work_list);
+
 /*
  * desc: the forward's descriptor (q/k/v/o strides); dtype must be MARS_DTYPE_BF16.
  * gs:   strides of d_o, dq, dk, dv (same alignment rules as q/k/v/o).

@@ -18,6 +18,7 @@ __all__ = [
     "mars_strerror",
     "mars_attn_fwd",
     "mars_attn_work",
+    "mars_attn_bwd_plan",
     "mars_mask_materialize",
     "mars_tile_map",
     "mars_attn_tilelog_geometry",
@@ -201,6 +202,17 @@ def mars_attn_bwd_workspace_bytes(batch, hq, hkv, d, P, Lr, B, dtype=torch.bfloa
     _check(L.load().mars_attn_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
            "mars_attn_bwd_workspace_bytes")
     return n.value
+
+
+def mars_attn_bwd_plan(batch, hq, hkv, d, P, Lr, B):
+    """The dK/dV schedule of :func:`mars_attn_bwd` for a layout (host only, see mars.h):
+    dict with chunk_tiles, max_chunks, items and work_list."""
+    desc = attn_desc(batch, hq, hkv, d, P, Lr, B, torch.bfloat16)
+    tc, nch, wl = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    n = ctypes.c_int64()
+    _check(L.load().mars_attn_bwd_plan(ctypes.byref(desc), ctypes.byref(tc), ctypes.byref(nch), ctypes.byref(n),
+                                       ctypes.byref(wl)), "mars_attn_bwd_plan")
+    return {"chunk_tiles": tc.value, "max_chunks": nch.value, "items": n.value, "work_list": bool(wl.value)}
 
 
 def mars_attn_bwd(q, k, v, o, lse, dout, prompt_len, resp_len, block, scale=0.0, dq=None, dk=None, dv=None,

@@ -74,6 +74,9 @@ _SIGNATURES = {
                                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
     "mars_attn_fwd_tilelog": (ctypes.c_int, [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]),
     "mars_attn_bwd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "mars_attn_bwd_plan": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int32)]),
     "mars_attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnBwdStrides), P, P, P, P, P, P,
                                      P, P, P, P, ctypes.c_size_t, P]),
     "mars_decode_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(DecodeDesc), ctypes.POINTER(ctypes.c_size_t)]),

@@ -1211,10 +1211,38 @@ BwdLayout bwd_layout(int batch, int hq, int hkv, int d, int P, int L, int B, int
     return w;
 }
 
+// Position tiles the walk of key block kb visits.
+int kblock_tiles(const BwdLayout& w, int kb, int P, int L, int B, int N) {
+    const int kb0 = kb * w.kpb;
+    int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
+    const int nr = kblock_tile_ranges(kb0, kb0 + w.kpb < N ? kb0 + w.kpb : N, P, L, B, N, rs, re);
+    int npt = 0;
+    for (int i = 0; i < nr; ++i) npt += re[i] - rs[i];
+    return npt;
+}
+
+// (key block, chunk) entries of the dK/dV grid: the chunks that exist, which is fewer than
+// key blocks x the largest chunk count wherever walks differ in length.
+int64_t bwd_work_items(const BwdLayout& w, int P, int L, int B, int N) {
+    int64_t n = 0;
+    for (int kb = 0; kb < w.kblocks; ++kb) n += walk_chunks(kblock_tiles(w, kb, P, L, B, N), w.tc);
+    return n;
+}
+
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int d, int P, int L, int B) {
     return bwd_layout(batch, hq, hkv, d, P, L, B, P + 2 * L).total;
+}
+
+void attn_bwd_plan(int batch, int hq, int hkv, int d, int P, int L, int B, int* chunk_tiles, int* max_chunks,
+                   int64_t* items, int* work_list) {
+    const int N = P + 2 * L;
+    const BwdLayout w = bwd_layout(batch, hq, hkv, d, P, L, B, N);
+    *chunk_tiles = w.tc;
+    *max_chunks = w.nch;
+    *items = bwd_work_items(w, P, L, B, N);
+    *work_list = *items <= kOrderMax ? 1 : 0;
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
@@ -1292,24 +1320,13 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s) {
     kp.nord = 0;
     kp.rot = 0;
     int64_t kgrid = (int64_t)w.nch * w.kblocks * bg_count;
-    auto kblock_tiles = [&](int kb) {   // query tiles key block kb visits
-        const int kb0 = kb * w.kpb;
-        int rs[3] = {0, 0, 0}, re[3] = {0, 0, 0};
-        const int nr = kblock_tile_ranges(kb0, kb0 + w.kpb < a.N ? kb0 + w.kpb : a.N, a.P, a.L, a.B, a.N, rs, re);
-        int npt = 0;
-        for (int i = 0; i < nr; ++i) npt += re[i] - rs[i];
-        return npt;
-    };
-    // The list holds the chunks that exist, which is fewer than key blocks x the largest
-    // chunk count wherever walks differ in length.
-    int64_t nent = 0;
-    for (int kb = 0; kb < w.kblocks && nent <= kOrderMax; ++kb) nent += walk_chunks(kblock_tiles(kb), w.tc);
+    const int64_t nent = bwd_work_items(w, a.P, a.L, a.B, a.N);
     if (nent <= kOrderMax) {
         int len[kOrderMax];
         int hist[kOrderMax + 2] = {0};
         int n = 0, maxlen = 0;
         for (int kb = 0; kb < w.kblocks; ++kb) {
-            const int npt = kblock_tiles(kb);
+            const int npt = kblock_tiles(w, kb, a.P, a.L, a.B, a.N);
             const int nch = walk_chunks(npt, w.tc);
             for (int cc = 0; cc < nch; ++cc) {
                 len[n] = (int)((int64_t)(cc + 1) * npt / nch - (int64_t)cc * npt / nch);

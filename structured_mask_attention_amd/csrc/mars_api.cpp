@@ -128,6 +128,23 @@ int mars_attn_bwd_workspace_bytes(const mars_attn_desc* desc, size_t* bytes) {
     return MARS_OK;
 }
 
+int mars_attn_bwd_plan(const mars_attn_desc* desc, int32_t* chunk_tiles, int32_t* max_chunks, int64_t* items,
+                       int32_t* work_list) {
+    int st = check_attn_desc(desc);
+    if (st) return st;
+    if (!chunk_tiles || !max_chunks || !items || !work_list) return MARS_EINVAL;
+    if (desc->dtype != MARS_DTYPE_BF16) return MARS_EUNSUPPORTED;
+    int tc = 0, nch = 0, list = 0;
+    int64_t n = 0;
+    mars::attn_bwd_plan(desc->batch, desc->n_q_heads, desc->n_kv_heads, desc->head_dim, desc->prompt_len,
+                        desc->resp_len, desc->block, &tc, &nch, &n, &list);
+    *chunk_tiles = tc;
+    *max_chunks = nch;
+    *items = n;
+    *work_list = list;
+    return MARS_OK;
+}
+
 int mars_attn_bwd(const mars_attn_desc* desc, const mars_attn_bwd_strides* gs, const void* q, const void* k,
                   const void* v, const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
                   void* ws, size_t ws_bytes, hipStream_t stream) {

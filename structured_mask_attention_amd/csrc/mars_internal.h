@@ -45,6 +45,9 @@ struct AttnBwdArgs {
 };
 size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int d, int P, int L, int B);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t s);
+// The dK/dV schedule launch_attn_bwd_bf16 would use (host only).
+void attn_bwd_plan(int batch, int hq, int hkv, int d, int P, int L, int B, int* chunk_tiles, int* max_chunks,
+                   int64_t* items, int* work_list);
 
 // Debug mask kernels (mask_kernels.hip).
 hipError_t launch_mask_materialize(int P, int L, int B, uint8_t* mask, hipStream_t s);

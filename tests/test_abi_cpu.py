@@ -47,6 +47,44 @@ def test_attn_work_matches_oracle(P, Lr, B):
     assert vis2 == O.visible_tile_elems(P, Lr, B, 16, 48)
 
 
+# Keys per dK/dV workgroup of the backward (192 at head_dim 128, 128 at head_dim 64) and the
+# kernels' 32-position tiles: the geometry mars_attn_bwd_plan counts in.
+BWD_KEYS_PER_WG = {64: 128, 128: 192}
+
+
+@pytest.mark.parametrize("d,P,Lr,B", [(64, 40, 150, 4), (128, 33, 700, 8), (64, 130, 120, 4), (128, 0, 300, 1),
+                                      (64, 1000, 3000, 16), (128, 5, 37, 64)])
+def test_bwd_plan_items_brute_force(d, P, Lr, B):
+    """The backward's dK/dV work items: for every key block, the 32-position tiles holding a row
+    that sees one of its keys, counted on the oracle's dense mask (tile classes of 32 x keys-per-
+    workgroup tiles), split into min(8, max(1, ceil(tiles / chunk_tiles))) chunks."""
+    plan = M.mars_attn_bwd_plan(2, 4, 2, d, P, Lr, B)
+    kpb = BWD_KEYS_PER_WG[d]
+    tiles = (O.tile_map(O.mask_rules(P, Lr, B), 32, kpb) != 0).sum(axis=0)
+    tc = plan["chunk_tiles"]
+    assert tc >= 4
+    chunks = np.minimum(8, np.maximum(1, -(-tiles // tc)))
+    assert plan["items"] == int(chunks.sum())
+    assert plan["max_chunks"] == int(chunks.max())
+    assert plan["work_list"] == (plan["items"] <= 1024)
+
+
+def test_bwd_plan_work_list_limit():
+    """The two head_dim 64 layouts the GPU tests run on either side of the 1024-entry work
+    list: N = 16512 has 129 key blocks x 8 chunks > 1024 but only 804 chunks that exist (list);
+    N = 26128 has 1064 (closed-form order).  The bench's three training layouts use the list."""
+    a = M.mars_attn_bwd_plan(1, 2, 1, 64, 16384, 64, 8)
+    assert (a["max_chunks"], a["items"], a["work_list"]) == (8, 804, True)
+    assert 129 * a["max_chunks"] > 1024
+    b = M.mars_attn_bwd_plan(1, 2, 1, 64, 26000, 64, 8)
+    assert (b["items"], b["work_list"]) == (1064, False)
+    for bt, hq, hkv, d, P, Lr, B in [(1, 28, 4, 128, 1024, 7168, 32), (4, 28, 4, 128, 512, 1536, 8),
+                                     (8, 14, 2, 64, 256, 512, 4)]:
+        assert M.mars_attn_bwd_plan(bt, hq, hkv, d, P, Lr, B)["work_list"]
+    with pytest.raises(M.MarsError):
+        M.mars_attn_bwd_plan(1, 2, 1, 96, 16, 16, 4)
+
+
 def _attn(desc, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
     return L.load().mars_attn_fwd(ctypes.byref(desc), q, k, v, o, lse, None)
 

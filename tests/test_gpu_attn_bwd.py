@@ -173,6 +173,7 @@ def test_bwd_long_walk_order(P, kblk):
     of dS sum to zero).  Two launches bit-identical."""
     b, hq, hkv, d, L, B = 1, 2, 1, 64, 64, 8
     N = P + 2 * L
+    assert M.mars_attn_bwd_plan(b, hq, hkv, d, P, L, B)["work_list"] == (P == 16384)
     print(f"case bwd long walk order d={d} P={P} L={L} B={B} N={N}", flush=True)
     q, k, v = I.small_train_inputs(b, hq, hkv, d, P, L, 77)
     do = I.small_grad_output(b, hq, d, P, L, 77)
