@@ -96,3 +96,38 @@ def test_decode_large_scores_and_late_maxima(q_gain):
     torch.cuda.synchronize()
     ref = O.decode(to_np64(q), to_np64(kw), to_np64(x.v_win), to_np64(kc), to_np64(x.v_cache), lens.numpy())
     check_close(to_np64(out), ref, f"decode large scores gain {q_gain}")
+
+
+def test_decode_strided_views():
+    """Caches stored position-major ([b, cap, Hkv, D], the per-token layout, viewed as
+    [b, Hkv, cap, D]: position stride Hkv*D, head stride D), window tensors and the output as
+    views of larger buffers.  Bit-identical to the contiguous call, and against the oracle; the
+    padding around the output view stays untouched."""
+    batch, hq, hkv, d, W, cap = 3, 28, 4, 128, 4, 1100
+    lens = [1100, 513, 2]
+    print(f"case decode strided views cap={cap}", flush=True)
+    s = I.DecodeShape("adhoc", batch, hq, hkv, d, W, cap, 0, cap, 8, 0.95, 0.5, 606)
+    x = I.decode_inputs(s, with_logits=False)
+    cache_len = torch.tensor(lens, dtype=torch.int32, device=dev())
+    qw, kw, vw, kc, vc = (t.to(dev()) for t in (x.q_win, x.k_win, x.v_win, x.k_cache, x.v_cache))
+    ref = M.mars_decode_step(qw, kw, vw, kc, vc, cache_len)
+
+    def pos_major(c):
+        return c.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+    def padded_heads(t):
+        big = torch.zeros((t.shape[0], t.shape[1], t.shape[2] + 3, d), dtype=t.dtype, device=t.device)
+        big[:, :, :t.shape[2]] = t
+        return big[:, :, :t.shape[2]]
+
+    kcs, vcs = pos_major(kc), pos_major(vc)
+    assert kcs.stride(2) == hkv * d and kcs.stride(1) == d
+    obuf = torch.full((batch, W, hq + 3, d), 7.0, dtype=torch.bfloat16, device=dev())
+    out = obuf[:, :, :hq]
+    M.mars_decode_step(padded_heads(qw), padded_heads(kw), padded_heads(vw), kcs, vcs, cache_len, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.all(obuf[:, :, hq:] == 7.0)
+    want = O.decode(to_np64(x.q_win), to_np64(x.k_win), to_np64(x.v_win), to_np64(x.k_cache), to_np64(x.v_cache),
+                    np.asarray(lens))
+    check_close(to_np64(out), want, "decode strided views")
