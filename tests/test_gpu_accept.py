@@ -69,7 +69,8 @@ def test_accept_tau_outside_unit_interval_is_rejected(tau):
     assert (n == -7).all()
 
 
-@pytest.mark.parametrize("batch,W,V", [(3, 4, 1001), (2, 1, 7), (2, 7, 8193), (1, 64, 300), (5, 5, 1), (2, 3, 16384)])
+@pytest.mark.parametrize("batch,W,V", [(3, 4, 1001), (2, 1, 7), (2, 7, 8193), (1, 64, 300), (5, 5, 1), (2, 3, 16384),
+                                       (2, 64, 152064)])
 def test_accept_shapes(batch, W, V):
     """Ragged vocabularies: rows padded to a 16-byte multiple, the kernel reads V entries."""
     logits = I.logits_inputs(batch, W, V, seed=V + W, spike_hi=8.0)
@@ -77,6 +78,25 @@ def test_accept_shapes(batch, W, V):
     padded = torch.full((batch, W, Vp), 30.0, dtype=torch.bfloat16)   # pad would win any argmax
     padded[:, :, :V] = logits
     check_accept(padded[:, :, :V], 0.6, f"accept b{batch} W{W} V{V}", max_tie=1)
+
+
+def test_accept_long_prefixes_at_the_largest_window():
+    """Window 64 over the full 152 064-entry vocabulary, each sequence built to stop at a known
+    row: rows before k_b carry a spike of 25 (pmax ~ 1 - 1e-5, far above tau = 0.9), row k_b
+    none (pmax ~ 1e-5), later rows the spike again, which must not count.  n_accept = k_b, and
+    64 when no row is low, with every token and pmax against the oracle."""
+    W, V = 64, 152064
+    stops = [0, 1, 17, 40, 63, 64]
+    x = np.random.default_rng(4711).standard_normal((len(stops), W, V), dtype=np.float32)
+    ids = np.random.default_rng(4712).integers(0, V, size=(len(stops), W))
+    for bi, k in enumerate(stops):
+        for i in range(W):
+            if i != k:
+                x[bi, i, ids[bi, i]] += 25.0
+    tok, _, n = check_accept(I.to_bf16(x), 0.9, "accept long prefixes W64")
+    assert n.tolist() == [max(1, k) for k in stops]
+    spiked = np.array([[i != k for i in range(W)] for k in stops])
+    assert np.array_equal(tok[spiked], ids[spiked])
 
 
 def test_accept_ties_take_lowest_index():

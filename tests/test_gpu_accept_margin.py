@@ -56,7 +56,7 @@ def test_margin_full_workload(tau):
 
 
 @pytest.mark.parametrize("batch,W,V", [(3, 4, 1001), (2, 1, 7), (2, 7, 8193), (1, 64, 300), (5, 5, 1), (2, 3, 16384),
-                                       (2, 2, 40000)])
+                                       (2, 2, 40000), (2, 64, 152064)])
 def test_margin_shapes(batch, W, V):
     """Ragged vocabularies: rows padded to a 16-byte multiple, the kernel reads V entries."""
     logits = I.logits_inputs(batch, W, V, seed=V + 3 * W, spike_hi=8.0)
