@@ -67,11 +67,15 @@ def test_decode_w1_equals_ar_step_of_training_kernel():
 
 
 def test_decode_deterministic():
+    """The full 7B decode workload twice, the second time into a workspace filled with garbage
+    first (only partials of chunks that exist are read, each written by the same call)."""
     s = I.DECODE7B
     x = I.decode_inputs(s, with_logits=False)
     args = [t.to(dev()) for t in (x.q_win, x.k_win, x.v_win, x.k_cache, x.v_cache, x.cache_len)]
     o1 = M.mars_decode_step(*args)
-    o2 = M.mars_decode_step(*args)
+    ws = torch.full((M.mars_decode_workspace_bytes(s.batch, s.hq, s.hkv, s.d, s.W, s.cap),), 0xA5,
+                    dtype=torch.uint8, device=dev())
+    o2 = M.mars_decode_step(*args, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
