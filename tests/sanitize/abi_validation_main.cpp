@@ -137,6 +137,29 @@ static void attention() {
     EXPECT(mars_attn_bwd_workspace_bytes(&d, &need), MARS_OK);
     EXPECT(mars_attn_bwd_workspace_bytes(&f, &need), MARS_EUNSUPPORTED);
     EXPECT(mars_attn_bwd_workspace_bytes(&d, nullptr), MARS_EINVAL);
+    {
+        int32_t tc = 0, nch = 0, wl = 0;
+        int64_t items = 0;
+        EXPECT(mars_attn_bwd_plan(&d, &tc, &nch, &items, &wl), MARS_OK);
+        EXPECT(mars_attn_bwd_plan(&d, nullptr, &nch, &items, &wl), MARS_EINVAL);
+        EXPECT(mars_attn_bwd_plan(&d, &tc, &nch, nullptr, &wl), MARS_EINVAL);
+        EXPECT(mars_attn_bwd_plan(&f, &tc, &nch, &items, &wl), MARS_EUNSUPPORTED);
+        EXPECT(mars_attn_bwd_plan(nullptr, &tc, &nch, &items, &wl), MARS_EINVAL);
+        // The largest layout the descriptor allows (2^24 positions, blocks of 1): the host's
+        // chunk plan and workspace size in 64-bit arithmetic.
+        mars_attn_desc big = d;
+        big.prompt_len = (1 << 24) - 2 * 1000;
+        big.resp_len = 1000;
+        big.block = 1;
+        size_t big_need = 0;
+        EXPECT(mars_attn_bwd_plan(&big, &tc, &nch, &items, &wl), MARS_OK);
+        EXPECT(mars_attn_bwd_workspace_bytes(&big, &big_need), MARS_OK);
+        if (items < 1 || wl != (items <= 1024) || big_need < ((size_t)1 << 24) * 8) {
+            fprintf(stderr, "implausible plan at 2^24 positions: items %lld, list %d, ws %zu\n", (long long)items,
+                    (int)wl, big_need);
+            ++g_fail;
+        }
+    }
     const float* lse = (const float*)FAKE;
     EXPECT(mars_attn_bwd(&d, nullptr, FAKE, FAKE, FAKE, FAKE, lse, FAKE, FAKE, FAKE, FAKE, FAKE, 1u << 30, nullptr),
            MARS_EINVAL);
